@@ -1,0 +1,207 @@
+"""CPU oracle for the eviction-scoring hot path.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The product library
+(``kv_cache_eviction_kvscore_amd``) never imports it, and nothing here imports the
+product: the two share no code. The seeded input generator lives in its own module
+and holds none of the method's arithmetic.
+
+Parts and the passages they follow:
+
+* :func:`scores` -- fp64 attention + per-token score (C, ``oracle.c``). DropKV page,
+  Key Contribution 1 and "Methodology in Plain English": score_j =
+  p_j/(1-p_j) * ||a - v_j||_2 per query row, accumulated over the observation
+  window; query heads of a GQA group are summed (PyramidKV page, aggregated
+  window score).
+* :func:`layer_budgets` -- RippleKV page, Eq. 9 (min-max normalisation), Eq. 10
+  (multiplier r^s_hat), Eq. 11 (clip to [1/gamma, gamma], rescale to mean one),
+  Eq. 12 (B/|A| * w_l) under Eq. 5 (sum of budgets = B), in exact rational
+  arithmetic after the fp64 multipliers.
+* :func:`kept_positions` -- DropKV page: keep the largest individual scores
+  ("delete the k smallest"), and always keep the most recent w tokens.
+* :func:`gather` -- RippleKV page, Eq. 4: the compressed cache is the (k, v)
+  pairs at the retained positions.
+
+Parity pins: see ``tests/test_oracle_pins.py`` (brute-force single-token removal,
+closed forms, invariants) and ``tests/test_budget_oracle.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (OpenMP, plain -O2)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", _LIB_PATH, _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_eval.restype = ctypes.c_int
+        lib.oracle_eval.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_double] + [ctypes.c_void_p] * 4 + \
+            [ctypes.c_int32] + [ctypes.c_void_p] * 6
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def scores(q, k, v, *, num_seqs, num_layers, num_q_heads, num_kv_heads, head_dim, window, cu_seqlens,
+           kv_strides=None, scale=None, mode=0, units=None, want_rows=False):
+    """fp64 scores for the requested units (all units by default).
+
+    q: uint16 bf16 bits, [L][S][Hq][W][d]. k, v: uint16 bf16 bits addressed by
+    ``kv_strides`` = (k_layer, k_head, k_token, v_layer, v_head, v_token) in
+    elements (default: contiguous [L][Hkv][N][d]). A unit is
+    u = (s*L + l)*Hkv + g. Returns a dict with ``score`` [L][Hkv][N] (NaN where not
+    computed) and, with ``want_rows``, per-row ``a``, ``lse``, ``jstar``, ``dom``
+    (the argmax pair's term) in [L][S][Hq][W] order, plus ``pmax`` per unit.
+    """
+    lib = _load()
+    S, L, Hq, Hkv, d, W = num_seqs, num_layers, num_q_heads, num_kv_heads, head_dim, window
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    N = int(cu[-1])
+    if kv_strides is None:
+        kv_strides = (Hkv * N * d, N * d, d, Hkv * N * d, N * d, d)
+    strides = np.asarray(kv_strides, dtype=np.int64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    q = np.ascontiguousarray(q).view(np.uint16)
+    k = np.ascontiguousarray(k).view(np.uint16)
+    v = np.ascontiguousarray(v).view(np.uint16)
+    assert q.size == L * S * Hq * W * d
+    dims = np.asarray([S, L, Hq, Hkv, d, W, mode], dtype=np.int32)
+    if units is None:
+        uarr = None
+        nu = S * L * Hkv
+    else:
+        uarr = np.ascontiguousarray(np.asarray(units, dtype=np.int32))
+        nu = len(uarr)
+    score = np.full((L, Hkv, N), np.nan)
+    rows = L * S * Hq * W
+    a = np.full((rows, d), np.nan) if want_rows else None
+    lse = np.full(rows, np.nan) if want_rows else None
+    jstar = np.full(rows, -1, dtype=np.int32) if want_rows else None
+    dom = np.full(rows, np.nan) if want_rows else None
+    pmax = np.zeros(nu)
+    rc = lib.oracle_eval(_ptr(dims), _ptr(cu), _ptr(strides), float(scale), _ptr(q), _ptr(k), _ptr(v),
+                         _ptr(uarr), nu, _ptr(score), _ptr(a), _ptr(lse), _ptr(jstar), _ptr(dom), _ptr(pmax))
+    if rc != 0:
+        raise ValueError(f"oracle_eval failed with code {rc}")
+    out = {"score": score, "pmax": pmax}
+    if want_rows:
+        out.update(a=a, lse=lse, jstar=jstar, dom=dom)
+    return out
+
+
+# --------------------------------------------------------------------------- budgets
+def _multipliers(sens, ratio, gamma):
+    """RippleKV Eq. 9-11 up to (and including) the clip; fp64 like the page's math."""
+    s = [float(x) for x in sens]
+    smin, smax = min(s), max(s)
+    if smax == smin:
+        shat = [0.0] * len(s)  # Eq. 9: constant profile -> s_hat = 0 (uniform)
+    else:
+        shat = [(x - smin) / (smax - smin) for x in s]
+    wt = [math.exp(math.log(ratio) * x) for x in shat]  # Eq. 10: exp(log r * s_hat) = r^s_hat
+    if math.isfinite(gamma):
+        wt = [min(max(x, 1.0 / gamma), gamma) for x in wt]  # Eq. 11: clip to [1/gamma, gamma]
+    return wt
+
+
+def layer_budgets(sens, ratio, gamma, total, lo, hi):
+    """Integer per-layer budgets b_l for one sequence (RippleKV Eq. 5, 9-12).
+
+    After the fp64 multipliers, everything is exact (``fractions.Fraction``):
+    mean-one rescale (Eq. 11), targets B/|A|*w_l (Eq. 12), projection onto
+    [lo, hi] keeping the total (the unique x_l = clip(lambda*w_l, lo, hi) with
+    sum x_l = B), and largest-remainder rounding so that sum b_l = B exactly
+    (Eq. 5); equal remainders go to the lower layer index.
+    """
+    Lc = len(sens)
+    total = int(total)
+    if Lc == 0:
+        return []
+    if total < Lc * lo or total > Lc * hi:
+        raise ValueError("infeasible budget total")
+    wt = [Fraction(x) for x in _multipliers(sens, ratio, gamma)]
+    mean = sum(wt) / Lc
+    w = [x / mean for x in wt]  # Eq. 11: mean one over the layers
+    x = [Fraction(total, Lc) * wl for wl in w]  # Eq. 12 before rounding
+    if any(xi < lo or xi > hi for xi in x):
+        x = _box_projection(w, Fraction(total), Fraction(lo), Fraction(hi))
+    base = [xi.numerator // xi.denominator for xi in x]
+    rem = [xi - b for xi, b in zip(x, base)]
+    extra = total - sum(base)
+    order = sorted(range(Lc), key=lambda i: (-rem[i], i))
+    for i in order[:extra]:
+        base[i] += 1
+    return base
+
+
+def _box_projection(w, total, lo, hi):
+    """Exact x_l = clip(lam*w_l, lo, hi) with sum = total (f(lam) is monotone, piecewise linear)."""
+    def f(lam):
+        return sum(min(max(lam * wl, lo), hi) for wl in w)
+
+    pts = sorted(set([lo / wl for wl in w] + [hi / wl for wl in w]))
+    lam_lo = Fraction(0)
+    for p in pts:
+        if f(p) >= total:
+            fa, fb = f(lam_lo), f(p)
+            lam = lam_lo if fb == fa else lam_lo + (total - fa) * (p - lam_lo) / (fb - fa)
+            return [min(max(lam * wl, lo), hi) for wl in w]
+        lam_lo = p
+    return [min(max(lam_lo * wl, lo), hi) for wl in w]
+
+
+# --------------------------------------------------------------------------- selection
+def kept_positions(score_seg, n, window, budget):
+    """Kept token positions of one (sequence, layer, KV head) segment, ascending.
+
+    Candidates are positions [0, n - W). The k = min(b - W, n - W) candidates with
+    the largest scores are kept, ties broken towards the lower position (a full
+    sort on (-score, position)), together with the recent window [n - W, n).
+    """
+    cand = n - window
+    k = min(max(budget - window, 0), cand)
+    sc = np.asarray(score_seg[:cand])
+    order = np.lexsort((np.arange(cand), -sc))
+    chosen = order[:k]
+    return np.sort(np.concatenate([chosen, np.arange(cand, n)])).astype(np.int32)
+
+
+def gather(k_seg, v_seg, positions):
+    """Naive gather of the kept rows (RippleKV Eq. 4)."""
+    ko = np.empty((len(positions),) + k_seg.shape[1:], dtype=k_seg.dtype)
+    vo = np.empty((len(positions),) + v_seg.shape[1:], dtype=v_seg.dtype)
+    for r, p in enumerate(positions):
+        ko[r] = k_seg[p]
+        vo[r] = v_seg[p]
+    return ko, vo

@@ -1,0 +1,192 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+* Brute-force single-token removal (DropKV page, "Methodology in Plain English":
+  deleting a token renormalises the softmax over the survivors): recomputing the
+  output without token j must give a shift equal to the oracle's
+  p_j/(1-p_j)*||a - v_j|| (Key Contribution 1) for every visible (row, token).
+* Closed forms: two visible keys, identical keys, constant values.
+* Structure: window/head sums are linear (a unit equals the sum of its single
+  rows), the squared mode equals the square of the L2 mode for one row, the
+  argmax and its term.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+
+
+def bf16_bits(x):
+    t = torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def bits_f64(b):
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def make_unit(rng, G, W, d, n, qscale=1.0, kscale=1.0):
+    q = bf16_bits(rng.standard_normal((1, 1, G, W, d)) * qscale)
+    k = bf16_bits(rng.standard_normal((1, 1, n, d)) * kscale)
+    v = bf16_bits(rng.standard_normal((1, 1, n, d)))
+    return q, k, v
+
+
+def run_oracle(q, k, v, G, W, d, n, mode=0, rows=False):
+    return oracle.scores(q, k, v, num_seqs=1, num_layers=1, num_q_heads=G, num_kv_heads=1, head_dim=d,
+                         window=W, cu_seqlens=[0, n], mode=mode, want_rows=rows)
+
+
+CASES = [(1, 1, 4, 2), (1, 1, 8, 5), (2, 1, 8, 9), (1, 3, 4, 4), (2, 2, 8, 17), (3, 4, 16, 40), (2, 4, 8, 33)]
+
+
+@pytest.mark.parametrize("G,W,d,n", CASES)
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("qscale", [1.0, 4.0])
+def test_removal_identity_matches_brute_force(G, W, d, n, mode, qscale):
+    rng = np.random.default_rng(1000 * G + 100 * W + 10 * d + n + int(qscale))
+    q, k, v = make_unit(rng, G, W, d, n, qscale=qscale)
+    got = run_oracle(q, k, v, G, W, d, n, mode=mode)["score"][0, 0]
+    ref = brute.unit_scores(bits_f64(q).reshape(G * W, d), bits_f64(k).reshape(n, d), bits_f64(v).reshape(n, d),
+                            W, 1.0 / math.sqrt(d), mode=mode)
+    np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-14)
+    assert (got >= 0).all()
+
+
+def test_multi_unit_indexing_matches_brute_force():
+    """Ragged sequences, several layers and KV heads: every unit equals its own brute force."""
+    rng = np.random.default_rng(7)
+    S, L, Hkv, G, W, d = 2, 2, 2, 2, 3, 8
+    Hq = Hkv * G
+    ns = [11, 7]
+    cu = [0, 11, 18]
+    N = cu[-1]
+    q = bf16_bits(rng.standard_normal((L, S, Hq, W, d)) * 2)
+    k = bf16_bits(rng.standard_normal((L, Hkv, N, d)))
+    v = bf16_bits(rng.standard_normal((L, Hkv, N, d)))
+    out = oracle.scores(q, k, v, num_seqs=S, num_layers=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                        window=W, cu_seqlens=cu)["score"]
+    qf, kf, vf = bits_f64(q), bits_f64(k), bits_f64(v)
+    for s in range(S):
+        for l in range(L):
+            for g in range(Hkv):
+                rows = qf[l, s, g * G:(g + 1) * G].reshape(G * W, d)
+                ref = brute.unit_scores(rows, kf[l, g, cu[s]:cu[s + 1]], vf[l, g, cu[s]:cu[s + 1]], W,
+                                        1 / math.sqrt(d))
+                np.testing.assert_allclose(out[l, g, cu[s]:cu[s + 1]], ref, rtol=1e-9, atol=1e-14)
+
+
+def test_units_subset_only_touches_requested():
+    rng = np.random.default_rng(3)
+    S, L, Hkv, G, W, d = 1, 2, 2, 1, 2, 4
+    n = 9
+    q = bf16_bits(rng.standard_normal((L, S, Hkv * G, W, d)))
+    k = bf16_bits(rng.standard_normal((L, Hkv, n, d)))
+    v = bf16_bits(rng.standard_normal((L, Hkv, n, d)))
+    kw = dict(num_seqs=S, num_layers=L, num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=d, window=W,
+              cu_seqlens=[0, n])
+    full = oracle.scores(q, k, v, **kw)["score"]
+    part = oracle.scores(q, k, v, units=[3], **kw)["score"]  # unit 3 = (s0, l1, g1)
+    np.testing.assert_array_equal(part[1, 1], full[1, 1])
+    assert np.isnan(part[0]).all() and np.isnan(part[1, 0]).all()
+
+
+def test_two_visible_keys_closed_form():
+    """n = 2, one row: a - v_0 = p_1 (v_1 - v_0), so term_0 = p_0 ||v_1 - v_0|| and term_1 = p_1 ||v_1 - v_0||."""
+    rng = np.random.default_rng(11)
+    d = 8
+    for trial in range(5):
+        q, k, v = make_unit(rng, 1, 1, d, 2, qscale=2.0)
+        got = run_oracle(q, k, v, 1, 1, d, 2)["score"][0, 0]
+        qf, kf, vf = bits_f64(q).reshape(d), bits_f64(k).reshape(2, d), bits_f64(v).reshape(2, d)
+        s0, s1 = (kf @ qf) / math.sqrt(d)
+        p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        dist = math.sqrt(((vf[1] - vf[0]) ** 2).sum())
+        np.testing.assert_allclose(got, [p0 * dist, (1 - p0) * dist], rtol=1e-12)
+
+
+def test_identical_keys_closed_form():
+    """m identical visible keys: p = 1/m, a = mean(v), term_j = ||mean(v) - v_j|| / (m - 1)."""
+    rng = np.random.default_rng(12)
+    d, n = 8, 10
+    q = bf16_bits(rng.standard_normal((1, 1, 1, 1, d)))
+    krow = rng.standard_normal(d)
+    k = bf16_bits(np.tile(krow, (1, 1, n, 1)))
+    v = bf16_bits(rng.standard_normal((1, 1, n, d)))
+    got = run_oracle(q, k, v, 1, 1, d, n)["score"][0, 0]
+    vf = bits_f64(v).reshape(n, d)
+    vbar = vf.mean(axis=0)
+    ref = np.sqrt(((vbar - vf) ** 2).sum(axis=1)) / (n - 1)
+    np.testing.assert_allclose(got, ref, rtol=1e-12)
+
+
+def test_constant_values_give_zero_scores():
+    rng = np.random.default_rng(13)
+    G, W, d, n = 2, 3, 8, 20
+    q, k, _ = make_unit(rng, G, W, d, n)
+    v = bf16_bits(np.tile(rng.standard_normal(d), (1, 1, n, 1)))
+    got = run_oracle(q, k, v, G, W, d, n)["score"][0, 0]
+    assert np.abs(got).max() < 1e-15
+
+
+def test_squared_mode_is_square_of_l2_for_one_row():
+    rng = np.random.default_rng(14)
+    d, n = 16, 30
+    q, k, v = make_unit(rng, 1, 1, d, n, qscale=3.0)
+    l2 = run_oracle(q, k, v, 1, 1, d, n, mode=0)["score"][0, 0]
+    sq = run_oracle(q, k, v, 1, 1, d, n, mode=1)["score"][0, 0]
+    np.testing.assert_allclose(sq, l2 * l2, rtol=1e-12)
+    # identical ranking with one row
+    assert (np.argsort(-sq[:-1], kind="stable") == np.argsort(-l2[:-1], kind="stable")).all()
+
+
+def test_window_and_head_sum_is_linear():
+    """A G-head, W-row unit equals the sum of single-row problems truncated at each row's position."""
+    rng = np.random.default_rng(15)
+    G, W, d, n = 3, 4, 8, 25
+    q, k, v = make_unit(rng, G, W, d, n, qscale=2.0)
+    full = run_oracle(q, k, v, G, W, d, n)["score"][0, 0]
+    acc = np.zeros(n)
+    qr = q.reshape(G, W, d)
+    for h in range(G):
+        for i in range(W):
+            t = n - W + i
+            one = run_oracle(qr[h, i].reshape(1, 1, 1, 1, d).copy(), k[:, :, :t + 1].copy(), v[:, :, :t + 1].copy(),
+                             1, 1, d, t + 1)["score"][0, 0]
+            acc[:t + 1] += one
+    np.testing.assert_allclose(full, acc, rtol=1e-12)
+
+
+def test_rows_argmax_lse_and_dominant_term():
+    rng = np.random.default_rng(16)
+    G, W, d, n = 2, 3, 8, 21
+    q, k, v = make_unit(rng, G, W, d, n, qscale=3.0)
+    # a duplicated key: the argmax tie must resolve to the lower index
+    kk = k.reshape(n, d)
+    kk[9] = kk[4]
+    out = run_oracle(q, k, v, G, W, d, n, rows=True)
+    qf, kf, vf = bits_f64(q).reshape(G * W, d), bits_f64(kk), bits_f64(v).reshape(n, d)
+    for r in range(G * W):
+        t = n - W + r % W
+        logits = kf[:t + 1] @ qf[r] / math.sqrt(d)
+        j = int(out["jstar"][r])
+        assert logits[j] == logits.max() and j == int(np.flatnonzero(logits == logits.max())[0])
+        # sum_j exp(s_j - LSE) = 1
+        assert abs(np.exp(logits - out["lse"][r]).sum() - 1.0) < 1e-12
+        # the dominant term is the brute-force shift of removing j*
+        sh = brute.removal_shifts(qf[r], kf[:t + 1], vf[:t + 1], 1 / math.sqrt(d))
+        np.testing.assert_allclose(out["dom"][r], sh[j], rtol=1e-9)
+    assert (out["pmax"] <= 1.0).all() and (out["pmax"] > 0).all()
+
+
+def test_sizes_match_the_pages_formulas():
+    """PyramidKV page sizing formula 2*2*L*H*D*N bytes; DropKV scratch figures (n = 128K)."""
+    from kv_cache_eviction_kvscore_amd.configs import WORKLOADS
+    assert WORKLOADS[4].kv_bytes() == 2 * 2 * 32 * 8 * 128 * 131072 == 17_179_869_184
+    # fused scratch: one fp32 partial per (query head, token): 32 * 131072 * 4 B = 16 MiB (~17 MB)
+    assert 32 * 131072 * 4 == 16 * 2 ** 20
+    # naive intermediates w x n x d per query head at w = 8, bf16: 8 GiB (~9 GB)
+    assert 8 * 131072 * 128 * 32 * 2 == 8 * 2 ** 30
