@@ -1,0 +1,260 @@
+"""ctypes binding over libkvscore.so (include/kvscore.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels (or, for
+``budget`` and ``segment_offsets``, its host code). Tensors are torch tensors; the
+binding passes ``data_ptr()`` and torch's current HIP stream. The library must be
+built (``python -m kv_cache_eviction_kvscore_amd.build`` or ``__graft_entry__.build``);
+loading fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvscore.so")
+
+MODE_L2 = 0
+MODE_SQ = 1
+WS_ATTN_FWD = 0
+WS_SCORE = 1
+WS_TOPK = 2
+ERRORS = {1: "EINVAL", 2: "EWORKSPACE", 3: "EBUDGET", 4: "EDEVICE"}
+
+
+class KvscoreError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"kvscore {ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_layers", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("cu_seqlens", ctypes.POINTER(ctypes.c_int64)),
+        ("k_strides", ctypes.c_int64 * 3),
+        ("v_strides", ctypes.c_int64 * 3),
+        ("mode", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+EXPORTS = (
+    "kvscore_version", "kvscore_last_error", "kvscore_num_query_tiles", "kvscore_workspace_size",
+    "kvscore_attn_fwd", "kvscore_score", "kvscore_merge", "kvscore_budget", "kvscore_segment_offsets",
+    "kvscore_topk", "kvscore_compact",
+)
+
+_lib = None
+
+
+def load():
+    """Load libkvscore.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with kv_cache_eviction_kvscore_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(_Problem)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "kvscore_version": (i32, []),
+        "kvscore_last_error": (ctypes.c_char_p, []),
+        "kvscore_num_query_tiles": (i32, [P]),
+        "kvscore_workspace_size": (sz, [P, i32]),
+        "kvscore_attn_fwd": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "kvscore_score": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "kvscore_merge": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
+        "kvscore_budget": (ctypes.c_int, [vp, i32, ctypes.c_double, ctypes.c_double, i64, i32, i32, vp]),
+        "kvscore_segment_offsets": (ctypes.c_int, [P, vp, vp]),
+        "kvscore_topk": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
+        "kvscore_compact": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise KvscoreError(rc, load().kvscore_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Problem:
+    """Shape, strides and options of one call (mirrors ``kvscore_problem``)."""
+
+    def __init__(self, *, num_seqs, num_layers, num_q_heads, num_kv_heads, head_dim, window, cu_seqlens,
+                 k_strides, v_strides, mode=MODE_L2, softmax_scale=0.0):
+        self.cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        assert len(self.cu) == num_seqs + 1
+        self.c = _Problem(num_seqs, num_layers, num_q_heads, num_kv_heads, head_dim, window,
+                          self.cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                          (ctypes.c_int64 * 3)(*k_strides), (ctypes.c_int64 * 3)(*v_strides), mode,
+                          float(softmax_scale))
+        self.num_seqs, self.num_layers = num_seqs, num_layers
+        self.num_q_heads, self.num_kv_heads = num_q_heads, num_kv_heads
+        self.head_dim, self.window, self.mode = head_dim, window, mode
+
+    @classmethod
+    def for_tensors(cls, k: torch.Tensor, v: torch.Tensor, *, num_q_heads, window, cu_seqlens, mode=MODE_L2,
+                    softmax_scale=0.0):
+        """k, v: [L][Hkv][N][d] views (any strides with a unit-stride last dim)."""
+        L, Hkv, N, d = k.shape
+        return cls(num_seqs=len(cu_seqlens) - 1, num_layers=L, num_q_heads=num_q_heads, num_kv_heads=Hkv,
+                   head_dim=d, window=window, cu_seqlens=cu_seqlens, k_strides=tuple(k.stride()[:3]),
+                   v_strides=tuple(v.stride()[:3]), mode=mode, softmax_scale=softmax_scale)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+    @property
+    def units(self) -> int:
+        return self.num_layers * self.num_seqs * self.num_kv_heads
+
+    @property
+    def rows(self) -> int:
+        return self.units * (self.num_q_heads // self.num_kv_heads) * self.window
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu[-1])
+
+    def seqlen(self, s: int) -> int:
+        return int(self.cu[s + 1] - self.cu[s])
+
+    def num_query_tiles(self) -> int:
+        t = load().kvscore_num_query_tiles(self.ref)
+        if t == 0:
+            _check(1)
+        return int(t)
+
+    def workspace_size(self, which: int) -> int:
+        return int(load().kvscore_workspace_size(self.ref, which))
+
+
+def _need(t, nelem: int, dtype, name: str, device=True):
+    """Refuse tensors too small (or of the wrong type/device) for what the kernels address."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.untyped_storage().nbytes() - t.storage_offset() * t.element_size() < nelem * t.element_size():
+        raise ValueError(f"{name}: needs {nelem} elements")
+
+
+def _kv_extent(p: Problem, strides) -> int:
+    return ((p.num_layers - 1) * strides[0] + (p.num_kv_heads - 1) * strides[1]
+            + (p.total_tokens - 1) * strides[2] + p.head_dim)
+
+
+def _check_inputs(p: Problem, q, k, v):
+    _need(q, p.rows * p.head_dim, torch.bfloat16, "q_win")
+    if not q.is_contiguous():
+        raise ValueError("q_win must be contiguous [L][S][Hq][W][d]")
+    _need(k, _kv_extent(p, p.c.k_strides), torch.bfloat16, "k")
+    _need(v, _kv_extent(p, p.c.v_strides), torch.bfloat16, "v")
+
+
+def _check_rows(p: Problem, **tensors):
+    for name, (t, per_row, dt) in tensors.items():
+        _need(t, p.rows * per_row, dt, name)
+
+
+def version() -> int:
+    return int(load().kvscore_version())
+
+
+def attn_fwd(p: Problem, q, k, v, a, lse, jstar, dom, ws, stream=None):
+    _check_inputs(p, q, k, v)
+    _check_rows(p, a=(a, p.head_dim, torch.float32), lse=(lse, 1, torch.float32), jstar=(jstar, 1, torch.int32),
+                dom=(dom, 1, torch.float32))
+    _check(load().kvscore_attn_fwd(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(lse), _ptr(jstar), _ptr(dom),
+                                   _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def score(p: Problem, q, k, v, a, lse, jstar, partial, ws, stream=None):
+    _check_inputs(p, q, k, v)
+    _check_rows(p, a=(a, p.head_dim, torch.float32), lse=(lse, 1, torch.float32), jstar=(jstar, 1, torch.int32))
+    _need(partial, p.num_layers * p.num_kv_heads * p.num_query_tiles() * p.total_tokens, torch.float32, "partial")
+    _check(load().kvscore_score(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(lse), _ptr(jstar), _ptr(partial),
+                                _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def merge(p: Problem, partial, jstar, dom, score_out, stream=None):
+    _need(partial, p.num_layers * p.num_kv_heads * p.num_query_tiles() * p.total_tokens, torch.float32, "partial")
+    _check_rows(p, jstar=(jstar, 1, torch.int32), dom=(dom, 1, torch.float32))
+    _need(score_out, p.num_layers * p.num_kv_heads * p.total_tokens, torch.float32, "score")
+    _check(load().kvscore_merge(p.ref, _ptr(partial), _ptr(jstar), _ptr(dom), _ptr(score_out), _stream(stream)))
+
+
+def budget(sens: Sequence[float], ratio: float, gamma: float, total: int, lo: int, hi: int) -> np.ndarray:
+    """Host-only layer budgets for one sequence."""
+    s = np.ascontiguousarray(np.asarray(sens, dtype=np.float64))
+    out = np.zeros(len(s), dtype=np.int32)
+    g = math.inf if gamma is None else float(gamma)
+    _check(load().kvscore_budget(ctypes.c_void_p(s.ctypes.data), len(s), float(ratio), g, int(total), int(lo),
+                                 int(hi), ctypes.c_void_p(out.ctypes.data)))
+    return out
+
+
+def segment_offsets(p: Problem, budgets: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(np.asarray(budgets, dtype=np.int32))
+    assert b.shape == (p.num_seqs, p.num_layers)
+    off = np.zeros(p.units + 1, dtype=np.int64)
+    _check(load().kvscore_segment_offsets(p.ref, ctypes.c_void_p(b.ctypes.data), ctypes.c_void_p(off.ctypes.data)))
+    return off
+
+
+def _check_segments(p: Problem, b: np.ndarray, seg_off_dev) -> int:
+    """Host offsets from the budgets; the device copy must have their size. Returns the packed row count."""
+    off = segment_offsets(p, b)
+    _need(seg_off_dev, p.units + 1, torch.int64, "seg_offsets")
+    return int(off[-1])
+
+
+def topk(p: Problem, score_t, budgets: np.ndarray, seg_off_dev, kept, stream=None):
+    b = np.ascontiguousarray(np.asarray(budgets, dtype=np.int32))
+    R = _check_segments(p, b, seg_off_dev)
+    _need(score_t, p.num_layers * p.num_kv_heads * p.total_tokens, torch.float32, "score")
+    _need(kept, R, torch.int32, "kept_pos")
+    _check(load().kvscore_topk(p.ref, _ptr(score_t), ctypes.c_void_p(b.ctypes.data), _ptr(seg_off_dev), _ptr(kept),
+                               None, 0, _stream(stream)))
+
+
+def compact(p: Problem, k, v, budgets: np.ndarray, seg_off_dev, kept, k_out, v_out, stream=None):
+    b = np.ascontiguousarray(np.asarray(budgets, dtype=np.int32))
+    R = _check_segments(p, b, seg_off_dev)
+    _need(k, _kv_extent(p, p.c.k_strides), torch.bfloat16, "k")
+    _need(v, _kv_extent(p, p.c.v_strides), torch.bfloat16, "v")
+    _need(kept, R, torch.int32, "kept_pos")
+    _need(k_out, R * p.head_dim, torch.bfloat16, "k_out")
+    _need(v_out, R * p.head_dim, torch.bfloat16, "v_out")
+    _check(load().kvscore_compact(p.ref, _ptr(k), _ptr(v), ctypes.c_void_p(b.ctypes.data), _ptr(seg_off_dev),
+                                  _ptr(kept), _ptr(k_out), _ptr(v_out), _stream(stream)))

@@ -1,0 +1,344 @@
+// libkvscore host glue: argument validation, launch sizing, workspace sizes, the
+// host-only layer-budget map, and the C ABI declared in include/kvscore.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/kvscore.h"
+#include "kvs_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return KVSCORE_OK;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+int64_t next_pow2(int64_t x) {
+  int64_t r = 1;
+  while (r < x) r <<= 1;
+  return r;
+}
+
+// Validate the problem and fill the kernels' view of it.
+int make_dev(const kvscore_problem* p, kvs::Dev& d) {
+  if (!p) return fail(KVSCORE_EINVAL, "problem is NULL");
+  if (p->num_seqs < 1 || p->num_seqs > KVSCORE_MAX_SEQS)
+    return fail(KVSCORE_EINVAL, "num_seqs=%d outside [1, %d]", p->num_seqs, KVSCORE_MAX_SEQS);
+  if (p->num_layers < 1) return fail(KVSCORE_EINVAL, "num_layers=%d < 1", p->num_layers);
+  if (p->num_kv_heads < 1 || p->num_q_heads < p->num_kv_heads || p->num_q_heads % p->num_kv_heads != 0)
+    return fail(KVSCORE_EINVAL, "num_q_heads=%d must be a positive multiple of num_kv_heads=%d", p->num_q_heads,
+                p->num_kv_heads);
+  if (p->head_dim != 64 && p->head_dim != 128) return fail(KVSCORE_EINVAL, "head_dim=%d not in {64, 128}", p->head_dim);
+  if (p->window < 1) return fail(KVSCORE_EINVAL, "window=%d < 1", p->window);
+  const int G = p->num_q_heads / p->num_kv_heads;
+  if ((int64_t)G * p->window > KVSCORE_MAX_ROWS)
+    return fail(KVSCORE_EINVAL, "G*W=%lld query rows per unit exceeds %d", (long long)G * p->window, KVSCORE_MAX_ROWS);
+  if (p->mode != KVSCORE_MODE_L2 && p->mode != KVSCORE_MODE_SQ) return fail(KVSCORE_EINVAL, "mode=%d", p->mode);
+  if (!p->cu_seqlens) return fail(KVSCORE_EINVAL, "cu_seqlens is NULL");
+  if (p->cu_seqlens[0] != 0) return fail(KVSCORE_EINVAL, "cu_seqlens[0] must be 0");
+  int64_t max_n = 0;
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int64_t n = p->cu_seqlens[s + 1] - p->cu_seqlens[s];
+    if (n <= p->window) return fail(KVSCORE_EINVAL, "sequence %d has length %lld <= window %d", s, (long long)n, p->window);
+    if (n >= (int64_t)1 << 30) return fail(KVSCORE_EINVAL, "sequence %d too long", s);
+    max_n = std::max(max_n, n);
+  }
+  for (int t = 0; t < 3; ++t)
+    if (p->k_strides[t] < 0 || p->v_strides[t] < 0 || p->k_strides[t] % 8 || p->v_strides[t] % 8)
+      return fail(KVSCORE_EINVAL, "k/v strides must be non-negative multiples of 8 elements (16 bytes)");
+  if (p->k_strides[2] < p->head_dim || p->v_strides[2] < p->head_dim)
+    return fail(KVSCORE_EINVAL, "token stride smaller than head_dim");
+
+  d = kvs::Dev{};
+  d.S = p->num_seqs;
+  d.L = p->num_layers;
+  d.Hq = p->num_q_heads;
+  d.Hkv = p->num_kv_heads;
+  d.G = G;
+  d.d = p->head_dim;
+  d.W = p->window;
+  d.R = G * p->window;
+  d.Tq = (d.R + kvs::kRowsPerTileMax - 1) / kvs::kRowsPerTileMax;
+  d.RT = ((d.R + d.Tq - 1) / d.Tq + 31) / 32 * 32;
+  d.mode = p->mode;
+  d.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  d.c1 = (float)((double)d.scale * 1.4426950408889634);
+  d.ksl = p->k_strides[0];
+  d.ksh = p->k_strides[1];
+  d.kst = p->k_strides[2];
+  d.vsl = p->v_strides[0];
+  d.vsh = p->v_strides[1];
+  d.vst = p->v_strides[2];
+  d.N = p->cu_seqlens[p->num_seqs];
+  d.U = d.L * d.S * d.Hkv;
+  d.max_n = max_n;
+  for (int s = 0; s <= p->num_seqs; ++s) d.cu[s] = p->cu_seqlens[s];
+  // Chunk sizes: aim at ~2048 key-chunk workgroups per launch (8 per CU on 256 CUs).
+  int64_t keys = 0;
+  for (int s = 0; s < p->num_seqs; ++s) keys += (p->cu_seqlens[s + 1] - p->cu_seqlens[s]);
+  keys *= (int64_t)d.L * d.Hkv * d.Tq;
+  const int64_t target = std::min<int64_t>(65536, std::max<int64_t>(1024, next_pow2((keys + 2047) / 2048)));
+  d.fwd_chunk = (int)target;
+  d.score_chunk = (int)target;
+  d.fwd_chunks = (int)((max_n + d.fwd_chunk - 1) / d.fwd_chunk);
+  d.score_chunks = (int)((max_n + d.score_chunk - 1) / d.score_chunk);
+  return ok();
+}
+
+size_t ws_attn(const kvs::Dev& d) {
+  return (size_t)d.U * d.Tq * d.fwd_chunks * kvs::fwd_block_floats(d.RT, d.d) * sizeof(float);
+}
+size_t ws_score(const kvs::Dev& d) { return kvs::prep_bytes((int64_t)d.U * d.R, d.d); }
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KVSCORE_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return ok();
+  if (!ws) return fail(KVSCORE_EWORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (!aligned(ws, 256)) return fail(KVSCORE_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(KVSCORE_EWORKSPACE, "workspace has %zu bytes, need %zu", have, need);
+  return ok();
+}
+
+int check_budgets(const kvscore_problem* p, const int32_t* budgets, int* max_b) {
+  if (!budgets) return fail(KVSCORE_EINVAL, "budgets is NULL");
+  int mb = 0;
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int64_t n = p->cu_seqlens[s + 1] - p->cu_seqlens[s];
+    for (int l = 0; l < p->num_layers; ++l) {
+      const int32_t b = budgets[(int64_t)s * p->num_layers + l];
+      if (b < p->window || b > n)
+        return fail(KVSCORE_EBUDGET, "budget[%d][%d]=%d outside [window=%d, n=%lld]", s, l, b, p->window, (long long)n);
+      mb = std::max(mb, (int)b);
+    }
+  }
+  if (max_b) *max_b = mb;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvscore_version(void) { return 100; }
+
+const char* kvscore_last_error(void) { return g_err.c_str(); }
+
+int32_t kvscore_num_query_tiles(const kvscore_problem* p) {
+  kvs::Dev d;
+  if (make_dev(p, d)) return 0;
+  return d.Tq;
+}
+
+size_t kvscore_workspace_size(const kvscore_problem* p, int32_t which) {
+  kvs::Dev d;
+  if (make_dev(p, d)) return 0;
+  switch (which) {
+    case KVSCORE_WS_ATTN_FWD:
+      return ws_attn(d);
+    case KVSCORE_WS_SCORE:
+      return ws_score(d);
+    case KVSCORE_WS_TOPK:
+      return 0;
+    default:
+      fail(KVSCORE_EINVAL, "unknown workspace kind %d", which);
+      return 0;
+  }
+}
+
+int kvscore_attn_fwd(const kvscore_problem* p, const void* q_win, const void* k, const void* v, float* a, float* lse,
+                     int32_t* jstar, float* dom, void* workspace, size_t workspace_bytes, void* stream) {
+  kvs::Dev d;
+  if (int rc = make_dev(p, d)) return rc;
+  if (!q_win || !k || !v || !a || !lse || !jstar || !dom) return fail(KVSCORE_EINVAL, "NULL tensor argument");
+  if (!aligned(q_win, 16) || !aligned(k, 16) || !aligned(v, 16)) return fail(KVSCORE_EINVAL, "q/k/v not 16-byte aligned");
+  if (!aligned(a, 4) || !aligned(lse, 4) || !aligned(jstar, 4) || !aligned(dom, 4))
+    return fail(KVSCORE_EINVAL, "outputs not 4-byte aligned");
+  if (int rc = check_ws(workspace, workspace_bytes, ws_attn(d))) return rc;
+  return launched(kvs::launch_attn_fwd(d, q_win, k, v, a, lse, jstar, dom, workspace, (hipStream_t)stream),
+                  "kvscore_attn_fwd");
+}
+
+int kvscore_score(const kvscore_problem* p, const void* q_win, const void* k, const void* v, const float* a,
+                  const float* lse, const int32_t* jstar, float* partial, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  kvs::Dev d;
+  if (int rc = make_dev(p, d)) return rc;
+  if (!q_win || !k || !v || !a || !lse || !jstar || !partial) return fail(KVSCORE_EINVAL, "NULL tensor argument");
+  if (!aligned(q_win, 16) || !aligned(k, 16) || !aligned(v, 16)) return fail(KVSCORE_EINVAL, "q/k/v not 16-byte aligned");
+  if (!aligned(a, 4) || !aligned(lse, 4) || !aligned(jstar, 4) || !aligned(partial, 4))
+    return fail(KVSCORE_EINVAL, "buffers not 4-byte aligned");
+  if (int rc = check_ws(workspace, workspace_bytes, ws_score(d))) return rc;
+  return launched(kvs::launch_score(d, q_win, k, v, a, lse, jstar, partial, workspace, (hipStream_t)stream),
+                  "kvscore_score");
+}
+
+int kvscore_merge(const kvscore_problem* p, const float* partial, const int32_t* jstar, const float* dom, float* score,
+                  void* stream) {
+  kvs::Dev d;
+  if (int rc = make_dev(p, d)) return rc;
+  if (!partial || !jstar || !dom || !score) return fail(KVSCORE_EINVAL, "NULL tensor argument");
+  return launched(kvs::launch_merge(d, partial, jstar, dom, score, (hipStream_t)stream), "kvscore_merge");
+}
+
+int kvscore_budget(const double* sens, int32_t num_layers, double ratio, double gamma, int64_t total, int32_t lo,
+                   int32_t hi, int32_t* budgets_out) {
+  if (!sens || !budgets_out) return fail(KVSCORE_EINVAL, "NULL argument");
+  if (num_layers < 1) return fail(KVSCORE_EINVAL, "num_layers=%d < 1", num_layers);
+  if (!(ratio >= 1.0) || !std::isfinite(ratio)) return fail(KVSCORE_EINVAL, "ratio must be finite and >= 1");
+  if (std::isnan(gamma) || (gamma > 0 && gamma < 1.0)) return fail(KVSCORE_EINVAL, "gamma must be >= 1 (or <= 0 / inf)");
+  if (lo < 0 || hi < lo) return fail(KVSCORE_EINVAL, "need 0 <= lo <= hi");
+  const int L = num_layers;
+  if (total < (int64_t)L * lo || total > (int64_t)L * hi)
+    return fail(KVSCORE_EBUDGET, "total %lld outside [L*lo, L*hi] = [%lld, %lld]", (long long)total, (long long)L * lo,
+                (long long)L * hi);
+  for (int l = 0; l < L; ++l)
+    if (!std::isfinite(sens[l])) return fail(KVSCORE_EINVAL, "sensitivity %d not finite", l);
+
+  // Eq. 9: min-max normalisation, a constant profile gives s_hat = 0.
+  double smin = sens[0], smax = sens[0];
+  for (int l = 1; l < L; ++l) {
+    smin = std::min(smin, sens[l]);
+    smax = std::max(smax, sens[l]);
+  }
+  std::vector<double> w(L);
+  const double lr = std::log(ratio);
+  for (int l = 0; l < L; ++l) {
+    const double shat = (smax == smin) ? 0.0 : (sens[l] - smin) / (smax - smin);
+    w[l] = std::exp(lr * shat);  // Eq. 10
+  }
+  // Eq. 11: clip to [1/gamma, gamma], rescale to mean one.
+  if (gamma > 0 && std::isfinite(gamma))
+    for (int l = 0; l < L; ++l) w[l] = std::min(std::max(w[l], 1.0 / gamma), gamma);
+  double sum = 0.0;
+  for (int l = 0; l < L; ++l) sum += w[l];
+  const double mean = sum / L;
+  for (int l = 0; l < L; ++l) w[l] /= mean;
+  // Eq. 12 targets.
+  std::vector<double> x(L);
+  bool inside = true;
+  for (int l = 0; l < L; ++l) {
+    x[l] = (double)total / L * w[l];
+    inside = inside && x[l] >= lo && x[l] <= hi;
+  }
+  if (!inside) {
+    // x_l = clip(lam * w_l, lo, hi) with sum = total: f(lam) is nondecreasing and piecewise
+    // linear; walk its breakpoints and solve on the segment that reaches the total.
+    std::vector<double> bp;
+    for (int l = 0; l < L; ++l) {
+      bp.push_back(lo / w[l]);
+      bp.push_back(hi / w[l]);
+    }
+    std::sort(bp.begin(), bp.end());
+    auto f = [&](double lam) {
+      double t = 0;
+      for (int l = 0; l < L; ++l) t += std::min(std::max(lam * w[l], (double)lo), (double)hi);
+      return t;
+    };
+    double a = 0.0, lam = bp.back();
+    for (double b : bp) {
+      const double fb = f(b);
+      if (fb >= (double)total) {
+        const double fa = f(a);
+        lam = (fb == fa) ? a : a + ((double)total - fa) * (b - a) / (fb - fa);
+        break;
+      }
+      a = b;
+    }
+    for (int l = 0; l < L; ++l) x[l] = std::min(std::max(lam * w[l], (double)lo), (double)hi);
+  }
+  // Largest remainder so that the integers sum to the total (Eq. 5); ties to the lower layer.
+  std::vector<int64_t> base(L);
+  std::vector<double> rem(L);
+  int64_t assigned = 0;
+  for (int l = 0; l < L; ++l) {
+    base[l] = (int64_t)std::floor(x[l]);
+    rem[l] = x[l] - (double)base[l];
+    assigned += base[l];
+  }
+  std::vector<int> order(L);
+  for (int l = 0; l < L; ++l) order[l] = l;
+  std::stable_sort(order.begin(), order.end(), [&](int i, int j) { return rem[i] > rem[j]; });
+  int64_t extra = total - assigned;
+  for (int i = 0; i < L && extra > 0; ++i) {
+    const int l = order[i];
+    if (base[l] < hi) {
+      ++base[l];
+      --extra;
+    }
+  }
+  // Rounding of the fp64 targets can leave the sum one off in either direction.
+  for (int l = L - 1; l >= 0 && extra < 0; --l)
+    if (base[l] > lo) {
+      --base[l];
+      ++extra;
+    }
+  if (extra != 0) return fail(KVSCORE_EBUDGET, "could not distribute the total");
+  for (int l = 0; l < L; ++l) budgets_out[l] = (int32_t)base[l];
+  return ok();
+}
+
+int kvscore_segment_offsets(const kvscore_problem* p, const int32_t* budgets, int64_t* offsets_out) {
+  kvs::Dev d;
+  if (int rc = make_dev(p, d)) return rc;
+  if (!offsets_out) return fail(KVSCORE_EINVAL, "offsets_out is NULL");
+  if (int rc = check_budgets(p, budgets, nullptr)) return rc;
+  int64_t acc = 0;
+  for (int u = 0; u < d.U; ++u) {
+    int l, s, g;
+    kvs::unit_coords(d, u, l, s, g);
+    offsets_out[u] = acc;
+    acc += budgets[(int64_t)s * d.L + l];
+  }
+  offsets_out[d.U] = acc;
+  return ok();
+}
+
+int kvscore_topk(const kvscore_problem* p, const float* score, const int32_t* budgets, const int64_t* seg_offsets,
+                 int32_t* kept_pos, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  kvs::Dev d;
+  if (int rc = make_dev(p, d)) return rc;
+  if (!score || !seg_offsets || !kept_pos) return fail(KVSCORE_EINVAL, "NULL tensor argument");
+  if (int rc = check_budgets(p, budgets, nullptr)) return rc;
+  return launched(kvs::launch_topk(d, score, seg_offsets, kept_pos, (hipStream_t)stream), "kvscore_topk");
+}
+
+int kvscore_compact(const kvscore_problem* p, const void* k, const void* v, const int32_t* budgets,
+                    const int64_t* seg_offsets, const int32_t* kept_pos, void* k_out, void* v_out, void* stream) {
+  kvs::Dev d;
+  if (int rc = make_dev(p, d)) return rc;
+  if (!k || !v || !seg_offsets || !kept_pos || !k_out || !v_out) return fail(KVSCORE_EINVAL, "NULL tensor argument");
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16))
+    return fail(KVSCORE_EINVAL, "k/v/k_out/v_out not 16-byte aligned");
+  int max_b = 0;
+  if (int rc = check_budgets(p, budgets, &max_b)) return rc;
+  return launched(kvs::launch_compact(d, k, v, seg_offsets, kept_pos, k_out, v_out, max_b, (hipStream_t)stream),
+                  "kvscore_compact");
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal definitions shared by the libkvscore HIP sources (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvs {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+
+constexpr int kMaxSeqs = 64;
+constexpr int kRowsPerTileMax = 256;  // query rows one workgroup holds (8 waves x 32 rows)
+constexpr int kMergeChunk = 4096;     // tokens per merge workgroup
+constexpr int kCompactRows = 64;      // packed rows per compaction workgroup
+
+// Problem as the kernels see it (passed by value as a kernel argument).
+struct Dev {
+  int S, L, Hq, Hkv, G, d, W;
+  int R;       // rows per unit = G*W
+  int Tq;      // query tiles per unit
+  int RT;      // rows per query tile (multiple of 32, <= kRowsPerTileMax)
+  int mode;    // 0 = L2, 1 = SQ
+  float scale; // multiplies q.k
+  float c1;    // scale * log2(e)
+  int64_t ksl, ksh, kst, vsl, vsh, vst;  // element strides
+  int64_t N;                             // total tokens
+  int U;                                 // units = L*S*Hkv
+  int fwd_chunk;                         // keys per forward workgroup (multiple of 64)
+  int fwd_chunks;                        // max forward chunks over sequences
+  int score_chunk;                       // keys per score workgroup (multiple of 64)
+  int score_chunks;                      // max score chunks over sequences
+  int64_t max_n;                         // longest sequence
+  int64_t cu[kMaxSeqs + 1];
+};
+
+// unit u = (l*S + s)*Hkv + g
+__host__ __device__ inline void unit_coords(const Dev& p, int u, int& l, int& s, int& g) {
+  g = u % p.Hkv;
+  s = (u / p.Hkv) % p.S;
+  l = u / (p.Hkv * p.S);
+}
+
+// Forward split record block: [RT][d] fp32 O_rest | [RT][d] fp16 v* | [RT] m | [RT] m2 | [RT] l_rest | [RT] j*
+__host__ __device__ inline size_t fwd_block_floats(int RT, int d) { return (size_t)RT * d + (size_t)RT * d / 2 + 4 * (size_t)RT; }
+
+// Score-prep workspace: [rows][d] bf16 a_hat | [rows] fp32 ||a_hat||^2 | [rows] fp32 lse*log2(e)
+__host__ __device__ inline size_t prep_bytes(int64_t rows, int d) { return (size_t)rows * d * 2 + (size_t)rows * 8; }
+
+// Launchers (each .hip file owns its kernels). Return hipGetLastError() after launch.
+hipError_t launch_attn_fwd(const Dev& p, const void* q, const void* k, const void* v, float* a, float* lse,
+                           int32_t* jstar, float* dom, void* ws, hipStream_t st);
+hipError_t launch_score(const Dev& p, const void* q, const void* k, const void* v, const float* a,
+                        const float* lse, const int32_t* jstar, float* partial, void* ws, hipStream_t st);
+hipError_t launch_merge(const Dev& p, const float* partial, const int32_t* jstar, const float* dom, float* score,
+                        hipStream_t st);
+hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off, int32_t* kept, hipStream_t st);
+hipError_t launch_compact(const Dev& p, const void* k, const void* v, const int64_t* seg_off, const int32_t* kept,
+                          void* k_out, void* v_out, int max_budget, hipStream_t st);
+
+}  // namespace kvs

@@ -79,7 +79,7 @@ def scores(q, k, v, *, num_seqs, num_layers, num_q_heads, num_kv_heads, head_dim
     q: uint16 bf16 bits, [L][S][Hq][W][d]. k, v: uint16 bf16 bits addressed by
     ``kv_strides`` = (k_layer, k_head, k_token, v_layer, v_head, v_token) in
     elements (default: contiguous [L][Hkv][N][d]). A unit is
-    u = (s*L + l)*Hkv + g. Returns a dict with ``score`` [L][Hkv][N] (NaN where not
+    u = (l*S + s)*Hkv + g. Returns a dict with ``score`` [L][Hkv][N] (NaN where not
     computed) and, with ``want_rows``, per-row ``a``, ``lse``, ``jstar``, ``dom``
     (the argmax pair's term) in [L][S][Hq][W] order, plus ``pmax`` per unit.
     """

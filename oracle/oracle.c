@@ -188,7 +188,7 @@ static int unit_eval(const oracle_shape *sh, const uint16_t *q, const uint16_t *
 }
 
 /*
- * Evaluate a list of units u = (s*L + l)*Hkv + g (all units when units == NULL).
+ * Evaluate a list of units u = (l*S + s)*Hkv + g (all units when units == NULL).
  *   score : [L][Hkv][N] doubles; each selected unit's n_s entries are overwritten.
  *   a, lse, jstar, dom : per-row outputs in the [L][S][Hq][W](x d) layout, or NULL.
  *   pmax : [n_units or all] max softmax probability per unit, or NULL.
@@ -220,7 +220,7 @@ int oracle_eval(const int32_t *dims /* S,L,Hq,Hkv,d,W,mode */, const int64_t *cu
   for (int32_t ui = 0; ui < nu && rc == 0; ++ui) {
     const int32_t u = units ? units[ui] : ui;
     if (u < 0 || u >= total_units) { rc = -1; break; }
-    const int g = u % sh.Hkv, l = (u / sh.Hkv) % sh.L, s = u / (sh.Hkv * sh.L);
+    const int g = u % sh.Hkv, s = (u / sh.Hkv) % sh.S, l = u / (sh.Hkv * sh.S);
     const int64_t n = cu[s + 1] - cu[s];
     double *su = NULL;
     if (score) {

@@ -89,7 +89,7 @@ def test_units_subset_only_touches_requested():
     kw = dict(num_seqs=S, num_layers=L, num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=d, window=W,
               cu_seqlens=[0, n])
     full = oracle.scores(q, k, v, **kw)["score"]
-    part = oracle.scores(q, k, v, units=[3], **kw)["score"]  # unit 3 = (s0, l1, g1)
+    part = oracle.scores(q, k, v, units=[3], **kw)["score"]  # unit 3 = (l1, s0, g1)
     np.testing.assert_array_equal(part[1, 1], full[1, 1])
     assert np.isnan(part[0]).all() and np.isnan(part[1, 0]).all()
 
