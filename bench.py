@@ -1,0 +1,216 @@
+"""Benchmark: the whole eviction-scoring hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
+
+One step = kvscore_attn_fwd + kvscore_score + kvscore_merge + kvscore_topk +
+kvscore_compact over every (layer, KV head) of the workload, inputs already resident in
+HBM. The layer budgets (host map, O(L)) depend only on the profile and total, so they
+are computed once before timing and their host time is reported separately. Prints one
+JSON line (rank 0): whole-job scored prompt tokens/s, a roofline entry for the dominant
+kernel, per-call timings, and the CPU oracle timed on a bounded sample of units of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scored prompt tokens/sec (score+top-k+compact) at n=128K; % bf16 MFMA / HBM peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+CALLS = ("attn_fwd", "score", "merge", "topk", "compact")
+# the kernel files whose counters a committed traffic record describes
+KERNEL_SOURCES = {"score": "score.hip", "attn_fwd": "attn_fwd.hip", "compact": "compact.hip",
+                  "topk": "topk.hip", "merge": "merge.hip"}
+
+
+def algorithmic_work(w, budgets_rows: int, tq: int):
+    """Per-call algorithmic FLOP and HBM bytes for one step (the method's own work)."""
+    L, Hkv, G, d, W = w.num_layers, w.num_kv_heads, w.group, w.head_dim, w.window
+    # (row, key) pairs with the key visible to the row: row i of a unit sees n - W + i + 1 keys
+    pairs = sum(L * Hkv * G * (W * (n - W) + W * (W + 1) // 2) for n in w.seqlens)
+    N = w.total_tokens
+    rows = L * w.num_seqs * w.num_q_heads * W
+    kv = 2 * L * Hkv * N * d * 2  # K and V, bf16
+    q = rows * d * 2
+    th = L * Hkv * N  # (token, KV head, layer) triples
+    return {
+        "attn_fwd": {"flop": 4 * d * pairs, "bytes": kv + q + rows * (d * 4 + 12)},
+        "score": {"flop": 4 * d * pairs, "bytes": kv + q + rows * (d * 2 + 12) + 4 * tq * th},
+        "merge": {"flop": 0, "bytes": 4 * tq * th + 4 * th + rows * 8},
+        "topk": {"flop": 0, "bytes": 4 * th + 4 * budgets_rows},
+        "compact": {"flop": 0, "bytes": budgets_rows * (2 * 2 * d * 2 + 4)},
+        "pairs": pairs,
+    }
+
+
+def source_digest(name: str) -> str:
+    path = os.path.join(ROOT, "kv_cache_eviction_kvscore_amd", "csrc", KERNEL_SOURCES[name])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(name: str, workload: str):
+    """HBM traffic per launch from the committed counter record, if it still describes this kernel."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(workload, {}).get(name)
+    if not ent or ent.get("source_sha256_16") != source_digest(name):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, data, budgets, target_s: float, max_units: int):
+    """The oracle (as it stands) on a bounded sample of units: score + top-k + gather."""
+    import numpy as np
+    import oracle
+    from kv_cache_eviction_kvscore_amd import synth
+    cu = w.cu_seqlens()
+    U = w.num_layers * w.num_seqs * w.num_kv_heads
+    G, W, d = w.group, w.window, w.head_dim
+    R = G * W
+    rng = np.random.default_rng(12345)
+    order = rng.permutation(U)
+    spent, done, tokens_equiv = 0.0, 0, 0.0
+    for u in order[:max_units]:
+        g = u % w.num_kv_heads
+        s = (u // w.num_kv_heads) % w.num_seqs
+        l = u // (w.num_kv_heads * w.num_seqs)
+        n = w.seqlens[s]
+        q = synth.bf16_bits(data["q"].reshape(-1, d)[u * R:(u + 1) * R]).reshape(1, 1, G, W, d)
+        k = synth.bf16_bits(data["k"][l, g, cu[s]:cu[s + 1]]).reshape(1, 1, n, d)
+        v = synth.bf16_bits(data["v"][l, g, cu[s]:cu[s + 1]]).reshape(1, 1, n, d)
+        t0 = time.perf_counter()
+        sc = oracle.scores(q, k, v, num_seqs=1, num_layers=1, num_q_heads=G, num_kv_heads=1, head_dim=d,
+                           window=W, cu_seqlens=[0, n])["score"][0, 0]
+        kept = oracle.kept_positions(sc, n, W, int(budgets[s][l]))
+        oracle.gather(k.reshape(n, d), v.reshape(n, d), kept)
+        spent += time.perf_counter() - t0
+        done += 1
+        # this unit's share of the whole job's prompt tokens
+        tokens_equiv += n / (w.num_layers * w.num_kv_heads)
+        if spent >= target_s:
+            break
+    return {"value": tokens_equiv / spent, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} of {U} (layer, sequence, KV head) units of {w.name}, fp64 oracle score + full-sort "
+                      f"top-k + gather, {spent:.1f} s; tokens/s = the units' share of the prompt tokens / time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the path shards by (layer, KV head) units "
+                                   "with no communication, but multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from kv_cache_eviction_kvscore_amd import api, pipeline, synth
+    from kv_cache_eviction_kvscore_amd.configs import WORKLOADS
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    w = WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name} ({w.kv_bytes() / 1e9:.2f} GB of K/V)", file=sys.stderr, flush=True)
+    data = synth.generate(w, "cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    budgets = pipeline.workload_budgets(w)
+    budget_us = (time.perf_counter() - t0) * 1e6
+    prob = pipeline.problem_for(w, data["k"], data["v"])
+    pipe = pipeline.Pipeline(prob, budgets)
+    q, k, v = data["q"], data["k"], data["v"]
+    calls = [lambda: pipe.attn(q, k, v),
+             lambda: api.score(prob, q, k, v, pipe.a, pipe.lse, pipe.jstar, pipe.partial, pipe.ws_score),
+             lambda: api.merge(prob, pipe.partial, pipe.jstar, pipe.dom, pipe.score),
+             lambda: api.topk(prob, pipe.score, pipe.budgets, pipe.seg_off, pipe.kept),
+             lambda: api.compact(prob, k, v, pipe.budgets, pipe.seg_off, pipe.kept, pipe.k_out, pipe.v_out)]
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        for j, c in enumerate(calls):
+            c()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per_call = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+                for j, name in enumerate(CALLS)}
+    step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)]))
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = w.total_tokens
+    value = tokens / (ms_per_step / 1e3)
+
+    work = algorithmic_work(w, pipe.kept_rows, pipe.tq)
+    kernels = {}
+    for name in CALLS:
+        ms = per_call[name]
+        ent = {"ms": round(ms, 4)}
+        if work[name]["flop"]:
+            tf = work[name]["flop"] / (ms * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), frac_bf16_mfma=round(tf / PEAK_BF16_TFLOPS, 4))
+        gbs = work[name]["bytes"] / (ms * 1e-3) / 1e9
+        ent.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        kernels[name] = ent
+    dom_name = max(CALLS, key=lambda n: per_call[n])
+    if work[dom_name]["flop"]:
+        ach = work[dom_name]["flop"] / (per_call[dom_name] * 1e-3) / 1e12
+        roof = {"kernel": dom_name, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    else:
+        ach = work[dom_name]["bytes"] / (per_call[dom_name] * 1e-3) / 1e9
+        roof = {"kernel": dom_name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = committed_traffic(dom_name, w.name)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "seqlens": list(w.seqlens),
+                   "num_layers": w.num_layers, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "window": w.window, "kept_rows": pipe.kept_rows,
+                   "mode": "L2", "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernels": kernels,
+        "event_ms_per_step": round(step_ms, 4),
+        "budget_host_us": round(budget_us, 1),
+        "pairs_per_step": work["pairs"],
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle on a sample of units)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, data, budgets, args.cpu_seconds, max_units=16)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
