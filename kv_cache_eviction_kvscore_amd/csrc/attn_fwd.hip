@@ -12,7 +12,7 @@
 // Pass 1 (fwd_partial): grid (key chunk, query tile, unit). 8 waves; a computing wave
 // owns 32 rows, one row per lane (both half-waves hold the row). S^T = K.Q^T on
 // v_mfma_f32_32x32x16_bf16 and O^T += V^T.P^T on v_mfma_f32_32x32x16_f16; K/V tiles of
-// 64 keys are staged in LDS (register prefetch of the next tile), V converted to fp16
+// 64 keys are staged in LDS (registers prefetch the next tile), V converted to fp16
 // there (exact for |v| < 65504); V^T fragments come from ds_read_tr16_b64. P enters the
 // product in fp16 (unit roundoff 2^-11, eight times finer than bf16: with few keys per
 // row the rounding of P does not average out, and a^(-j*) feeds the isolated term),
@@ -28,7 +28,8 @@
 namespace kvs {
 namespace {
 
-constexpr int KT = 64;    // keys per tile
+constexpr int KT = 64;    // keys per compute sub-tile
+constexpr int KL = 64;    // keys per LDS tile (one barrier pair, prefetched one tile ahead)
 constexpr int KPAD = 8;   // bf16 padding per K row in LDS (b128 reads: 8 lanes hit distinct banks)
 constexpr int VPAD = 16;  // bf16 padding per V row in LDS (transpose reads: 4 keys x 32 B distinct banks)
 constexpr int SPAD = 4;   // bf16 padding per v* row
@@ -39,21 +40,21 @@ constexpr float kPUnscale = 1.f / 16384.f;
 
 template <int D>
 struct FwdSmem {
-  __bf16 k[KT][D + KPAD];
-  _Float16 v[KT][D + VPAD];
-  _Float16 vstar[kRowsPerTileMax][D + SPAD];
+  alignas(16) __bf16 k[KL][D + KPAD];  // 16-byte alignment lets the tile reads be ds_read_b128
+  alignas(16) _Float16 v[KL][D + VPAD];
+  alignas(16) _Float16 vstar[kRowsPerTileMax][D + SPAD];
 };
 
 // 8 bf16 -> 8 fp16 (exact in fp16's normal range; saturating towards zero beyond it)
-__device__ inline uint4 bf16x8_to_f16x8(uint4 u) {
-  const unsigned w[4] = {u.x, u.y, u.z, u.w};
+__device__ inline u32x4 bf16x8_to_f16x8(u32x4 u) {
+  const unsigned w[4] = {u[0], u[1], u[2], u[3]};
   unsigned r[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
     r[i] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(lo, hi));
   }
-  return uint4{r[0], r[1], r[2], r[3]};
+  return u32x4{r[0], r[1], r[2], r[3]};
 }
 
 __device__ inline float wave_shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
   constexpr int NKK = D / 16;  // k-steps of the QK^T contraction
   constexpr int NDB = D / 32;  // 32-wide d blocks of O^T
   constexpr int CPR = D / 8;   // 16-byte chunks per row
-  constexpr int NST = KT * CPR / NTHREADS;
+  constexpr int NST = KL * CPR / NTHREADS;  // 16-byte chunks per thread per tensor
   static_assert(NST >= 1, "tile too small for the block");
   __shared__ FwdSmem<D> sm;
 
@@ -104,112 +105,80 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
   const __bf16* kb0 = k + l * p.ksl + g * p.ksh + p.cu[s] * p.kst;
   const __bf16* vb0 = v + l * p.vsl + g * p.vsh + p.cu[s] * p.vst;
 
-  uint4 kst[NST], vstg[NST];
-  auto load_tile = [&](int64_t t0) {
+  // one 64-key sub-tile starting at key t0, LDS rows lb..lb+63
+  auto compute_tile = [&](const int64_t t0, const int lb) {
+    // ---- S^T = K Q^T for both 32-key blocks (chains interleaved): lane holds row l32 and,
+    // at element r of block kb, key 32kb + 8(r/4) + 4h + (r%4). Values stay raw q.k; the
+    // softmax scale enters through one FMA in front of exp2.
+    f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      const int c = tid + NTHREADS * i, key = c / CPR, part = c % CPR;
-      const int64_t j = t0 + key;
-      uint4 z = {0, 0, 0, 0};
-      kst[i] = (j < c1) ? *(const uint4*)(kb0 + j * p.kst + part * 8) : z;
-      vstg[i] = (j < c1) ? *(const uint4*)(vb0 + j * p.vst + part * 8) : z;
+    for (int kk = 0; kk < NKK; ++kk) {
+      const bf16x8 k0 = *(const bf16x8*)&sm.k[lb + l32][16 * kk + 8 * h];
+      const bf16x8 k1 = *(const bf16x8*)&sm.k[lb + 32 + l32][16 * kk + 8 * h];
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], acc1, 0, 0, 0);
     }
-  };
+    float tv[32];  // element e = 16*kb + r
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      tv[r] = acc0[r];
+      tv[16 + r] = acc1[r];
+    }
+    const int trel = (int)(t0 - c0);  // tile start relative to the chunk
+    if ((t0 + KT - 1 > n - p.W) || (t0 + KT > c1)) {
+      const int lim = (int)((tlim < c1 - 1 ? tlim : c1 - 1) - c0);  // last key this row may use, chunk-relative
+#pragma unroll
+      for (int e = 0; e < 32; ++e)
+        if (trel + 32 * (e >> 4) + 8 * ((e & 15) >> 2) + 4 * h + (e & 3) > lim) tv[e] = -INFINITY;
+    }
+    float lm = tv[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) lm = fmaxf(lm, tv[e]);
+    const float mt = fmaxf(lm, wave_shfl_xor_f(lm, 32));
 
-  load_tile(c0);
-  for (int64_t t0 = c0; t0 < c1; t0 += KT) {
-    __syncthreads();  // all waves are done with the previous tile
-#pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      const int c = tid + NTHREADS * i, key = c / CPR, part = c % CPR;
-      *(uint4*)&sm.k[key][part * 8] = kst[i];
-      *(uint4*)&sm.v[key][part * 8] = bf16x8_to_f16x8(vstg[i]);
-    }
-    __syncthreads();
-    if (t0 + KT < c1) load_tile(t0 + KT);
-    if (!computing) continue;
-
-    // ---- S^T = K Q^T for two 32-key blocks: lane holds row l32, keys 8(r/4)+4h+(r%4)
-    float tv[2][16];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 kf = *(const bf16x8*)&sm.k[kb * 32 + l32][16 * kk + 8 * h];
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tv[kb][r] = acc[r] * p.c1;
-    }
-    const bool boundary = (t0 + KT - 1 > n - p.W) || (t0 + KT > c1);
-    if (boundary) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t key = t0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key > tlim || key >= c1) tv[kb][r] = -INFINITY;
-        }
-    }
-    // Row state: m = running max (its key jst, value row in vstar), m2 = running max
-    // of every other key seen; the rest sums lrest / o are kept relative to m2 (so a
-    // dominant key never pushes the rest out of fp16's range).
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, tv[kb][r]);
-    mt = fmaxf(mt, wave_shfl_xor_f(mt, 32));
+    // Row state (raw q.k units): m = running max (key jst, value row in vstar), m2 = running
+    // max over every other key; the rest sums lrest / o are kept relative to m2, so a
+    // dominant key never pushes the rest out of fp16's range.
     const bool moved = mt > m;
     const bool any_moved = __any(moved);
-    int jt = 0x7fffffff;  // tile-relative key of the new argmax (rows that moved)
+    int jr = -1;          // this lane's element index of the new argmax, if it holds it
+    int jt = 0x7fffffff;  // chunk-relative key of the new argmax
     float m2n;
     if (any_moved) {
+      int jl = 64;
+      float hi2 = -INFINITY, lo2 = -INFINITY;
       if (moved) {
+        // elements run in key order within a lane: the first equal to mt is the lane's lowest key
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int e = 31; e >= 0; --e) jl = (tv[e] == mt) ? e : jl;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = (int)(t0 - c0) + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (tv[kb][r] == mt && key < jt) jt = key;
-          }
+        for (int e = 0; e < 32; ++e) {
+          lo2 = __builtin_amdgcn_fmed3f(lo2, hi2, tv[e]);
+          hi2 = fmaxf(hi2, tv[e]);
+        }
       }
-      jt = min(jt, wave_shfl_xor_i(jt, 32));
-      float mt2 = -INFINITY;  // tile max without the new argmax
-      if (moved) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = (int)(t0 - c0) + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key != jt) mt2 = fmaxf(mt2, tv[kb][r]);
-          }
-      }
-      mt2 = fmaxf(mt2, wave_shfl_xor_f(mt2, 32));
+      const int keyl = (jl < 64) ? trel + 32 * (jl >> 4) + 8 * ((jl & 15) >> 2) + 4 * h + (jl & 3) : 0x7fffffff;
+      jt = min(keyl, wave_shfl_xor_i(keyl, 32));
+      jr = (moved && keyl == jt) ? jl : -1;
+      // tile max without the new argmax: the lane holding it contributes its second largest
+      const float mt2l = moved ? ((jr >= 0) ? lo2 : hi2) : -INFINITY;
+      const float mt2 = fmaxf(mt2l, wave_shfl_xor_f(mt2l, 32));
       m2n = moved ? fmaxf(m, mt2) : fmaxf(m2, mt);  // the old max joins the rest when it moves
     } else {
       m2n = fmaxf(m2, mt);
     }
-    const float mb = ((m2n == -INFINITY) ? 0.f : m2n) - kPScaleLog2;
+    const float mb = ((m2n == -INFINITY) ? 0.f : m2n * p.c1) - kPScaleLog2;
 
-    float pr[2][16];  // 2^14 * exp2(t - m2n), the new argmax excluded
+    float pr[32];  // 2^14 * exp2(c1 * (s - m2n)); the new argmax excluded
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int e = 0; e < 32; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(tv[e], p.c1, -mb));
+    if (jr >= 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pr[kb][r] = __builtin_amdgcn_exp2f(tv[kb][r] - mb);
-    if (any_moved && moved) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = (int)(t0 - c0) + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key == jt) pr[kb][r] = 0.f;
-        }
+      for (int e = 0; e < 32; ++e) pr[e] = (e == jr) ? 0.f : pr[e];
     }
     // rescale the rest to the new m2
     if (__any(m2n > m2)) {
-      const float alpha = (m2n > m2) ? ((m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - m2n)) : 1.f;
+      const float alpha = (m2n > m2) ? ((m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m2 - m2n) * p.c1)) : 1.f;
       lrest *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -217,9 +186,9 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
     if (any_moved && moved) {
-      // the previous argmax joins the rest with weight exp2(m - m2n) <= 1 (2^14 scaled)
+      // the previous argmax joins the rest with weight exp2(c1 (m - m2n)) <= 1 (2^14 scaled)
       if (jst >= 0) {
-        const float wold = kPScale * __builtin_amdgcn_exp2f(m - m2n);
+        const float wold = kPScale * __builtin_amdgcn_exp2f((m - m2n) * p.c1);
         lrest += wold;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -230,30 +199,31 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
             for (int e = 0; e < 4; ++e) o[db][4 * qq + e] += wold * (float)vs[e];
           }
       }
-      const int jl = jt - (int)(t0 - c0);  // new argmax's slot in this tile
+      const int jslot = jt - trel;  // new argmax's key in this tile
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq)
-          *(f16x4*)&sm.vstar[row_t][32 * db + 8 * qq + 4 * h] = *(const f16x4*)&sm.v[jl][32 * db + 8 * qq + 4 * h];
+          *(f16x4*)&sm.vstar[row_t][32 * db + 8 * qq + 4 * h] =
+              *(const f16x4*)&sm.v[lb + jslot][32 * db + 8 * qq + 4 * h];
       jst = (int)c0 + jt;
       m = mt;
     }
     m2 = m2n;
 
     // ---- O^T += V^T P^T, 16 keys per k-step. B = P^T: lane (row, h) slots 8h..8h+7 =
-    // its P values r = 8*(ks&1) + 0..7 of block ks>>1, i.e. keys base+4h+{0..3}, base+8+4h+{0..3}.
-    // lrest sums the same fp16-rounded values that enter the product.
+    // its elements 8ks..8ks+7, i.e. keys 16ks+4h+{0..3} and 16ks+8+4h+{0..3}. lrest sums the
+    // same fp16-rounded values that enter the product (packed dot with (1, 1)).
     float ts = 0.f;
+    const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       f16x8 pf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pf[e] = (_Float16)pr[ks >> 1][8 * (ks & 1) + e];
-        ts += (float)pf[e];
-      }
-      const int kbase = 16 * ks + 4 * h;  // first key of this lane-half's two 4-key runs
+      for (int e = 0; e < 8; ++e) pf[e] = (_Float16)pr[8 * ks + e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ts = __builtin_amdgcn_fdot2(f16x2{pf[2 * e], pf[2 * e + 1]}, ones, ts, false);
+      const int kbase = lb + 16 * ks + 4 * h;  // first key of this lane-half's two 4-key runs
       const int sidx = lane & 15;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -270,6 +240,43 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       }
     }
     lrest += ts + wave_shfl_xor_f(ts, 32);
+  };
+
+
+  // K/V staging: the next LDS tile is loaded into registers while this one is computed.
+  // Keys past the chunk load the chunk's last row (in bounds; the loads stay unconditional);
+  // they are masked in the sub-tile that holds them.
+  u32x4 kst[NST], vst[NST];
+#pragma unroll
+  for (int i = 0; i < NST; ++i) {
+    const int c = tid + NTHREADS * i, key = c / CPR, part = c % CPR;
+    const int64_t j = (c0 + key < c1) ? c0 + key : c1 - 1;
+    kst[i] = *(const u32x4*)(kb0 + j * p.kst + part * 8);
+    vst[i] = *(const u32x4*)(vb0 + j * p.vst + part * 8);
+  }
+  for (int64_t t0 = c0; t0 < c1; t0 += KL) {
+    __syncthreads();  // all waves are done with the previous tile
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      const int c = tid + NTHREADS * i, key = c / CPR, part = c % CPR;
+      *(u32x4*)&sm.k[key][part * 8] = kst[i];
+      *(u32x4*)&sm.v[key][part * 8] = bf16x8_to_f16x8(vst[i]);
+    }
+    __syncthreads();
+    if (t0 + KL < c1) {
+#pragma unroll
+      for (int i = 0; i < NST; ++i) {
+        const int c = tid + NTHREADS * i, key = c / CPR, part = c % CPR;
+        const int64_t j = (t0 + KL + key < c1) ? t0 + KL + key : c1 - 1;
+        kst[i] = *(const u32x4*)(kb0 + j * p.kst + part * 8);
+        vst[i] = *(const u32x4*)(vb0 + j * p.vst + part * 8);
+      }
+    }
+    if (computing) {
+#pragma unroll
+      for (int sub = 0; sub < KL / KT; ++sub)
+        if (t0 + sub * KT < c1) compute_tile(t0 + sub * KT, sub * KT);
+    }
   }
 
   if (!computing) return;
@@ -291,8 +298,8 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
           *(const f16x4*)&sm.vstar[row_t][32 * db + 8 * qq + 4 * h];
     }
   if (h == 0) {
-    Mb[row_t] = m;
-    M2b[row_t] = m2;
+    Mb[row_t] = m * p.c1;  // log2 units from here on
+    M2b[row_t] = m2 * p.c1;
     Lb[row_t] = lrest * kPUnscale;
     Jb[row_t] = jst;
   }

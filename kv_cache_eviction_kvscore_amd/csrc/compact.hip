@@ -29,10 +29,10 @@ __global__ __launch_bounds__(256) void compact_kernel(Dev p, const __bf16* __res
     if (r >= b) break;
     const int64_t pos = kept[off0 + r];
     if (pos < 0 || pos >= n) continue;  // never read outside the sequence
-    const uint4 kx = *(const uint4*)(kb0 + pos * p.kst + part * 8);
-    const uint4 vx = *(const uint4*)(vb0 + pos * p.vst + part * 8);
-    *(uint4*)(ko + (off0 + r) * D + part * 8) = kx;
-    *(uint4*)(vo + (off0 + r) * D + part * 8) = vx;
+    const u32x4 kx = *(const u32x4*)(kb0 + pos * p.kst + part * 8);
+    const u32x4 vx = *(const u32x4*)(vb0 + pos * p.vst + part * 8);
+    *(u32x4*)(ko + (off0 + r) * D + part * 8) = kx;
+    *(u32x4*)(vo + (off0 + r) * D + part * 8) = vx;
   }
 }
 

@@ -93,13 +93,17 @@ int make_dev(const kvscore_problem* p, kvs::Dev& d) {
   d.U = d.L * d.S * d.Hkv;
   d.max_n = max_n;
   for (int s = 0; s <= p->num_seqs; ++s) d.cu[s] = p->cu_seqlens[s];
-  // Chunk sizes: aim at ~2048 key-chunk workgroups per launch (8 per CU on 256 CUs).
+  // Chunk sizes. The forward restarts its running max in every chunk (a warm-up where
+  // many rows' argmax moves), and one of its workgroups fills a CU: aim at ~2 chunks per
+  // CU. The score pass keeps no running state: ~8 chunks per CU for balance.
   int64_t keys = 0;
   for (int s = 0; s < p->num_seqs; ++s) keys += (p->cu_seqlens[s + 1] - p->cu_seqlens[s]);
   keys *= (int64_t)d.L * d.Hkv * d.Tq;
-  const int64_t target = std::min<int64_t>(65536, std::max<int64_t>(1024, next_pow2((keys + 2047) / 2048)));
-  d.fwd_chunk = (int)target;
-  d.score_chunk = (int)target;
+  auto chunk_for = [&](int64_t groups) {
+    return (int)std::min<int64_t>(65536, std::max<int64_t>(1024, next_pow2((keys + groups - 1) / groups)));
+  };
+  d.fwd_chunk = chunk_for(512);
+  d.score_chunk = chunk_for(2048);
   d.fwd_chunks = (int)((max_n + d.fwd_chunk - 1) / d.fwd_chunk);
   d.score_chunks = (int)((max_n + d.score_chunk - 1) / d.score_chunk);
   return ok();

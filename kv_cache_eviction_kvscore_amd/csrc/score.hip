@@ -14,10 +14,16 @@
 //   the row operands held in registers and K/V tiles of 64 keys staged in LDS: a lane
 //   owns one key column and 16 rows of each 32x32 block, so the sum over rows stays in
 //   the lane (plus one half-wave exchange), and the waves' column sums are added in
-//   LDS in wave order. Per pair: t = s*c1 - lse2, p = exp2(t), D = ||a||^2 + ||v||^2 -
-//   2x, and c*sqrt(D) = p*D*rsq(D*(1-p)^2): two transcendentals. Pairs (i, j*_i) are
-//   skipped (their term comes exactly from the forward); so are keys after a row's
-//   position. Both masks only act on tiles flagged in LDS, others run unmasked.
+//   LDS in wave order. The expansion runs on the matrix cores: the A.V^T accumulator
+//   starts at -||a_i||^2/2 (loop-invariant C input) and one extra k-step adds
+//   1 * (-||v_j||^2/2), the latter split exactly into three bf16 parts, so the accumulator
+//   is -D/2 with D = ||a - v||^2. Per pair: t = s*c1 - lse2, p = exp2(t), and
+//   c*sqrt(D) = sqrt(2) * p*(D/2)*rsq((D/2)*(1-p)^2): two transcendentals and seven other
+//   VALU operations; the sqrt(2) (2 in mode SQ) is applied once per token. Pairs
+//   (i, j*_i) are skipped (their term comes exactly from the forward); so are keys after
+//   a row's position. Both masks only act on tiles flagged in LDS, others run unmasked.
+//   Every pair that is not masked has p <= 1/2 (the row's argmax is isolated), so 1 - p
+//   needs no guard.
 #include "kvs_internal.hpp"
 
 namespace kvs {
@@ -30,9 +36,9 @@ constexpr int kMaxTilesPerChunk = 1024;  // score_chunk <= 65536
 
 template <int D>
 struct ScoreSmem {
-  __bf16 k[KT][D + KPAD];
-  __bf16 v[KT][D + KPAD];
-  float nv[KT];
+  alignas(16) __bf16 k[KT][D + KPAD];  // 16-byte alignment lets the tile reads be ds_read_b128
+  alignas(16) __bf16 v[KT][D + KPAD];
+  alignas(16) __bf16 nvx[KT][8];  // -||v||^2/2 as hi, mid, lo bf16 parts, then zeros
   float red[NTHREADS / 64][KT];
   int tlim[kRowsPerTileMax];
   int jst[kRowsPerTileMax];
@@ -121,42 +127,66 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
     }
   }
   // ---- row constants in the output layout: element r is row 8(r/4) + 4h + (r%4) of the wave
-  float LS[16], NA[16];
+  float LS[16];
+  f32x16 XC;  // -||a_hat||^2 / 2, the C input of the A.V^T chain
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int rt = wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
     const bool ok = computing && rt < rows_here;
     LS[r] = ok ? lse2[rbase + rt] : INFINITY;  // p = 0 for padding rows
-    NA[r] = ok ? na[rbase + rt] : 0.f;
+    XC[r] = ok ? -0.5f * na[rbase + rt] : 0.f;
   }
+  // augmented k-step: A side holds 1 in slots 0..2 (lanes of the first half-wave)
+  bf16x8 aug = {};
+  if (h == 0) {
+    aug[0] = (__bf16)1.f;
+    aug[1] = (__bf16)1.f;
+    aug[2] = (__bf16)1.f;
+  }
+  const float out_scale = (MODE == 0) ? 1.41421356237309515f : 2.f;
 
   const __bf16* kb0 = k + l * p.ksl + g * p.ksh + p.cu[s] * p.kst;
   const __bf16* vb0 = v + l * p.vsl + g * p.vsh + p.cu[s] * p.vst;
   float* pout = partial + ((int64_t)(l * p.Hkv + g) * p.Tq + qt) * p.N + p.cu[s];
   const int nw = (p.RT + 31) / 32;
 
-  uint4 kst[NST], vstg[NST];
-  auto load_tile = [&](int64_t t0) {
+  // K/V tiles: register ring of two buffers, prefetched two tiles ahead of the LDS write.
+  // A tile's column sums are flushed behind the next tile's first barrier.
+  struct Ring {
+    u32x4 k[NST], v[NST];
+  };
+  Ring A, B;
+  auto load_into = [&](Ring& r, int64_t t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       const int c = tid + NTHREADS * i, key = c / CPR, part = c % CPR;
-      const int64_t j = t0 + key;
-      uint4 z = {0, 0, 0, 0};
-      kst[i] = (j < c1) ? *(const uint4*)(kb0 + j * p.kst + part * 8) : z;
-      vstg[i] = (j < c1) ? *(const uint4*)(vb0 + j * p.vst + part * 8) : z;
+      // keys past the chunk load the chunk's last row (always in bounds, unconditional, so the
+      // loads of the two ring buffers can be waited for separately); they are masked later
+      const int64_t j = (t0 + key < c1) ? t0 + key : c1 - 1;
+      r.k[i] = *(const u32x4*)(kb0 + j * p.kst + part * 8);
+      r.v[i] = *(const u32x4*)(vb0 + j * p.vst + part * 8);
     }
   };
-
-  load_tile(c0);
-  for (int64_t t0 = c0; t0 < c1; t0 += KT) {
-    __syncthreads();  // previous tile's LDS reads (operands, column sums) are done
+  auto flush_cols = [&](int64_t tp) __attribute__((always_inline)) {  // tile tp's column sums, in wave order
+    if (tid < KT) {
+      const int64_t j = tp + tid;
+      if (j < c1) {
+        float acc = 0.f;
+        for (int w = 0; w < nw; ++w) acc += sm.red[w][tid];
+        pout[j] = acc * out_scale;
+      }
+    }
+  };
+  auto stage = [&](const Ring& r, int64_t t0) __attribute__((always_inline)) {
+    __syncthreads();  // the previous tile's operand reads and column sums are complete
+    if (t0 > c0) flush_cols(t0 - KT);
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       const int c = tid + NTHREADS * i, key = c / CPR, part = c % CPR;
-      *(uint4*)&sm.k[key][part * 8] = kst[i];
-      *(uint4*)&sm.v[key][part * 8] = vstg[i];
+      *(u32x4*)&sm.k[key][part * 8] = r.k[i];
+      *(u32x4*)&sm.v[key][part * 8] = r.v[i];
       // ||v||^2 of this key: 8 squares here, then a sum over the CPR consecutive lanes of the key
-      const bf16x8 vv = __builtin_bit_cast(bf16x8, vstg[i]);
+      const bf16x8 vv = __builtin_bit_cast(bf16x8, r.v[i]);
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -165,16 +195,26 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       }
 #pragma unroll
       for (int off = CPR / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-      if (part == 0) sm.nv[key] = ss;
+      if (part == 0) {
+        const float x = -0.5f * ss;
+        const __bf16 hi = (__bf16)x;
+        const __bf16 mid = (__bf16)(x - (float)hi);
+        const __bf16 lo = (__bf16)(x - (float)hi - (float)mid);
+        bf16x8 w8 = {};
+        w8[0] = hi;
+        w8[1] = mid;
+        w8[2] = lo;
+        *(bf16x8*)&sm.nvx[key][0] = w8;
+      }
     }
     __syncthreads();
-    if (t0 + KT < c1) load_tile(t0 + KT);
-
-    if (computing) {
+  };
+  auto compute_tile = [&](const int64_t t0) __attribute__((always_inline)) {
       const bool special = sm.flag[(t0 - c0) / KT] || (t0 + KT - 1 > n - p.W) || (t0 + KT > c1);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        f32x16 S = {}, X = {};
+        f32x16 S = {};
+        f32x16 X = XC;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
           const bf16x8 kf = *(const bf16x8*)&sm.k[kb * 32 + l32][16 * kk + 8 * h];
@@ -182,21 +222,23 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
           S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kk], kf, S, 0, 0, 0);
           X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], vf, X, 0, 0, 0);
         }
-        const float nvc = sm.nv[kb * 32 + l32];
+        {
+          bf16x8 nvf = {};
+          if (h == 0) nvf = *(const bf16x8*)&sm.nvx[kb * 32 + l32][0];
+          X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aug, nvf, X, 0, 0, 0);  // X = -D/2
+        }
         float col = 0.f;
         const int key = (int)(t0 + kb * 32 + l32);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pr = __builtin_amdgcn_exp2f(fmaf(S[r], p.c1, -LS[r]));
-          const float dd = fmaxf(fmaf(X[r], -2.f, NA[r] + nvc), 0.f);
+          const float dh = fmaxf(-X[r], 1e-30f);  // D/2, kept positive
           const float om = 1.f - pr;
           float term;
-          if (MODE == 0) {
-            const float w = fmaxf(dd * om * om, 1e-30f);
-            term = pr * dd * __builtin_amdgcn_rsqf(w);
-          } else {
-            term = pr * pr * dd * __builtin_amdgcn_rcpf(fmaxf(om * om, 1e-30f));
-          }
+          if (MODE == 0)
+            term = pr * dh * __builtin_amdgcn_rsqf(dh * om * om);  // p sqrt(D/2) / (1-p)
+          else
+            term = pr * pr * dh * __builtin_amdgcn_rcpf(om * om);  // p^2 (D/2) / (1-p)^2
           if (special) {
             const int rt = wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
             if (key > sm.tlim[rt] || key == sm.jst[rt]) term = 0.f;
@@ -206,17 +248,25 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
         col += __shfl_xor(col, 32, 64);
         if (h == 0) sm.red[wave][kb * 32 + l32] = col;
       }
-    }
-    __syncthreads();
-    if (tid < KT) {
-      const int64_t j = t0 + tid;
-      if (j < c1) {
-        float acc = 0.f;
-        for (int w = 0; w < nw; ++w) acc += sm.red[w][tid];
-        pout[j] = acc;
-      }
+      };
+
+  load_into(A, c0);
+  if (c0 + KT < c1) load_into(B, c0 + KT);
+  int64_t last = c0;
+  for (int64_t t0 = c0; t0 < c1; t0 += 2 * KT) {
+    stage(A, t0);
+    if (t0 + 2 * KT < c1) load_into(A, t0 + 2 * KT);
+    if (computing) compute_tile(t0);
+    last = t0;
+    if (t0 + KT < c1) {
+      stage(B, t0 + KT);
+      if (t0 + 3 * KT < c1) load_into(B, t0 + 3 * KT);
+      if (computing) compute_tile(t0 + KT);
+      last = t0 + KT;
     }
   }
+  __syncthreads();
+  flush_cols(last);
 }
 
 }  // namespace
