@@ -22,11 +22,14 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# per-source extras: the score pass's accumulators feed VALU work directly, so its MFMAs
+# write VGPRs (the row operands are kept in AGPRs)
+EXTRA = {"score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + CFLAGS + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "not a recognized feature for this target"
     err = "\n".join(x for x in r.stderr.splitlines() if noise not in x and "(ignoring feature)" not in x)

@@ -334,6 +334,16 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
       win = c;
     }
   }
+  const size_t ro = (size_t)u * p.R + row;
+  if (win < 0) {  // no visible key recorded (cannot happen for valid shapes: key 0 is always visible)
+    for (int e = lane; e < D; e += 64) a[ro * D + e] = 0.f;
+    if (lane == 0) {
+      dom[ro] = 0.f;
+      lse[ro] = -INFINITY;
+      jstar[ro] = -1;
+    }
+    return;
+  }
   float M2 = -INFINITY;  // max over every key but the global argmax
   for (int c = 0; c < nch; ++c) {
     if (*(const int*)stat(c, 3) < 0) continue;
@@ -366,7 +376,6 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
   const float lt = rel * lr;
   const float pstar = 1.f / (1.f + lt);
   float d2 = 0.f;
-  const size_t ro = (size_t)u * p.R + row;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;

@@ -11,6 +11,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // native 16-byte vector (HIP's uint4 is a class type: arrays of it are copied with memcpy and
 // are not promoted to registers)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

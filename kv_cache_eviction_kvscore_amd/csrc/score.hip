@@ -9,41 +9,91 @@
 //
 // score_prep: a_hat = bf16(a) (the MFMA operand), ||a_hat||^2 from the rounded values
 //   (so the expansion is the exact ||a_hat - v||^2 up to fp32 rounding), lse*log2(e).
-// score_kernel: grid (key chunk, query tile, unit); up to 8 computing waves of 32 rows.
-//   Orientation S = Q.K^T, X = A_hat.V^T (rows x keys) on v_mfma_f32_32x32x16_bf16 with
-//   the row operands held in registers and K/V tiles of 64 keys staged in LDS: a lane
-//   owns one key column and 16 rows of each 32x32 block, so the sum over rows stays in
-//   the lane (plus one half-wave exchange), and the waves' column sums are added in
-//   LDS in wave order. The expansion runs on the matrix cores: the A.V^T accumulator
-//   starts at -||a_i||^2/2 (loop-invariant C input) and one extra k-step adds
-//   1 * (-||v_j||^2/2), the latter split exactly into three bf16 parts, so the accumulator
-//   is -D/2 with D = ||a - v||^2. Per pair: t = s*c1 - lse2, p = exp2(t), and
-//   c*sqrt(D) = sqrt(2) * p*(D/2)*rsq((D/2)*(1-p)^2): two transcendentals and seven other
+// score_kernel: grid (key chunk, query tile, unit); up to 4 waves of 64 rows (two 32-row
+//   blocks each, one wave per SIMD). Orientation S = Q.K^T, X = A_hat.V^T (rows x keys)
+//   on v_mfma_f32_32x32x16_bf16 with the row operands held in registers. K/V tiles of 64
+//   keys go from HBM straight into LDS (global_load_lds_dwordx4, no register staging)
+//   through a ring of four buffers, so two tiles are in flight while one is computed.
+//   A tile keeps whole key rows (each DMA instruction moves four or eight full rows);
+//   the 16-byte chunks of row r are XOR-swizzled with a function of r so that the 32
+//   keys x 16 slots an MFMA operand needs are read conflict-free with ds_read_b128, and
+//   every fragment read feeds two MFMAs (one per row block). A lane owns one key column
+//   and 16 rows of each 32x32 block, so the sum over rows stays in the lane (plus one
+//   half-wave exchange); the waves' column sums are added in LDS in wave order. The
+//   VALU work of a 32-key block is scheduled between the MFMAs of the next block, so
+//   matrix cores and VALU overlap.
+//   The expansion runs on the matrix cores: one extra k-step per row block multiplies
+//   (1, 1, 1, -||a_i||^2/2 in three parts) by (-||v_j||^2/2 in three parts, 1, 1, 1);
+//   every part is an exact bf16 split, so the A.V^T accumulator is -D/2 with
+//   D = ||a - v||^2. ||v_j||^2 is summed from the tile in LDS (v_dot2_f32_bf16) one
+//   tile ahead of its use. Per pair: t = s*c1 - lse2, p = exp2(t), and
+//   c*sqrt(D) = sqrt(2) * p*(D/2)*rsq((D/2)*(1-p)^2): two transcendentals and six other
 //   VALU operations; the sqrt(2) (2 in mode SQ) is applied once per token. Pairs
 //   (i, j*_i) are skipped (their term comes exactly from the forward); so are keys after
 //   a row's position. Both masks only act on tiles flagged in LDS, others run unmasked.
 //   Every pair that is not masked has p <= 1/2 (the row's argmax is isolated), so 1 - p
 //   needs no guard.
+#include <type_traits>
+
 #include "kvs_internal.hpp"
+
+#ifndef KVS_SCHED
+#define KVS_SCHED 0
+#endif
 
 namespace kvs {
 namespace {
 
-constexpr int KT = 64;
-constexpr int KPAD = 8;
-constexpr int NTHREADS = 512;
+constexpr int KT = 64;   // keys per LDS tile
+constexpr int KB = 32;   // keys per MFMA block
+constexpr int NBUF = 4;  // tile ring: computed, next (its ||v||^2 summed), two in flight
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int RB = 2;                    // 32-row blocks per wave
 constexpr int kMaxTilesPerChunk = 1024;  // score_chunk <= 65536
 
 template <int D>
 struct ScoreSmem {
-  alignas(16) __bf16 k[KT][D + KPAD];  // 16-byte alignment lets the tile reads be ds_read_b128
-  alignas(16) __bf16 v[KT][D + KPAD];
-  alignas(16) __bf16 nvx[KT][8];  // -||v||^2/2 as hi, mid, lo bf16 parts, then zeros
-  float red[NTHREADS / 64][KT];
+  // tile ring: [buffer][tensor K, V][key][D] with row r's 16-byte chunks XOR-swizzled
+  alignas(16) __bf16 tile[NBUF][2][KT * D];
+  alignas(16) __bf16 nvx[2][KT][8];  // (-||v||^2/2 as hi, mid, lo bf16 parts, 1, 1, 1, 0, 0)
+  float red[3][NWAVES][KT];
   int tlim[kRowsPerTileMax];
   int jst[kRowsPerTileMax];
   unsigned char flag[kMaxTilesPerChunk];
 };
+
+// chunk position of chunk c of key row r is c ^ swz(r): sixteen consecutive rows read at
+// one chunk index land on sixteen different 16-byte bank groups (also eight consecutive
+// rows within 128 bytes), and swz(r + 32) = swz(r)
+template <int D>
+__device__ inline int swz(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return (r & 7) ^ ((r >> 3) & 1);
+}
+
+template <int D>
+struct BlockAcc {
+  f32x16 S[RB], X[RB];
+};
+
+__device__ inline void dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+
+// x as three bf16 parts (hi, mid, lo) whose sum is x to about 24 bits
+struct Split3 {
+  __bf16 hi, mid, lo;
+};
+__device__ inline Split3 split3(float x) {
+  Split3 r;
+  r.hi = (__bf16)x;
+  const float r1 = x - (float)r.hi;
+  r.mid = (__bf16)r1;
+  r.lo = (__bf16)(r1 - (float)r.mid);
+  return r;
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void score_prep_kernel(int64_t rows, const float* __restrict__ a,
@@ -79,10 +129,16 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
                                                          const float* __restrict__ lse2,
                                                          const int32_t* __restrict__ jstar,
                                                          float* __restrict__ partial) {
-  constexpr int NKK = D / 16;
-  constexpr int CPR = D / 8;
-  constexpr int NST = KT * CPR / NTHREADS;
-  static_assert(NST >= 1 && CPR <= 64, "tile shape");
+  constexpr int NKK = D / 16;             // k-steps per row operand
+  constexpr int RS = D * 2;               // bytes per key row
+  constexpr int CPK = D / 8;              // 16-byte chunks per key row
+  constexpr int TB = KT * RS;             // bytes per tensor tile
+  constexpr int IPT = KT * CPK / 64;      // DMA wave instructions per tensor tile
+  constexpr int NLD = 2 * IPT / NWAVES;   // DMA instructions per wave per tile
+  constexpr int CPL = D / 32;             // chunks per lane in the ||v||^2 sum
+  constexpr int PPR = 16 * RB / NKK;      // pairs of a finished block per k-step region
+  static_assert(IPT * 2 % NWAVES == 0 && (NLD == 8 || NLD == 4), "tile shape");
+  static_assert(KT == NWAVES * 16, "norm pass: four lanes per key, 16 keys per wave");
   __shared__ ScoreSmem<D> sm;
 
   const int u = blockIdx.z, qt = blockIdx.y, ch = blockIdx.x;
@@ -95,178 +151,321 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   const int ntiles = (int)((c1 - c0 + KT - 1) / KT);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-  const bool computing = wave * 32 < p.RT;
+  const int wrow0 = wave * 32 * RB;  // first tile row of this wave
+  const bool computing = wrow0 < p.RT;
   const int64_t rbase = (int64_t)u * p.R + (int64_t)qt * p.RT;  // first row of this tile (global row index)
   const int rows_here = min(p.RT, p.R - qt * p.RT);
+  const int nw = (p.RT + 32 * RB - 1) / (32 * RB);
+
+  const __bf16* kb0 = k + l * p.ksl + g * p.ksh + p.cu[s] * p.kst;
+  const __bf16* vb0 = v + l * p.vsl + g * p.vsh + p.cu[s] * p.vst;
+  float* pout = partial + ((int64_t)(l * p.Hkv + g) * p.Tq + qt) * p.N + p.cu[s];
+
+  // DMA of tile it into ring buffer it % NBUF. Wave instruction f (of 2*IPT) fills the
+  // 64 chunk slots 64(f % IPT) .. +63 of tensor f / IPT: slot (row r, position c') takes
+  // chunk c' ^ swz(r) of key row r. Keys past the chunk load its last row (in bounds,
+  // unconditional); their columns are masked and never written.
+  auto issue = [&](int it) __attribute__((always_inline)) {
+    const int64_t t0 = c0 + (int64_t)it * KT;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int f = i * NWAVES + wave;
+      const int tensor = f / IPT, slot = (f % IPT) * 64 + lane;
+      const int r = slot / CPK, c = (slot % CPK) ^ swz<D>(r);
+      const int64_t j0 = t0 + r;
+      const int64_t j = j0 < c1 ? j0 : c1 - 1;
+      const __bf16* src = tensor == 0 ? kb0 + j * p.kst : vb0 + j * p.vst;
+      dma16(src + 8 * c, &sm.tile[it % NBUF][tensor][(f % IPT) * 64 * 8]);
+    }
+  };
+  // -||v||^2/2 of tile it (landed, visible), into nvx[it & 1]: wave w sums keys
+  // 16w..16w+15, four lanes per key (lanes key%16 + 16c), CPL chunks each.
+  auto norms = [&](int it) __attribute__((always_inline)) {
+    const char* vt = (const char*)sm.tile[it % NBUF][1];
+    const int key = 16 * wave + (lane & 15), cg = lane >> 4;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      const int c = CPL * cg + e;
+      const u32x4 w = *(const u32x4*)(vt + key * RS + ((c ^ swz<D>(key)) << 4));
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        // copy the element out first: a bit_cast of a vector-element lvalue reads element 0
+        const unsigned wm = w[m];
+        const bf16x2 x = __builtin_bit_cast(bf16x2, wm);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+      }
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    if (cg == 0) {
+      const Split3 sp = split3(-0.5f * ss);
+      bf16x8 w8 = {};
+      w8[0] = sp.hi;
+      w8[1] = sp.mid;
+      w8[2] = sp.lo;
+      w8[3] = (__bf16)1.f;
+      w8[4] = (__bf16)1.f;
+      w8[5] = (__bf16)1.f;
+      *(bf16x8*)&sm.nvx[it & 1][key][0] = w8;
+    }
+  };
 
   // ---- per-row masks in LDS, tile flags for rows whose argmax falls in this chunk
   for (int t = tid; t < ntiles; t += NTHREADS) sm.flag[t] = 0;
-  if (tid < p.RT) {
-    const bool ok = tid < rows_here;
-    sm.tlim[tid] = ok ? (int)(n - p.W + (qt * p.RT + tid) % p.W) : -1;
-    sm.jst[tid] = ok ? jstar[rbase + tid] : -1;
+  for (int t = tid; t < kRowsPerTileMax; t += NTHREADS) {
+    const bool ok = t < rows_here;
+    sm.tlim[t] = ok ? (int)(n - p.W + (qt * p.RT + t) % p.W) : -1;
+    sm.jst[t] = ok ? jstar[rbase + t] : -1;
   }
+  issue(0);
   __syncthreads();
-  if (tid < rows_here) {
-    const int js = sm.jst[tid];
+  for (int t = tid; t < rows_here; t += NTHREADS) {
+    const int js = sm.jst[t];
     if (js >= c0 && js < c1) sm.flag[(js - c0) / KT] = 1;
   }
 
-  // ---- row operands (A side): lane row l32, k-slots 8h..8h+7
-  bf16x8 qf[NKK], af[NKK];
-  {
-    const int rt = wave * 32 + l32;
+  // ---- row operands (A side) of the wave's two row blocks: lane row l32, k-slots 8h..8h+7
+  bf16x8 qf[RB][NKK], af[RB][NKK], aug[RB];
+  float LS[RB][16];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rt = wrow0 + 32 * rb + l32;
     const bool ok = computing && rt < rows_here;
     const __bf16* qrow = q + (rbase + (ok ? rt : 0)) * D;
     const __bf16* arow = ahat + (rbase + (ok ? rt : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       bf16x8 z = {};
-      qf[kk] = ok ? *(const bf16x8*)(qrow + 16 * kk + 8 * h) : z;
-      af[kk] = ok ? *(const bf16x8*)(arow + 16 * kk + 8 * h) : z;
+      qf[rb][kk] = ok ? *(const bf16x8*)(qrow + 16 * kk + 8 * h) : z;
+      af[rb][kk] = ok ? *(const bf16x8*)(arow + 16 * kk + 8 * h) : z;
+    }
+    // augmented k-step, A side: (1, 1, 1, -||a_hat||^2/2 in three parts) in slots 0..5
+    bf16x8 w8 = {};
+    if (h == 0) {
+      w8[0] = (__bf16)1.f;
+      w8[1] = (__bf16)1.f;
+      w8[2] = (__bf16)1.f;
+      if (ok) {
+        const Split3 sp = split3(-0.5f * na[rbase + rt]);
+        w8[3] = sp.hi;
+        w8[4] = sp.mid;
+        w8[5] = sp.lo;
+      }
+    }
+    aug[rb] = w8;
+    // row constants in the output layout: element r is row 8(r/4) + 4h + (r%4) of the block
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ro = wrow0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+      LS[rb][r] = (computing && ro < rows_here) ? lse2[rbase + ro] : INFINITY;  // p = 0 for padding rows
     }
   }
-  // ---- row constants in the output layout: element r is row 8(r/4) + 4h + (r%4) of the wave
-  float LS[16];
-  f32x16 XC;  // -||a_hat||^2 / 2, the C input of the A.V^T chain
+  // the row operands live in AGPRs (MFMA reads them there), which leaves the VGPRs to
+  // the accumulators the VALU consumes
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int rt = wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-    const bool ok = computing && rt < rows_here;
-    LS[r] = ok ? lse2[rbase + rt] : INFINITY;  // p = 0 for padding rows
-    XC[r] = ok ? -0.5f * na[rbase + rt] : 0.f;
-  }
-  // augmented k-step: A side holds 1 in slots 0..2 (lanes of the first half-wave)
-  bf16x8 aug = {};
-  if (h == 0) {
-    aug[0] = (__bf16)1.f;
-    aug[1] = (__bf16)1.f;
-    aug[2] = (__bf16)1.f;
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+a"(qf[rb][kk]), "+a"(af[rb][kk]));
+    asm volatile("" : "+a"(aug[rb]));
   }
   const float out_scale = (MODE == 0) ? 1.41421356237309515f : 2.f;
-
-  const __bf16* kb0 = k + l * p.ksl + g * p.ksh + p.cu[s] * p.kst;
-  const __bf16* vb0 = v + l * p.vsl + g * p.vsh + p.cu[s] * p.vst;
-  float* pout = partial + ((int64_t)(l * p.Hkv + g) * p.Tq + qt) * p.N + p.cu[s];
-  const int nw = (p.RT + 31) / 32;
-
-  // K/V tiles: register ring of two buffers, prefetched two tiles ahead of the LDS write.
-  // A tile's column sums are flushed behind the next tile's first barrier.
-  struct Ring {
-    u32x4 k[NST], v[NST];
-  };
-  Ring A, B;
-  auto load_into = [&](Ring& r, int64_t t0) __attribute__((always_inline)) {
+  // byte offset, within a tensor tile, of this lane's operand chunk (key l32, slots
+  // 16kk + 8h .. +7) for k-step kk; block b adds 32 rows
+  int koff[NKK];
 #pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      const int c = tid + NTHREADS * i, key = c / CPR, part = c % CPR;
-      // keys past the chunk load the chunk's last row (always in bounds, unconditional, so the
-      // loads of the two ring buffers can be waited for separately); they are masked later
-      const int64_t j = (t0 + key < c1) ? t0 + key : c1 - 1;
-      r.k[i] = *(const u32x4*)(kb0 + j * p.kst + part * 8);
-      r.v[i] = *(const u32x4*)(vb0 + j * p.vst + part * 8);
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = l32 * RS + (((2 * kk) ^ h ^ swz<D>(l32)) << 4);
+
+  // term of one pair of a finished block: row (rb, r) of this wave, this lane's key
+  auto pair_term = [&](auto masked, const BlockAcc<D>& acc, const int rb, const int r, const int key)
+      __attribute__((always_inline)) {
+    const float pr = __builtin_amdgcn_exp2f(fmaf(acc.S[rb][r], p.c1, -LS[rb][r]));
+    const float ax = fabsf(acc.X[rb][r]);  // D/2
+    const float om = 1.f - pr;
+    float term;
+    if (MODE == 0) {
+      // p sqrt(D/2) / (1-p) = p (D/2) rsq((D/2)(1-p)^2); the tiny addend keeps D = 0 finite
+      term = (pr * ax) * __builtin_amdgcn_rsqf(fmaf(ax * om, om, 1e-30f));
+    } else {
+      term = (pr * pr * ax) * __builtin_amdgcn_rcpf(fmaf(om, om, 1e-30f));  // p^2 (D/2) / (1-p)^2
+    }
+    if constexpr (decltype(masked)::value) {
+      const int rt = wrow0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+      term = (key > sm.tlim[rt] || key == sm.jst[rt]) ? 0.f : term;
+    }
+    return term;
+  };
+  // adds the terms of pairs pi0 .. pi0+PPR-1 (pair pi = row (pi / 16, pi % 16)) to col,
+  // written stage by stage so the PPR independent chains interleave
+  auto pair_terms = [&](auto masked, const BlockAcc<D>& acc, const int pi0, const int key, float& col)
+      __attribute__((always_inline)) {
+    float pr[PPR], ax[PPR], om[PPR], w[PPR], t[PPR];
+#pragma unroll
+    for (int i = 0; i < PPR; ++i) {
+      const int pi = pi0 + i;
+      pr[i] = __builtin_amdgcn_exp2f(fmaf(acc.S[pi >> 4][pi & 15], p.c1, -LS[pi >> 4][pi & 15]));
+    }
+#pragma unroll
+    for (int i = 0; i < PPR; ++i) {
+      const int pi = pi0 + i;
+      ax[i] = fabsf(acc.X[pi >> 4][pi & 15]);  // D/2
+      om[i] = 1.f - pr[i];
+    }
+    if (MODE == 0) {
+      // p sqrt(D/2) / (1-p) = p (D/2) rsq((D/2)(1-p)^2); the tiny addend keeps D = 0 finite
+#pragma unroll
+      for (int i = 0; i < PPR; ++i) w[i] = __builtin_amdgcn_rsqf(fmaf(ax[i] * om[i], om[i], 1e-30f));
+#pragma unroll
+      for (int i = 0; i < PPR; ++i) t[i] = pr[i] * ax[i];
+    } else {
+      // p^2 (D/2) / (1-p)^2
+#pragma unroll
+      for (int i = 0; i < PPR; ++i) w[i] = __builtin_amdgcn_rcpf(fmaf(om[i], om[i], 1e-30f));
+#pragma unroll
+      for (int i = 0; i < PPR; ++i) t[i] = pr[i] * pr[i] * ax[i];
+    }
+#pragma unroll
+    for (int i = 0; i < PPR; ++i) {
+      if constexpr (decltype(masked)::value) {
+        const int pi = pi0 + i, r = pi & 15;
+        const int rt = wrow0 + 32 * (pi >> 4) + 8 * (r >> 2) + 4 * h + (r & 3);
+        col += (key > sm.tlim[rt] || key == sm.jst[rt]) ? 0.f : t[i] * w[i];
+      } else {
+        col = fmaf(t[i], w[i], col);
+      }
     }
   };
-  auto flush_cols = [&](int64_t tp) __attribute__((always_inline)) {  // tile tp's column sums, in wave order
+  // a finished block's column sums (both half-waves hold the sum and write it)
+  auto store_col = [&](float col, float* red) __attribute__((always_inline)) {
+    col += __shfl_xor(col, 32, 64);
+    red[l32] = col;
+  };
+  // the VALU work of a finished block alone (the last block of the chunk)
+  auto valu = [&](auto masked, const BlockAcc<D>& acc, const int key0, float* red) __attribute__((always_inline)) {
+    float col = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) col += pair_term(masked, acc, rb, r, key0 + l32);
+    store_col(col, red);
+  };
+  struct Frag {
+    bf16x8 k, v;
+  };
+  // The MFMAs of one 32-key block (K rows at kt, V rows at kt + TB, the block's first
+  // nvx entry at nvp; S = Q.K^T, X = -D/2), one region per k-step: its four MFMAs and the
+  // terms of PPR pairs of the previous block (prev, keys key0p.., column sums to redp),
+  // fenced so that matrix cores and VALU overlap and the PPR independent pair chains
+  // hide each other's latency. Operand chunks are read one k-step ahead; the last
+  // k-step reads the first chunks of the next block (at kt_next) into fnext. f0 holds
+  // this block's first chunks. The augmented k-step sits mid-chain, off the chain's tail.
+  auto step = [&](auto masked, auto has_prev, const char* kt, const __bf16* nvp, const Frag f0,
+                  const char* kt_next, Frag& fnext, const BlockAcc<D>& prev, const int key0p, float* redp)
+      __attribute__((always_inline)) {
+    BlockAcc<D> acc;
+    Frag cur = f0;
+    const bf16x8 nv = *(const bf16x8*)(nvp + 8 * l32);  // this lane's key
+    float col = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      Frag nxt;
+      if (kk + 1 < NKK) {
+        nxt.k = *(const bf16x8*)(kt + koff[kk + 1]);
+        nxt.v = *(const bf16x8*)(kt + TB + koff[kk + 1]);
+      } else {
+        fnext.k = *(const bf16x8*)(kt_next + koff[0]);
+        fnext.v = *(const bf16x8*)(kt_next + TB + koff[0]);
+      }
+      if (kk == NKK / 2) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc.X[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aug[rb], nv, acc.X[rb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        acc.S[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rb][kk], cur.k, kk ? acc.S[rb] : f32x16{}, 0, 0, 0);
+        acc.X[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb][kk], cur.v, kk ? acc.X[rb] : f32x16{}, 0, 0, 0);
+      }
+      if constexpr (decltype(has_prev)::value) {
+        pair_terms(masked, prev, kk * PPR, key0p + l32, col);
+        asm volatile("" : "+v"(col));  // the region's VALU work stays in the region
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + 1 < NKK) cur = nxt;
+    }
+    if constexpr (decltype(has_prev)::value) store_col(col, redp);
+    return acc;
+  };
+  auto flush_cols = [&](int it) __attribute__((always_inline)) {  // tile it's column sums, in wave order
     if (tid < KT) {
-      const int64_t j = tp + tid;
+      const int64_t j = c0 + (int64_t)it * KT + tid;
       if (j < c1) {
         float acc = 0.f;
-        for (int w = 0; w < nw; ++w) acc += sm.red[w][tid];
+        for (int w = 0; w < nw; ++w) acc += sm.red[it % 3][w][tid];
         pout[j] = acc * out_scale;
       }
     }
   };
-  auto stage = [&](const Ring& r, int64_t t0) __attribute__((always_inline)) {
-    __syncthreads();  // the previous tile's operand reads and column sums are complete
-    if (t0 > c0) flush_cols(t0 - KT);
-#pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      const int c = tid + NTHREADS * i, key = c / CPR, part = c % CPR;
-      *(u32x4*)&sm.k[key][part * 8] = r.k[i];
-      *(u32x4*)&sm.v[key][part * 8] = r.v[i];
-      // ||v||^2 of this key: 8 squares here, then a sum over the CPR consecutive lanes of the key
-      const bf16x8 vv = __builtin_bit_cast(bf16x8, r.v[i]);
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f = (float)vv[e];
-        ss += f * f;
-      }
-#pragma unroll
-      for (int off = CPR / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-      if (part == 0) {
-        const float x = -0.5f * ss;
-        const __bf16 hi = (__bf16)x;
-        const __bf16 mid = (__bf16)(x - (float)hi);
-        const __bf16 lo = (__bf16)(x - (float)hi - (float)mid);
-        bf16x8 w8 = {};
-        w8[0] = hi;
-        w8[1] = mid;
-        w8[2] = lo;
-        *(bf16x8*)&sm.nvx[key][0] = w8;
-      }
+  auto special = [&](int it) __attribute__((always_inline)) {
+    const int64_t t0 = c0 + (int64_t)it * KT;
+    return sm.flag[it] || (t0 + KT - 1 > n - p.W) || (t0 + KT > c1);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  // Ring schedule (one barrier per tile). At the top of iteration t, tiles t+1 and t+2
+  // are in flight; waiting until at most NLD of this wave's DMA instructions are
+  // outstanding means tile t+1 has landed. After the barrier: buffer (t+3)%4, last read
+  // by tile t-1's MFMAs, takes tile t+3; tile t+1's norms are summed; tile t is computed
+  // from buffer t%4 with the norms summed one iteration earlier. The VALU work of a
+  // tile's second block runs in the next iteration, between the MFMAs of its first.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 landed
+  __syncthreads();
+  norms(0);
+  if (ntiles > 1) issue(1);
+  if (ntiles > 2) issue(2);
+  BlockAcc<D> pend;
+  Frag fr;
+  auto tile_k = [&](int it) __attribute__((always_inline)) { return (const char*)sm.tile[it % NBUF][0]; };
+  auto key0 = [&](int it, int b) __attribute__((always_inline)) { return (int)(c0 + (int64_t)it * KT + b * KB); };
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 2 < ntiles) {
+      if constexpr (NLD == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
-  };
-  auto compute_tile = [&](const int64_t t0) __attribute__((always_inline)) {
-      const bool special = sm.flag[(t0 - c0) / KT] || (t0 + KT - 1 > n - p.W) || (t0 + KT > c1);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 S = {};
-        f32x16 X = XC;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const bf16x8 kf = *(const bf16x8*)&sm.k[kb * 32 + l32][16 * kk + 8 * h];
-          const bf16x8 vf = *(const bf16x8*)&sm.v[kb * 32 + l32][16 * kk + 8 * h];
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kk], kf, S, 0, 0, 0);
-          X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], vf, X, 0, 0, 0);
-        }
-        {
-          bf16x8 nvf = {};
-          if (h == 0) nvf = *(const bf16x8*)&sm.nvx[kb * 32 + l32][0];
-          X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aug, nvf, X, 0, 0, 0);  // X = -D/2
-        }
-        float col = 0.f;
-        const int key = (int)(t0 + kb * 32 + l32);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(fmaf(S[r], p.c1, -LS[r]));
-          const float dh = fmaxf(-X[r], 1e-30f);  // D/2, kept positive
-          const float om = 1.f - pr;
-          float term;
-          if (MODE == 0)
-            term = pr * dh * __builtin_amdgcn_rsqf(dh * om * om);  // p sqrt(D/2) / (1-p)
-          else
-            term = pr * pr * dh * __builtin_amdgcn_rcpf(om * om);  // p^2 (D/2) / (1-p)^2
-          if (special) {
-            const int rt = wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > sm.tlim[rt] || key == sm.jst[rt]) term = 0.f;
-          }
-          col += term;
-        }
-        col += __shfl_xor(col, 32, 64);
-        if (h == 0) sm.red[wave][kb * 32 + l32] = col;
+    if (t >= 2) flush_cols(t - 2);
+    if (t + 3 < ntiles) issue(t + 3);
+    if (t + 1 < ntiles) norms(t + 1);
+    if (computing) {
+      const char* k0 = tile_k(t);
+      const char* k1 = k0 + KB * RS;
+      const char* kn = tile_k(t + 1 < ntiles ? t + 1 : t);  // the next tile has landed and is visible
+      if (t == 0) {
+        fr.k = *(const bf16x8*)(k0 + koff[0]);
+        fr.v = *(const bf16x8*)(k0 + TB + koff[0]);
       }
-      };
-
-  load_into(A, c0);
-  if (c0 + KT < c1) load_into(B, c0 + KT);
-  int64_t last = c0;
-  for (int64_t t0 = c0; t0 < c1; t0 += 2 * KT) {
-    stage(A, t0);
-    if (t0 + 2 * KT < c1) load_into(A, t0 + 2 * KT);
-    if (computing) compute_tile(t0);
-    last = t0;
-    if (t0 + KT < c1) {
-      stage(B, t0 + KT);
-      if (t0 + 3 * KT < c1) load_into(B, t0 + 3 * KT);
-      if (computing) compute_tile(t0 + KT);
-      last = t0 + KT;
+      Frag f1;
+      BlockAcc<D> a0;
+      float* redp = sm.red[(t + 2) % 3][wave] + KB;  // tile t-1, block 1
+      if (t == 0) a0 = step(F_{}, F_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, 0, redp);
+      else if (special(t - 1)) a0 = step(T_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp);
+      else a0 = step(F_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp);
+      float* red0 = sm.red[t % 3][wave];
+      if (special(t)) pend = step(T_{}, T_{}, k1, sm.nvx[t & 1][KB], f1, kn, fr, a0, key0(t, 0), red0);
+      else pend = step(F_{}, T_{}, k1, sm.nvx[t & 1][KB], f1, kn, fr, a0, key0(t, 0), red0);
     }
   }
+  if (computing) {
+    float* red1 = sm.red[(ntiles - 1) % 3][wave] + KB;
+    if (special(ntiles - 1)) valu(T_{}, pend, key0(ntiles - 1, 1), red1);
+    else valu(F_{}, pend, key0(ntiles - 1, 1), red1);
+  }
   __syncthreads();
-  flush_cols(last);
+  if (ntiles >= 2) flush_cols(ntiles - 2);
+  flush_cols(ntiles - 1);
 }
 
 }  // namespace
