@@ -38,7 +38,13 @@
 #include "kvs_internal.hpp"
 
 #ifndef KVS_SCHED
-#define KVS_SCHED 0
+#define KVS_SCHED 1
+#endif
+#ifndef KVS_SCHED_MASK
+#define KVS_SCHED_MASK 0x402
+#endif
+#ifndef KVS_SCHED_N
+#define KVS_SCHED_N 10
 #endif
 
 namespace kvs {
@@ -157,6 +163,11 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   const int rows_here = min(p.RT, p.R - qt * p.RT);
   const int nw = (p.RT + 32 * RB - 1) / (32 * RB);
 
+  // fields the lambdas below use, as locals: a by-reference capture of the by-value
+  // argument would be re-read from kernel-argument memory with vector loads
+  const int64_t kst = p.kst, vst = p.vst;
+  const float c1s = p.c1;
+  const int W = p.W;
   const __bf16* kb0 = k + l * p.ksl + g * p.ksh + p.cu[s] * p.kst;
   const __bf16* vb0 = v + l * p.vsl + g * p.vsh + p.cu[s] * p.vst;
   float* pout = partial + ((int64_t)(l * p.Hkv + g) * p.Tq + qt) * p.N + p.cu[s];
@@ -174,7 +185,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       const int r = slot / CPK, c = (slot % CPK) ^ swz<D>(r);
       const int64_t j0 = t0 + r;
       const int64_t j = j0 < c1 ? j0 : c1 - 1;
-      const __bf16* src = tensor == 0 ? kb0 + j * p.kst : vb0 + j * p.vst;
+      const __bf16* src = tensor == 0 ? kb0 + j * kst : vb0 + j * vst;
       dma16(src + 8 * c, &sm.tile[it % NBUF][tensor][(f % IPT) * 64 * 8]);
     }
   };
@@ -211,8 +222,68 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
     }
   };
 
+  // The same DMA for a full tile, one instruction at a time (issued between MFMAs): lane
+  // offsets, in elements from the tile's first row, precomputed once.
+  int doff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int f = i * NWAVES + wave;
+    const int tensor = f / IPT, slot = (f % IPT) * 64 + lane;
+    const int r = slot / CPK, c = (slot % CPK) ^ swz<D>(r);
+    doff[i] = r * (int)(tensor == 0 ? kst : vst) + 8 * c;
+  }
+  auto issue_one = [&](int it, int i) __attribute__((always_inline)) {
+    const int f = i * NWAVES + wave;
+    const int tensor = f / IPT;
+    const int64_t t0 = c0 + (int64_t)it * KT;
+    const __bf16* base = tensor == 0 ? kb0 + t0 * kst : vb0 + t0 * vst;
+    dma16(base + doff[i], &sm.tile[it % NBUF][tensor][(f % IPT) * 64 * 8]);
+  };
+  // The norm pass split in stages (run one per MFMA region): 0 reads the chunks, 1 sums
+  // their squares, 2 combines the four lanes of a key, 3 splits and stores.
+  struct NormState {
+    u32x4 w[CPL];
+    float ss;
+  };
+  auto norms_stage = [&](int it, int stage, NormState& st) __attribute__((always_inline)) {
+    const int key = 16 * wave + (lane & 15), cg = lane >> 4;
+    if (stage == 0) {
+      const char* vt = (const char*)sm.tile[it % NBUF][1];
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const int c = CPL * cg + e;
+        st.w[e] = *(const u32x4*)(vt + key * RS + ((c ^ swz<D>(key)) << 4));
+      }
+    } else if (stage == 1) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const unsigned wm = st.w[e][m];  // element copied out (see norms)
+          const bf16x2 x = __builtin_bit_cast(bf16x2, wm);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+        }
+      st.ss = ss;
+    } else if (stage == 2) {
+      st.ss += __shfl_xor(st.ss, 16, 64);
+      st.ss += __shfl_xor(st.ss, 32, 64);
+    } else if (stage == 3) {
+      const Split3 sp = split3(-0.5f * st.ss);
+      bf16x8 w8 = {};
+      w8[0] = sp.hi;
+      w8[1] = sp.mid;
+      w8[2] = sp.lo;
+      w8[3] = (__bf16)1.f;
+      w8[4] = (__bf16)1.f;
+      w8[5] = (__bf16)1.f;
+      if (cg == 0) *(bf16x8*)&sm.nvx[it & 1][key][0] = w8;
+    }
+  };
+
   // ---- per-row masks in LDS, tile flags for rows whose argmax falls in this chunk
   for (int t = tid; t < ntiles; t += NTHREADS) sm.flag[t] = 0;
+  for (int t = tid; t < 3 * NWAVES * KT; t += NTHREADS) (&sm.red[0][0][0])[t] = 0.f;  // waves that never compute add zeros
   for (int t = tid; t < kRowsPerTileMax; t += NTHREADS) {
     const bool ok = t < rows_here;
     sm.tlim[t] = ok ? (int)(n - p.W + (qt * p.RT + t) % p.W) : -1;
@@ -279,7 +350,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   // term of one pair of a finished block: row (rb, r) of this wave, this lane's key
   auto pair_term = [&](auto masked, const BlockAcc<D>& acc, const int rb, const int r, const int key)
       __attribute__((always_inline)) {
-    const float pr = __builtin_amdgcn_exp2f(fmaf(acc.S[rb][r], p.c1, -LS[rb][r]));
+    const float pr = __builtin_amdgcn_exp2f(fmaf(acc.S[rb][r], c1s, -LS[rb][r]));
     const float ax = fabsf(acc.X[rb][r]);  // D/2
     const float om = 1.f - pr;
     float term;
@@ -303,7 +374,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
 #pragma unroll
     for (int i = 0; i < PPR; ++i) {
       const int pi = pi0 + i;
-      pr[i] = __builtin_amdgcn_exp2f(fmaf(acc.S[pi >> 4][pi & 15], p.c1, -LS[pi >> 4][pi & 15]));
+      pr[i] = __builtin_amdgcn_exp2f(fmaf(acc.S[pi >> 4][pi & 15], c1s, -LS[pi >> 4][pi & 15]));
     }
 #pragma unroll
     for (int i = 0; i < PPR; ++i) {
@@ -359,9 +430,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   // hide each other's latency. Operand chunks are read one k-step ahead; the last
   // k-step reads the first chunks of the next block (at kt_next) into fnext. f0 holds
   // this block's first chunks. The augmented k-step sits mid-chain, off the chain's tail.
+  // aux(kk) adds other work (DMA issue, norm stages) to region kk.
   auto step = [&](auto masked, auto has_prev, const char* kt, const __bf16* nvp, const Frag f0,
-                  const char* kt_next, Frag& fnext, const BlockAcc<D>& prev, const int key0p, float* redp)
-      __attribute__((always_inline)) {
+                  const char* kt_next, Frag& fnext, const BlockAcc<D>& prev, const int key0p, float* redp,
+                  auto&& aux) __attribute__((always_inline)) {
     BlockAcc<D> acc;
     Frag cur = f0;
     const bf16x8 nv = *(const bf16x8*)(nvp + 8 * l32);  // this lane's key
@@ -390,25 +462,40 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
         pair_terms(masked, prev, kk * PPR, key0p + l32, col);
         asm volatile("" : "+v"(col));  // the region's VALU work stays in the region
       }
+      aux(kk);
+#if KVS_SCHED
+      // within the region: each MFMA followed by a share of the VALU work, so the matrix
+      // pipe is fed while the VALU runs
+#pragma unroll
+      for (int i = 0; i < 2 * RB + (kk == NKK / 2 ? RB : 0); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(KVS_SCHED_MASK, KVS_SCHED_N, 0);
+      }
+#endif
       __builtin_amdgcn_sched_barrier(0);
       if (kk + 1 < NKK) cur = nxt;
     }
     if constexpr (decltype(has_prev)::value) store_col(col, redp);
     return acc;
   };
-  auto flush_cols = [&](int it) __attribute__((always_inline)) {  // tile it's column sums, in wave order
+  // tile it's column sums, added in wave order (the same order as the in-region flush)
+  static_assert(NWAVES == 4, "column sums add four wave rows");
+  auto flush_cols = [&](int it) __attribute__((always_inline)) {
     if (tid < KT) {
       const int64_t j = c0 + (int64_t)it * KT + tid;
       if (j < c1) {
-        float acc = 0.f;
-        for (int w = 0; w < nw; ++w) acc += sm.red[it % 3][w][tid];
-        pout[j] = acc * out_scale;
+        const float(*rd)[KT] = sm.red[it % 3];
+        pout[j] = (((rd[0][tid] + rd[1][tid]) + rd[2][tid]) + rd[3][tid]) * out_scale;
       }
     }
   };
+  // tile flags as bits: lane L holds tiles 32L .. 32L+31 (a chunk has at most 1024 tiles)
+  static_assert(kMaxTilesPerChunk <= 32 * 64, "flag bits");
+  unsigned flagbits = 0;  // filled once the flags are visible (below)
   auto special = [&](int it) __attribute__((always_inline)) {
     const int64_t t0 = c0 + (int64_t)it * KT;
-    return sm.flag[it] || (t0 + KT - 1 > n - p.W) || (t0 + KT > c1);
+    const unsigned fb = (unsigned)__builtin_amdgcn_readlane((int)flagbits, it >> 5);
+    return ((fb >> (it & 31)) & 1u) || (t0 + KT - 1 > n - W) || (t0 + KT > c1);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -421,6 +508,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   // tile's second block runs in the next iteration, between the MFMAs of its first.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 landed
   __syncthreads();
+  for (int i = 0; i < 32; ++i) {
+    const int t = 32 * lane + i;
+    if (t < ntiles && sm.flag[t]) flagbits |= 1u << i;
+  }
   norms(0);
   if (ntiles > 1) issue(1);
   if (ntiles > 2) issue(2);
@@ -436,9 +527,16 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
-    if (t >= 2) flush_cols(t - 2);
-    if (t + 3 < ntiles) issue(t + 3);
-    if (t + 1 < ntiles) norms(t + 1);
+    // fast path: the DMA of tile t+3, the column sums of tile t-2 and the norms of tile
+    // t+1 run inside the MFMA regions; it needs a previous block and a full tile t+3
+    // (gfast is uniform over the workgroup: it decides who writes tile t-2's column sums)
+    const bool gfast = t >= 1 && t + 3 < ntiles && c0 + (int64_t)(t + 4) * KT <= c1;
+    const bool fast = computing && gfast;
+    if (!fast) {
+      if (t + 3 < ntiles) issue(t + 3);
+      if (t + 1 < ntiles) norms(t + 1);
+    }
+    if (!gfast && t >= 2) flush_cols(t - 2);
     if (computing) {
       const char* k0 = tile_k(t);
       const char* k1 = k0 + KB * RS;
@@ -450,12 +548,52 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       Frag f1;
       BlockAcc<D> a0;
       float* redp = sm.red[(t + 2) % 3][wave] + KB;  // tile t-1, block 1
-      if (t == 0) a0 = step(F_{}, F_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, 0, redp);
-      else if (special(t - 1)) a0 = step(T_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp);
-      else a0 = step(F_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp);
       float* red0 = sm.red[t % 3][wave];
-      if (special(t)) pend = step(T_{}, T_{}, k1, sm.nvx[t & 1][KB], f1, kn, fr, a0, key0(t, 0), red0);
-      else pend = step(F_{}, T_{}, k1, sm.nvx[t & 1][KB], f1, kn, fr, a0, key0(t, 0), red0);
+      auto none = [](int) {};
+      if (fast) {
+        // tile t-2's columns 16w .. 16w+15 by wave w (four lanes per column store the same value)
+        float fl[NWAVES];
+        const int fcol = 16 * wave + (lane & 15);
+        auto aux_a = [&](int kk) __attribute__((always_inline)) {
+#pragma unroll
+          for (int i = 0; i < NLD; ++i)
+            if (i * NKK / NLD == kk) issue_one(t + 3, i);
+          if (kk == 0) {
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) fl[w] = sm.red[(t + 1) % 3][w][fcol];
+          } else if (kk == 2) {
+            pout[c0 + (int64_t)(t - 2) * KT + fcol] = (((fl[0] + fl[1]) + fl[2]) + fl[3]) * out_scale;
+          }
+        };
+        NormState ns;
+        auto aux_b = [&](int kk) __attribute__((always_inline)) {
+          if (kk < 4) norms_stage(t + 1, kk, ns);
+        };
+        if (t >= 2) {
+          if (special(t - 1)) a0 = step(T_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp, aux_a);
+          else a0 = step(F_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp, aux_a);
+        } else {  // t == 1: no tile t-2 to flush
+          auto aux_a1 = [&](int kk) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i)
+              if (i * NKK / NLD == kk) issue_one(t + 3, i);
+          };
+          if (special(t - 1)) a0 = step(T_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp, aux_a1);
+          else a0 = step(F_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp, aux_a1);
+        }
+        if (special(t)) pend = step(T_{}, T_{}, k1, sm.nvx[t & 1][KB], f1, kn, fr, a0, key0(t, 0), red0, aux_b);
+        else pend = step(F_{}, T_{}, k1, sm.nvx[t & 1][KB], f1, kn, fr, a0, key0(t, 0), red0, aux_b);
+      } else {
+        if (t == 0) a0 = step(F_{}, F_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, 0, redp, none);
+        else if (special(t - 1)) a0 = step(T_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp, none);
+        else a0 = step(F_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp, none);
+        if (special(t)) pend = step(T_{}, T_{}, k1, sm.nvx[t & 1][KB], f1, kn, fr, a0, key0(t, 0), red0, none);
+        else pend = step(F_{}, T_{}, k1, sm.nvx[t & 1][KB], f1, kn, fr, a0, key0(t, 0), red0, none);
+      }
+    } else if (gfast && t >= 2) {  // this wave's share of tile t-2's column sums
+      const int fcol = 16 * wave + (lane & 15);
+      const float(*rd)[KT] = sm.red[(t + 1) % 3];
+      pout[c0 + (int64_t)(t - 2) * KT + fcol] = (((rd[0][fcol] + rd[1][fcol]) + rd[2][fcol]) + rd[3][fcol]) * out_scale;
     }
   }
   if (computing) {
