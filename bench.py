@@ -30,9 +30,17 @@ CALLS = ("attn_fwd", "score", "merge", "topk", "compact")
 # the kernel files whose counters a committed traffic record describes
 KERNEL_SOURCES = {"score": "score.hip", "attn_fwd": "attn_fwd.hip", "compact": "compact.hip",
                   "topk": "topk.hip", "merge": "merge.hip"}
-# the roofline each call is judged against: the forward streams K/V once at 256 FLOP/B (below the
-# ~312 FLOP/B ridge), the score pass is reported against the bf16 matrix peak, the rest move bytes
-KERNEL_BOUND = {"attn_fwd": "hbm", "score": "mfma", "merge": "hbm", "topk": "hbm", "compact": "hbm"}
+# the kernels (by name fragment) that make up each call, for counter records
+CALL_KERNELS = {"attn_fwd": ("fwd_partial_kernel", "fwd_combine_kernel"), "score": ("score_prep_kernel", "score_kernel"),
+                "merge": ("merge_kernel",), "topk": ("topk_kernel",), "compact": ("compact_kernel",)}
+
+
+def bound_of(work: dict) -> str:
+    """The roofline that binds a call: HBM when its algorithmic bytes take longer at peak bandwidth
+    than its FLOP at the bf16 matrix peak (arithmetic intensity below the ~312 FLOP/B ridge)."""
+    if not work["flop"]:
+        return "hbm"
+    return "hbm" if work["bytes"] / PEAK_HBM_GBS / 1e9 >= work["flop"] / PEAK_BF16_TFLOPS / 1e12 else "mfma"
 
 
 def algorithmic_work(w, budgets_rows: int, tq: int):
@@ -72,6 +80,47 @@ def committed_traffic(name: str, workload: str):
     if not ent or ent.get("source_sha256_16") != source_digest(name):
         return None
     return ent.get("bytes_per_launch")
+
+
+def traffic_from(fetch_dir: str, write_dir: str, out_path: str, workload: str, copy_mib: int) -> dict:
+    """HBM bytes per launch of each call from two rocprofv3 --pmc runs of this script (one with
+    FETCH_SIZE, one with WRITE_SIZE, both with --calibrate-copy-mib). Each counter is scaled by what it
+    reads for the calibration kernel (torch.neg over copy_mib MiB: that many bytes read and written)."""
+    import csv
+    import glob
+
+    def per_dispatch(d: str, counter: str) -> dict:
+        acc = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                key = "neg" if "neg_kernel" in name else next(
+                    (k for ks in CALL_KERNELS.values() for k in ks if k in name), None)
+                if key is None:
+                    continue
+                acc.setdefault(key, {}).setdefault(row["Dispatch_Id"], 0.0)
+                acc[key][row["Dispatch_Id"]] += float(row["Counter_Value"])
+        return {k: sum(v.values()) / len(v) for k, v in acc.items()}  # KiB per dispatch
+
+    fetch, write = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
+    nbytes = copy_mib * (1 << 20)
+    fs, ws = nbytes / (fetch["neg"] * 1024), nbytes / (write["neg"] * 1024)
+    rec = {}
+    for call, ks in CALL_KERNELS.items():
+        fb = fs * 1024 * sum(fetch.get(k, 0.0) for k in ks)
+        wb = ws * 1024 * sum(write.get(k, 0.0) for k in ks)
+        rec[call] = {"source_sha256_16": source_digest(call), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                     "bytes_per_launch": round(fb + wb), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)}
+    allrec = {}
+    if os.path.exists(out_path):
+        with open(out_path) as f:
+            allrec = json.load(f)
+    allrec[workload] = rec
+    with open(out_path, "w") as f:
+        json.dump(allrec, f, indent=1)
+    return rec
 
 
 def cpu_baseline(w, data, budgets, target_s: float, max_units: int):
@@ -121,7 +170,17 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain elementwise kernel (torch.neg) over this many MiB of fp32, three "
                          "times: it reads and writes exactly that many bytes, which calibrates HBM counters")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of this script "
+                         "into HBM bytes per launch, written to --traffic-out")
+    ap.add_argument("--traffic-out", default=os.path.join(ROOT, "profiles", "traffic.json"))
     args = ap.parse_args()
+    if args.traffic_from:
+        from kv_cache_eviction_kvscore_amd.configs import WORKLOADS
+        rec = traffic_from(args.traffic_from[0], args.traffic_from[1], args.traffic_out, WORKLOADS[args.workload].name,
+                           args.calibrate_copy_mib or 1024)
+        print(json.dumps(rec, indent=1))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the path shards by (layer, KV head) units "
                                    "with no communication, but multi-GPU runs are not part of it",
@@ -194,7 +253,7 @@ def main():
         ent.update(gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
         kernels[name] = ent
     dom_name = max(CALLS, key=lambda n: per_call[n])
-    if KERNEL_BOUND[dom_name] == "mfma":
+    if bound_of(work[dom_name]) == "mfma":
         ach = work[dom_name]["flop"] / (per_call[dom_name] * 1e-3) / 1e12
         roof = {"kernel": dom_name, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
