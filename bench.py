@@ -274,6 +274,10 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "event_ms_per_step": round(step_ms, 4),
+        # scored (token, KV head, layer) triples per second, and the rate of a caller whose prefill
+        # already produced a and lse (every call but the forward)
+        "triples_per_s": round(w.num_layers * w.num_kv_heads * w.total_tokens / (ms_per_step / 1e3), 1),
+        "value_without_attn_fwd": round(tokens / ((step_ms - per_call["attn_fwd"]) / 1e3), 1),
         "budget_host_us": round(budget_us, 1),
         "pairs_per_step": work["pairs"],
     }
