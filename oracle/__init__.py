@@ -182,19 +182,45 @@ def _box_projection(w, total, lo, hi):
 
 
 # --------------------------------------------------------------------------- selection
-def kept_positions(score_seg, n, window, budget):
+def pooled_scores(score_seg, cand, pool):
+    """Max-pool of the prefix scores (DropKV page, "Methodology in Plain English": a
+    max-pool over neighbouring scores, after SnapKV; kernel size 11 in its experiments).
+
+    Token j < cand gets max(score[i]) over i in [j - pool//2, j + pool//2] and
+    0 <= i < cand: a centred window of odd size `pool`, truncated at the prefix's
+    edges. pool = 1 returns the scores unchanged.
+    """
+    if pool < 1 or pool % 2 == 0:
+        raise ValueError("pool must be a positive odd size")
+    sc = np.asarray(score_seg[:cand], dtype=np.float64)
+    h = pool // 2
+    out = np.empty(cand)
+    for j in range(cand):
+        out[j] = sc[max(0, j - h):min(cand, j + h + 1)].max()
+    return out
+
+
+def kept_positions(score_seg, n, window, budget, pool=1, n_sink=0):
     """Kept token positions of one (sequence, layer, KV head) segment, ascending.
 
-    Candidates are positions [0, n - W). The k = min(b - W, n - W) candidates with
-    the largest scores are kept, ties broken towards the lower position (a full
-    sort on (-score, position)), together with the recent window [n - W, n).
+    Always kept: the recent window [n - W, n) (DropKV page: the most recent w tokens are
+    always retained) and the first ns = min(n_sink, n - W) positions (attention sinks:
+    the "Preserve Attention Sinks" rule locks the first tokens). The other candidates
+    [ns, n - W) compete: the k = min(b - W - ns, n - W - ns) with the largest ranking key
+    are kept, ties broken towards the lower position (a full sort on (-key, position)).
+    The ranking key is the score, or with pool > 1 the pooled score of pooled_scores
+    (the pool runs over the whole prefix [0, n - W), sinks included).
     """
     cand = n - window
-    k = min(max(budget - window, 0), cand)
-    sc = np.asarray(score_seg[:cand])
-    order = np.lexsort((np.arange(cand), -sc))
+    ns = min(max(n_sink, 0), cand)
+    if budget < window + ns:
+        raise ValueError("budget smaller than the window plus the sinks")
+    key = pooled_scores(score_seg, cand, pool) if pool > 1 else np.asarray(score_seg[:cand], dtype=np.float64)
+    comp = np.arange(ns, cand)
+    k = min(budget - window - ns, cand - ns)
+    order = comp[np.lexsort((comp, -key[ns:cand]))]
     chosen = order[:k]
-    return np.sort(np.concatenate([chosen, np.arange(cand, n)])).astype(np.int32)
+    return np.sort(np.concatenate([np.arange(ns), chosen, np.arange(cand, n)])).astype(np.int32)
 
 
 def gather(k_seg, v_seg, positions):
