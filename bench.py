@@ -170,6 +170,9 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain elementwise kernel (torch.neg) over this many MiB of fp32, three "
                          "times: it reads and writes exactly that many bytes, which calibrates HBM counters")
+    ap.add_argument("--pool", type=int, default=1,
+                    help="rank candidates by the score max-pooled over this odd window (1 = off)")
+    ap.add_argument("--sinks", type=int, default=0, help="first tokens always kept (attention sinks)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of this script "
                          "into HBM bytes per launch, written to --traffic-out")
@@ -198,15 +201,16 @@ def main():
     data = synth.generate(w, "cuda")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    budgets = pipeline.workload_budgets(w)
+    budgets = pipeline.workload_budgets(w, args.sinks)
     budget_us = (time.perf_counter() - t0) * 1e6
     prob = pipeline.problem_for(w, data["k"], data["v"])
-    pipe = pipeline.Pipeline(prob, budgets)
+    pipe = pipeline.Pipeline(prob, budgets, pool=args.pool, n_sink=args.sinks)
     q, k, v = data["q"], data["k"], data["v"]
     calls = [lambda: pipe.attn(q, k, v),
              lambda: api.score(prob, q, k, v, pipe.a, pipe.lse, pipe.jstar, pipe.partial, pipe.ws_score),
              lambda: api.merge(prob, pipe.partial, pipe.jstar, pipe.dom, pipe.score),
-             lambda: api.topk(prob, pipe.score, pipe.budgets, pipe.seg_off, pipe.kept),
+             lambda: api.topk(prob, pipe.score, pipe.budgets, pipe.seg_off, pipe.kept, pool=args.pool,
+                              n_sink=args.sinks, ws=pipe.ws_topk),
              lambda: api.compact(prob, k, v, pipe.budgets, pipe.seg_off, pipe.kept, pipe.k_out, pipe.v_out)]
 
     if args.calibrate_copy_mib:
@@ -242,6 +246,8 @@ def main():
     value = tokens / (ms_per_step / 1e3)
 
     work = algorithmic_work(w, pipe.kept_rows, pipe.tq)
+    if args.pool > 1:  # the pooled keys: one more read of the scores and a write of the keys
+        work["topk"]["bytes"] += 8 * w.num_layers * w.num_kv_heads * w.total_tokens
     kernels = {}
     for name in CALLS:
         ms = per_call[name]
@@ -270,7 +276,7 @@ def main():
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "seqlens": list(w.seqlens),
                    "num_layers": w.num_layers, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "window": w.window, "kept_rows": pipe.kept_rows,
-                   "mode": "L2", "parallelism": "single GPU"},
+                   "mode": "L2", "pool": args.pool, "n_sink": args.sinks, "parallelism": "single GPU"},
         "roofline": roof,
         "kernels": kernels,
         "event_ms_per_step": round(step_ms, 4),

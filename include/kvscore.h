@@ -13,7 +13,8 @@
  *   kvscore_merge      sums the query-tile partials in a fixed order and adds the
  *                      isolated argmax terms: score[l][g][j].
  *   kvscore_budget     (host) per-layer budgets from a sensitivity profile.
- *   kvscore_topk       per unit: the b - W highest-scoring candidates plus the W most
+ *   kvscore_topk       per unit: the highest-scoring candidates (optionally by a
+ *                      max-pooled key, optionally pinning sinks) plus the W most
  *                      recent tokens, as ascending positions in a packed array.
  *   kvscore_compact    gathers the kept K and V rows into a packed ragged cache.
  *
@@ -174,17 +175,26 @@ int kvscore_budget(const double* sens, int32_t num_layers, double ratio, double 
 int kvscore_segment_offsets(const kvscore_problem* p, const int32_t* budgets, int64_t* offsets_out);
 
 /*
- * Per-unit selection (DropKV page: keep the largest individual scores, pin the
- * recent w tokens; RippleKV Eq. 4: retained positions per layer): for unit u with
- * budget b = budgets[s][l], keep the k = b - W candidates j < n_s - W with the
- * largest score (ties to the lower j) and every j >= n_s - W; write them ascending to
- * kept_pos[seg_offsets[u] ..]. score: device fp32 [L][Hkv][N] (values >= 0).
- * budgets: HOST int32 [S][L] (validated here); seg_offsets: DEVICE copy of
+ * Per-unit selection (DropKV page, "Methodology in Plain English": keep the largest
+ * individual scores, pin the recent w tokens, max-pool over neighbouring scores after
+ * SnapKV; "Preserve Attention Sinks": keep the first tokens; RippleKV Eq. 4: retained
+ * positions per layer). For unit u with budget b = budgets[s][l] and ns = min(n_sink,
+ * n_s - W): keep every j < ns, every j >= n_s - W, and the k = b - W - ns competitors
+ * ns <= j < n_s - W with the largest ranking key (ties to the lower j); write them
+ * ascending to kept_pos[seg_offsets[u] ..]. The ranking key is score[j], or with
+ * pool > 1 the maximum of score over [j - pool/2, j + pool/2] within [0, n_s - W).
+ * score: device fp32 [L][Hkv][N] (values >= 0). budgets: HOST int32 [S][L], each in
+ * [W + ns, n_s] (validated here). seg_offsets: DEVICE copy of
  * kvscore_segment_offsets(p, budgets). kept_pos: device int32 [offsets[U]].
+ * pool: odd, 1 <= pool <= 255 (1 = no pooling). n_sink >= 0 (0 = no sinks).
+ * workspace: device, kvscore_workspace_size(p, KVSCORE_WS_TOPK) bytes (the pooled
+ * keys), needed only when pool > 1 (may be NULL otherwise).
+ * Errors: KVSCORE_EINVAL (bad pool / n_sink / pointer), KVSCORE_EBUDGET (a budget
+ * outside [W + ns, n_s]), KVSCORE_EWORKSPACE.
  */
 int kvscore_topk(const kvscore_problem* p, const float* score, const int32_t* budgets,
-                 const int64_t* seg_offsets, int32_t* kept_pos, void* workspace, size_t workspace_bytes,
-                 void* stream);
+                 const int64_t* seg_offsets, int32_t* kept_pos, int32_t pool, int32_t n_sink, void* workspace,
+                 size_t workspace_bytes, void* stream);
 
 /*
  * Compaction into the packed ragged cache (RippleKV Eq. 4): for every segment u and

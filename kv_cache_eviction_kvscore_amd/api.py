@@ -24,7 +24,8 @@ MODE_SQ = 1
 WS_ATTN_FWD = 0
 WS_SCORE = 1
 WS_TOPK = 2
-ERRORS = {1: "EINVAL", 2: "EWORKSPACE", 3: "EBUDGET", 4: "EDEVICE"}
+OK, EINVAL, EWORKSPACE, EBUDGET, EDEVICE = 0, 1, 2, 3, 4
+ERRORS = {EINVAL: "EINVAL", EWORKSPACE: "EWORKSPACE", EBUDGET: "EBUDGET", EDEVICE: "EDEVICE"}
 
 
 class KvscoreError(RuntimeError):
@@ -78,7 +79,7 @@ def load():
         "kvscore_merge": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
         "kvscore_budget": (ctypes.c_int, [vp, i32, ctypes.c_double, ctypes.c_double, i64, i32, i32, vp]),
         "kvscore_segment_offsets": (ctypes.c_int, [P, vp, vp]),
-        "kvscore_topk": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
+        "kvscore_topk": (ctypes.c_int, [P, vp, vp, vp, vp, i32, i32, vp, sz, vp]),
         "kvscore_compact": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -239,13 +240,19 @@ def _check_segments(p: Problem, b: np.ndarray, seg_off_dev) -> int:
     return int(off[-1])
 
 
-def topk(p: Problem, score_t, budgets: np.ndarray, seg_off_dev, kept, stream=None):
+def topk(p: Problem, score_t, budgets: np.ndarray, seg_off_dev, kept, stream=None, *, pool: int = 1, n_sink: int = 0,
+         ws=None):
+    """Selection; pool > 1 ranks by the max-pooled score and needs ``ws`` (WS_TOPK bytes)."""
     b = np.ascontiguousarray(np.asarray(budgets, dtype=np.int32))
     R = _check_segments(p, b, seg_off_dev)
     _need(score_t, p.num_layers * p.num_kv_heads * p.total_tokens, torch.float32, "score")
     _need(kept, R, torch.int32, "kept_pos")
+    nbytes = 0
+    if pool > 1:
+        nbytes = p.workspace_size(WS_TOPK)
+        _need(ws, nbytes, torch.uint8, "workspace")
     _check(load().kvscore_topk(p.ref, _ptr(score_t), ctypes.c_void_p(b.ctypes.data), _ptr(seg_off_dev), _ptr(kept),
-                               None, 0, _stream(stream)))
+                               int(pool), int(n_sink), _ptr(ws) if pool > 1 else None, nbytes, _stream(stream)))
 
 
 def compact(p: Problem, k, v, budgets: np.ndarray, seg_off_dev, kept, k_out, v_out, stream=None):

@@ -113,6 +113,7 @@ size_t ws_attn(const kvs::Dev& d) {
   return (size_t)d.U * d.Tq * d.fwd_chunks * kvs::fwd_block_floats(d.RT, d.d) * sizeof(float);
 }
 size_t ws_score(const kvs::Dev& d) { return kvs::prep_bytes((int64_t)d.U * d.R, d.d); }
+size_t ws_topk(const kvs::Dev& d) { return (size_t)d.L * d.Hkv * d.N * sizeof(float); }  // pooled keys
 
 int launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(KVSCORE_EDEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -147,7 +148,7 @@ int check_budgets(const kvscore_problem* p, const int32_t* budgets, int* max_b) 
 
 extern "C" {
 
-int32_t kvscore_version(void) { return 100; }
+int32_t kvscore_version(void) { return 101; }
 
 const char* kvscore_last_error(void) { return g_err.c_str(); }
 
@@ -166,7 +167,7 @@ size_t kvscore_workspace_size(const kvscore_problem* p, int32_t which) {
     case KVSCORE_WS_SCORE:
       return ws_score(d);
     case KVSCORE_WS_TOPK:
-      return 0;
+      return ws_topk(d);
     default:
       fail(KVSCORE_EINVAL, "unknown workspace kind %d", which);
       return 0;
@@ -322,14 +323,31 @@ int kvscore_segment_offsets(const kvscore_problem* p, const int32_t* budgets, in
 }
 
 int kvscore_topk(const kvscore_problem* p, const float* score, const int32_t* budgets, const int64_t* seg_offsets,
-                 int32_t* kept_pos, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+                 int32_t* kept_pos, int32_t pool, int32_t n_sink, void* workspace, size_t workspace_bytes,
+                 void* stream) {
   kvs::Dev d;
   if (int rc = make_dev(p, d)) return rc;
   if (!score || !seg_offsets || !kept_pos) return fail(KVSCORE_EINVAL, "NULL tensor argument");
+  if (pool < 1 || pool > kvs::kMaxPoolSize || pool % 2 == 0)
+    return fail(KVSCORE_EINVAL, "pool=%d must be odd, in [1, %d]", pool, kvs::kMaxPoolSize);
+  if (n_sink < 0) return fail(KVSCORE_EINVAL, "n_sink=%d < 0", n_sink);
   if (int rc = check_budgets(p, budgets, nullptr)) return rc;
-  return launched(kvs::launch_topk(d, score, seg_offsets, kept_pos, (hipStream_t)stream), "kvscore_topk");
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int64_t cand = p->cu_seqlens[s + 1] - p->cu_seqlens[s] - p->window;
+    const int64_t ns = std::min<int64_t>(n_sink, cand);
+    for (int l = 0; l < p->num_layers; ++l) {
+      const int32_t b = budgets[(int64_t)s * p->num_layers + l];
+      if (b < p->window + ns)
+        return fail(KVSCORE_EBUDGET, "budget[%d][%d]=%d below window + sinks (%d + %lld)", s, l, b, p->window,
+                    (long long)ns);
+    }
+  }
+  if (pool > 1) {
+    if (int rc = check_ws(workspace, workspace_bytes, ws_topk(d))) return rc;
+  }
+  return launched(kvs::launch_topk(d, score, seg_offsets, kept_pos, pool, n_sink, (float*)workspace,
+                                   (hipStream_t)stream),
+                  "kvscore_topk");
 }
 
 int kvscore_compact(const kvscore_problem* p, const void* k, const void* v, const int32_t* budgets,

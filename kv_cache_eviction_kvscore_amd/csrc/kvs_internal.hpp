@@ -63,7 +63,9 @@ hipError_t launch_score(const Dev& p, const void* q, const void* k, const void* 
                         const float* lse, const int32_t* jstar, float* partial, void* ws, hipStream_t st);
 hipError_t launch_merge(const Dev& p, const float* partial, const int32_t* jstar, const float* dom, float* score,
                         hipStream_t st);
-hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off, int32_t* kept, hipStream_t st);
+hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off, int32_t* kept, int pool, int n_sink,
+                       float* pooled, hipStream_t st);
+constexpr int kMaxPoolSize = 255;
 hipError_t launch_compact(const Dev& p, const void* k, const void* v, const int64_t* seg_off, const int32_t* kept,
                           void* k_out, void* v_out, int max_budget, hipStream_t st);
 

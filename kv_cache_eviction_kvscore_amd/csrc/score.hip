@@ -161,7 +161,6 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   const bool computing = wrow0 < p.RT;
   const int64_t rbase = (int64_t)u * p.R + (int64_t)qt * p.RT;  // first row of this tile (global row index)
   const int rows_here = min(p.RT, p.R - qt * p.RT);
-  const int nw = (p.RT + 32 * RB - 1) / (32 * RB);
 
   // fields the lambdas below use, as locals: a by-reference capture of the by-value
   // argument would be re-read from kernel-argument memory with vector loads

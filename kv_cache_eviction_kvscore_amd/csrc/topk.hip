@@ -1,10 +1,16 @@
-// Per-unit selection: the k = b - W highest-scoring candidates (positions < n - W,
-// ties to the lower position) plus the W most recent positions, written ascending.
+// Per-unit selection: the first ns = min(n_sink, n - W) positions (attention sinks), the W
+// most recent positions, and the k = b - W - ns competitors in [ns, n - W) with the
+// largest ranking key (ties to the lower position), written ascending. The ranking key is
+// the score, or its max-pool over a centred odd window truncated to the prefix [0, n - W).
 //
 // DropKV page, "Methodology in Plain English": rank tokens by their individual shift
 // and delete the smallest (i.e. keep the largest); the most recent w tokens are always
-// retained. RippleKV page, Eq. 4: the retained positions of a layer form its
-// compressed cache.
+// retained; a max-pool over neighbouring scores (after SnapKV). "Preserve Attention
+// Sinks": the first tokens stay. RippleKV page, Eq. 4: the retained positions of a layer
+// form its compressed cache.
+//
+// pool_kernel (pool > 1): grid (4096-token tile, unit); the tile and its halo are loaded
+// into LDS (-inf outside the prefix) and every token takes the maximum of its window.
 //
 // One 1024-thread workgroup per (layer, sequence, KV head) unit. Radix select of the
 // k-th largest key over order-preserving uint32 images of the fp32 scores (4 passes of
@@ -35,7 +41,37 @@ __device__ inline int wave_incl_scan(int x, int lane) {
   return x;
 }
 
-__global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict__ score,
+constexpr int PT = 4096;  // tokens per pooling workgroup
+constexpr int kMaxPool = 255;
+
+__global__ __launch_bounds__(256) void pool_kernel(Dev p, const float* __restrict__ score, int pool,
+                                                   float* __restrict__ pooled) {
+  __shared__ float tile[PT + kMaxPool - 1];
+  const int u = blockIdx.y;
+  int l, s, g;
+  unit_coords(p, u, l, s, g);
+  const int64_t n = p.cu[s + 1] - p.cu[s];
+  const int64_t cand = n - p.W;
+  const int64_t j0 = (int64_t)blockIdx.x * PT;
+  if (j0 >= cand) return;  // uniform
+  const int h = pool >> 1;
+  const int64_t base = (int64_t)(l * p.Hkv + g) * p.N + p.cu[s];
+  const float* sc = score + base;
+  for (int i = threadIdx.x; i < PT + 2 * h; i += 256) {
+    const int64_t j = j0 - h + i;
+    tile[i] = (j >= 0 && j < cand) ? sc[j] : -INFINITY;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < PT; i += 256) {
+    const int64_t j = j0 + i;
+    if (j >= cand) break;
+    float m = tile[i];
+    for (int e = 1; e < pool; ++e) m = fmaxf(m, tile[i + e]);
+    pooled[base + j] = m;
+  }
+}
+
+__global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict__ score, int n_sink,
                                                  const int64_t* __restrict__ seg_off, int32_t* __restrict__ kept) {
   __shared__ unsigned whist[NWAVES][256];
   __shared__ unsigned hist[256];
@@ -47,16 +83,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
   unit_coords(p, u, l, s, g);
   const int64_t n = p.cu[s + 1] - p.cu[s];
   const int64_t cand = n - p.W;
+  const int64_t ns = n_sink < cand ? n_sink : cand;  // pinned sinks [0, ns); competitors [ns, cand)
   const int64_t off0 = seg_off[u];
   const int64_t b = seg_off[u + 1] - off0;
-  int64_t k = b - p.W;
+  int64_t k = b - p.W - ns;
   if (k < 0) k = 0;
-  if (k > cand) k = cand;
+  if (k > cand - ns) k = cand - ns;
   const float* sc = score + (int64_t)(l * p.Hkv + g) * p.N + p.cu[s];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
   // 0: keep no candidate, 1: keep all candidates, 2: keep key > T and the first need_eq keys == T
-  int sel = (k == 0) ? 0 : (k == cand ? 1 : 2);
+  int sel = (k == 0) ? 0 : (k == cand - ns ? 1 : 2);
   unsigned T = 0;
   int64_t need_eq = 0;
   if (sel == 2) {
@@ -66,7 +103,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
       const int shift = 24 - 8 * pass;
       for (int i = tid; i < NWAVES * 256; i += NT) (&whist[0][0])[i] = 0;
       __syncthreads();
-      for (int64_t j = tid; j < cand; j += NT) {
+      for (int64_t j = ns + tid; j < cand; j += NT) {
         const unsigned key = f2key(sc[j]);
         if ((key & pmask) == prefix) atomicAdd(&whist[wave][(key >> shift) & 255u], 1u);
       }
@@ -121,7 +158,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
       sure[e] = false;
       tie[e] = false;
       if (j < n) {
-        if (j >= cand) {
+        if (j >= cand || j < ns) {
           sure[e] = true;
         } else if (sel == 1) {
           sure[e] = true;
@@ -170,8 +207,15 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
 
 }  // namespace
 
-hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off, int32_t* kept, hipStream_t st) {
-  hipLaunchKernelGGL(topk_kernel, dim3(p.U), dim3(NT), 0, st, p, score, seg_off, kept);
+hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off, int32_t* kept, int pool, int n_sink,
+                       float* pooled, hipStream_t st) {
+  const float* key = score;
+  if (pool > 1) {
+    const dim3 gp((unsigned)((p.max_n + PT - 1) / PT), p.U);
+    hipLaunchKernelGGL(pool_kernel, gp, dim3(256), 0, st, p, score, pool, pooled);
+    key = pooled;
+  }
+  hipLaunchKernelGGL(topk_kernel, dim3(p.U), dim3(NT), 0, st, p, key, n_sink, seg_off, kept);
   return hipGetLastError();
 }
 

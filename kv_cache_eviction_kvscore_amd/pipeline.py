@@ -13,21 +13,24 @@ import torch
 from . import api
 
 
-def layer_budgets(w, s: int) -> np.ndarray:
-    """Per-layer budgets of sequence s of a workload (host map of the library)."""
+def layer_budgets(w, s: int, n_sink: int = 0) -> np.ndarray:
+    """Per-layer budgets of sequence s of a workload (host map of the library); every
+    layer keeps at least the window and the sinks."""
     prof, ratio, gamma, total = w.budget_request(s)
-    return api.budget(prof, ratio, gamma, total, w.window, w.seqlens[s])
+    lo = w.window + min(n_sink, w.seqlens[s] - w.window)
+    return api.budget(prof, ratio, gamma, total, lo, w.seqlens[s])
 
 
-def workload_budgets(w) -> np.ndarray:
-    return np.stack([layer_budgets(w, s) for s in range(w.num_seqs)]).astype(np.int32)
+def workload_budgets(w, n_sink: int = 0) -> np.ndarray:
+    return np.stack([layer_budgets(w, s, n_sink) for s in range(w.num_seqs)]).astype(np.int32)
 
 
 class Pipeline:
     """Owns the outputs and workspaces of one problem and runs the hot path."""
 
-    def __init__(self, prob: api.Problem, budgets: np.ndarray, device="cuda"):
+    def __init__(self, prob: api.Problem, budgets: np.ndarray, device="cuda", *, pool: int = 1, n_sink: int = 0):
         self.p = prob
+        self.pool, self.n_sink = pool, n_sink
         self.budgets = np.ascontiguousarray(np.asarray(budgets, dtype=np.int32))
         dev = torch.device(device)
         d, rows = prob.head_dim, prob.rows
@@ -41,6 +44,8 @@ class Pipeline:
         self.score = torch.empty((L, Hkv, N), dtype=torch.float32, device=dev)
         self.ws_fwd = torch.empty(max(1, prob.workspace_size(api.WS_ATTN_FWD)), dtype=torch.uint8, device=dev)
         self.ws_score = torch.empty(max(1, prob.workspace_size(api.WS_SCORE)), dtype=torch.uint8, device=dev)
+        self.ws_topk = (torch.empty(prob.workspace_size(api.WS_TOPK), dtype=torch.uint8, device=dev)
+                        if pool > 1 else None)
         self.seg_off_host = api.segment_offsets(prob, self.budgets)
         self.seg_off = torch.from_numpy(self.seg_off_host).to(dev)
         R = int(self.seg_off_host[-1])
@@ -57,7 +62,8 @@ class Pipeline:
         api.merge(self.p, self.partial, self.jstar, self.dom, self.score, stream)
 
     def select(self, k, v, stream=None):
-        api.topk(self.p, self.score, self.budgets, self.seg_off, self.kept, stream)
+        api.topk(self.p, self.score, self.budgets, self.seg_off, self.kept, stream, pool=self.pool,
+                 n_sink=self.n_sink, ws=self.ws_topk)
         api.compact(self.p, k, v, self.budgets, self.seg_off, self.kept, self.k_out, self.v_out, stream)
 
     def run(self, q, k, v, stream=None):

@@ -31,8 +31,10 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def run_gpu(w: Workload, mode: int = api.MODE_L2, data=None, k_layout: str = "head_major"):
-    """Generate (or take) inputs on the GPU and run the whole pipeline once."""
+def run_gpu(w: Workload, mode: int = api.MODE_L2, data=None, k_layout: str = "head_major", pool: int = 1,
+            n_sink: int = 0):
+    """Generate (or take) inputs on the GPU and run the whole pipeline once (pool > 1: rank by
+    the max-pooled score; n_sink: pinned first tokens, budgets then start at W + sinks)."""
     if data is None:
         data = synth.generate(w, "cuda")
     q, k, v = data["q"], data["k"], data["v"]
@@ -40,8 +42,8 @@ def run_gpu(w: Workload, mode: int = api.MODE_L2, data=None, k_layout: str = "he
         k = k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
         v = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     prob = pipeline.problem_for(w, k, v, mode)
-    budgets = pipeline.workload_budgets(w)
-    pipe = pipeline.Pipeline(prob, budgets)
+    budgets = pipeline.workload_budgets(w, n_sink)
+    pipe = pipeline.Pipeline(prob, budgets, pool=pool, n_sink=n_sink)
     pipe.run(q, k, v)
     torch.cuda.synchronize()
     return dict(q=q, k=k, v=v, prob=prob, budgets=budgets, pipe=pipe, out=pipe.outputs())
@@ -115,19 +117,23 @@ def check_unit(w: Workload, run, u: int, mode: int = api.MODE_L2, report: Option
     seg = run["out"]["seg_off"]
     b = int(seg[u + 1] - seg[u])
     kept = out["kept"][seg[u]:seg[u + 1]].cpu().numpy().astype(np.int64)
-    assert len(kept) == b and (np.diff(kept) > 0).all() and kept[0] >= 0 and kept[-1] < n
-    assert set(range(n - W, n)) <= set(kept.tolist())
-    # the GPU's top-k is exactly the full sort of its own fp32 scores
-    own = oracle.kept_positions(sc.astype(np.float32).astype(np.float64), n, W, b)
-    np.testing.assert_array_equal(kept, own)
-    # against the oracle's scores: equal outside the threshold band
-    ok = oracle.kept_positions(rs, n, W, b)
+    pool, n_sink = run["pipe"].pool, run["pipe"].n_sink
     cand = n - W
-    k = b - W
+    ns = min(n_sink, cand)
+    assert len(kept) == b and (np.diff(kept) > 0).all() and kept[0] >= 0 and kept[-1] < n
+    assert set(range(n - W, n)) <= set(kept.tolist()) and set(range(ns)) <= set(kept.tolist())
+    # the GPU's top-k is exactly the full sort of its own fp32 scores (pooled the same way)
+    own = oracle.kept_positions(sc.astype(np.float32).astype(np.float64), n, W, b, pool, n_sink)
+    np.testing.assert_array_equal(kept, own)
+    # against the oracle's scores: equal outside the threshold band of the ranking key (a
+    # max-pool moves no key by more than the largest score error)
+    ok = oracle.kept_positions(rs, n, W, b, pool, n_sink)
+    key = oracle.pooled_scores(rs, cand, pool) if pool > 1 else rs[:cand]
+    k = b - W - ns
     band = set()
-    if 0 < k < cand:
-        theta = np.sort(rs[:cand])[::-1][k - 1]
-        band = set(np.flatnonzero(np.abs(rs[:cand] - theta) <= BAND_RTOL * theta + atol).tolist())
+    if 0 < k < cand - ns:
+        theta = np.sort(key[ns:cand])[::-1][k - 1]
+        band = set((ns + np.flatnonzero(np.abs(key[ns:cand] - theta) <= BAND_RTOL * theta + atol)).tolist())
     gk, okk = set(kept.tolist()) - band, set(ok.tolist()) - band
     assert gk == okk, f"unit {u}: kept sets differ outside the band: {sorted(gk ^ okk)[:10]}"
 

@@ -1,5 +1,6 @@
 """The C ABI without a GPU: the library loads, exports what include/kvscore.h declares,
 validates arguments on the host, and its host-only budget map agrees with the oracle."""
+import ctypes
 import math
 import os
 import re
@@ -88,7 +89,8 @@ def test_query_tiles_and_workspace_sizes():
     p2 = make_problem(num_q_heads=28, num_kv_heads=4, window=64)  # 448 rows -> 2 tiles
     assert p2.num_query_tiles() == 2
     assert p2.workspace_size(api.WS_SCORE) == p2.rows * 128 * 2 + p2.rows * 8
-    assert p2.workspace_size(api.WS_TOPK) == 0
+    # the pooled ranking keys: one fp32 per (layer, KV head, token)
+    assert p2.workspace_size(api.WS_TOPK) == p2.num_layers * p2.num_kv_heads * p2.total_tokens * 4
 
 
 def test_segment_offsets_layout_and_budget_validation():
@@ -150,3 +152,26 @@ def test_budget_errors(case):
     args.update(case)
     with pytest.raises(api.KvscoreError):
         api.budget(**args)
+
+
+def _topk_rc(p, budgets, pool, n_sink, ws_bytes=0):
+    """Calls kvscore_topk with placeholder device pointers: every case here fails validation,
+    which happens before any launch, so the pointers are never used."""
+    lib = api.load()
+    b = np.ascontiguousarray(np.asarray(budgets, dtype=np.int32))
+    fake = ctypes.c_void_p(0x1000)
+    return lib.kvscore_topk(p.ref, fake, ctypes.c_void_p(b.ctypes.data), fake, fake, pool, n_sink,
+                            fake if ws_bytes else None, ws_bytes, None)
+
+
+def test_topk_pool_and_sink_validation():
+    p = make_problem(num_seqs=2, cu_seqlens=[0, 100, 150])  # W = 16, L = 2
+    good = np.array([[40, 40], [30, 30]], dtype=np.int32)
+    assert _topk_rc(p, good, 4, 0) == api.EINVAL  # even pool
+    assert _topk_rc(p, good, 0, 0) == api.EINVAL
+    assert _topk_rc(p, good, 257, 0) == api.EINVAL  # beyond the largest pool
+    assert _topk_rc(p, good, 1, -1) == api.EINVAL
+    assert _topk_rc(p, np.array([[40, 40], [30, 19]], dtype=np.int32), 1, 4) == api.EBUDGET  # 19 < 16 + 4
+    assert "window + sinks" in api.load().kvscore_last_error().decode()
+    assert _topk_rc(p, good, 11, 4) == api.EWORKSPACE  # pooling needs the workspace
+    assert _topk_rc(p, good, 11, 4, ws_bytes=16) == api.EWORKSPACE  # too small

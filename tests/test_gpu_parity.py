@@ -18,7 +18,7 @@ from parity import check_unit, run_gpu, sample_units, say
 pytestmark = pytest.mark.gpu
 
 
-def _check_all(w, units, mode=api.MODE_L2, **kw):
+def _check_all(w, units, mode=api.MODE_L2, **kw):  # kw: data, k_layout, pool, n_sink
     say(f"[parity] {w.name} mode={mode} units={units} {kw}")
     run = run_gpu(w, mode, **kw)
     rep = {}
@@ -158,3 +158,25 @@ def test_softmax_scale_override():
     pipe2.run(data["q"], data["k"], data["v"])
     torch.cuda.synchronize()
     assert torch.equal(pipe.score, pipe2.score)
+
+
+# ---- max-pooled ranking key and attention sinks (DropKV page: max-pool over neighbouring
+# scores, kernel 11 in its experiments; "Preserve Attention Sinks": the first 4 tokens)
+
+
+def test_pool11_sinks4_workload2_all_units():
+    w = WORKLOADS[2]
+    _check_all(w, list(range(w.num_layers * w.num_seqs * w.num_kv_heads)), pool=11, n_sink=4)
+
+
+def test_pool13_sinks4_ragged_workload5_sampled():
+    w = WORKLOADS[5]
+    _check_all(w, sample_units(w, 6), pool=13, n_sink=4)
+
+
+@pytest.mark.parametrize("pool,n_sink,budget", [(255, 0, 120), (3, 40, 120), (1, 4, 120), (11, 1000, 200)])
+def test_pool_and_sink_edges(pool, n_sink, budget):
+    # pool wider than the prefix, sinks filling much of a short prefix, sinks without pooling,
+    # more sinks than candidates (everything kept)
+    w = Workload(f"pool{pool}_sink{n_sink}", 18, 1, 4, 2, 64, (200,), 32, (6,), "fixed", budget)
+    _check_all(w, [0], pool=pool, n_sink=n_sink)
