@@ -181,6 +181,62 @@ def _box_projection(w, total, lo, hi):
     return [min(max(lam_lo * wl, lo), hi) for wl in w]
 
 
+def pyramid_budgets(num_layers, total, lo, hi, gamma):
+    """Integer per-layer budgets from the PyramidKV schedule (PyramidKV page,
+    "Layer-Adaptive Dynamic Budget Allocation"): C_l = C_min + (C_max - C_min) *
+    (1 - (l-1)/(L-1))^gamma for 1-based l, so the lowest layer gets C_max and the highest
+    C_min, and the layers share the uniform total.
+
+    Reading: C_min = lo, and C_max is whatever makes sum C_l = total (the page reallocates
+    the uniform total with no increase). A layer with f_l = 0 (the top one, for gamma > 0)
+    stays at lo, so totals above (L - 1) * hi + lo are infeasible. The curve f_l is taken
+    in fp64 (L = 1: f = 1);
+    from there everything is exact (``fractions.Fraction``): x_l = clip(lo + lam*f_l, lo,
+    hi) with sum x_l = total (lam solved on the piecewise-linear sum), then largest-
+    remainder rounding with equal remainders to the lower layer.
+    """
+    L = int(num_layers)
+    total = int(total)
+    if L <= 0:
+        return []
+    if total < L * lo or total > L * hi or gamma < 0:
+        raise ValueError("infeasible pyramid budget")
+    if L == 1:
+        f = [Fraction(1)]
+    else:
+        f = [Fraction(math.pow(1.0 - l / (L - 1), gamma)) for l in range(L)]
+    lo_f, hi_f, T = Fraction(lo), Fraction(hi), Fraction(total)
+    if total > sum(hi if fl > 0 else lo for fl in f):
+        raise ValueError("infeasible pyramid budget: the top layer stays at lo")  # f_l = 0 pins it
+
+    def xs(lam):
+        return [min(max(lo_f + lam * fl, lo_f), hi_f) for fl in f]
+
+    if sum(f) == 0:  # every layer at the floor; only total == L*lo is feasible then
+        x = [lo_f] * L
+    else:
+        pts = sorted(set([(hi_f - lo_f) / fl for fl in f if fl > 0]))
+        lam_lo = Fraction(0)
+        x = None
+        for pt in pts + [None]:
+            if pt is None:  # beyond the last breakpoint the sum is constant (every f_l > 0 at hi)
+                x = xs(lam_lo)
+                break
+            fa, fb = sum(xs(lam_lo)), sum(xs(pt))
+            if fb >= T:
+                lam = lam_lo if fb == fa else lam_lo + (T - fa) * (pt - lam_lo) / (fb - fa)
+                x = xs(lam)
+                break
+            lam_lo = pt
+    base = [xi.numerator // xi.denominator for xi in x]
+    rem = [xi - b for xi, b in zip(x, base)]
+    extra = total - sum(base)
+    order = sorted(range(L), key=lambda i: (-rem[i], i))
+    for i in order[:extra]:
+        base[i] += 1
+    return base
+
+
 # --------------------------------------------------------------------------- selection
 def pooled_scores(score_seg, cand, pool):
     """Max-pool of the prefix scores (DropKV page, "Methodology in Plain English": a

@@ -18,6 +18,9 @@
  *   - Query heads that share a KV head (grouped-query attention) are summed into
  *     that KV head's score, as the PyramidKV page's aggregated window score sums
  *     over heads (its "Observation Window and Aggregated Attention Eviction").
+ *   - Mode 2 is that aggregated window score itself: S_j = sum over the window rows
+ *     and the group's heads of the attention weight p_ij (the SnapKV/PyramidKV
+ *     ranking). Its isolated argmax term is the pair's weight p*.
  *
  * Everything is fp64. Inputs are bf16 bit patterns, converted exactly. Nothing is
  * blocked, fused or reordered beyond the definition: for one (sequence, layer,
@@ -47,7 +50,7 @@ typedef struct {
   const int64_t *cu; /* [S+1] */
   int64_t ksl, ksh, kst, vsl, vsh, vst;
   double scale; /* multiplies q.k */
-  int32_t mode; /* 0 = L2, 1 = SQ */
+  int32_t mode; /* 0 = L2, 1 = SQ, 2 = attention sum */
 } oracle_shape;
 
 static double bf16_to_double(uint16_t h) {
@@ -149,6 +152,10 @@ static int unit_eval(const oracle_shape *sh, const uint16_t *q, const uint16_t *
         if (j > t) continue; /* causal: row r never saw key j */
         const double x = S[(int64_t)r * n + j] - LSE[r];
         const double p = exp(x);
+        if (sh->mode == 2) { /* attention sum (PyramidKV aggregated window score) */
+          acc += p;
+          continue;
+        }
         const double one_minus_p = -expm1(x);
         const double c = p / one_minus_p;
         const double *ar = A + (int64_t)r * d;
@@ -168,6 +175,10 @@ static int unit_eval(const oracle_shape *sh, const uint16_t *q, const uint16_t *
     for (int r = 0; r < R; ++r) {
       const int64_t j = jstar_rows[r];
       const double x = S[(int64_t)r * n + j] - LSE[r];
+      if (sh->mode == 2) { /* the argmax pair's attention weight p* */
+        dom_rows[r] = exp(x);
+        continue;
+      }
       const double c = exp(x) / (-expm1(x));
       const double *ar = A + (int64_t)r * d;
       double dist2 = 0.0;

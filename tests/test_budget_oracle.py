@@ -112,3 +112,53 @@ def test_gather_is_a_row_copy():
     pos = np.array([0, 3, 4, 49], dtype=np.int32)
     ko, vo = oracle.gather(k, v, pos)
     assert (ko == k[[0, 3, 4, 49]]).all() and (vo == v[[0, 3, 4, 49]]).all()
+
+
+# ---- PyramidKV schedule (PyramidKV page, "Layer-Adaptive Dynamic Budget Allocation":
+# C_l = C_min + (C_max - C_min)(1 - (l-1)/(L-1))^gamma; the layers share the uniform total)
+# Hand-derived cases (0-based l, f_l = (1 - l/(L-1))^gamma, x_l = lo + lam f_l, sum = total):
+#   L=5, gamma=1, lo=10, T=100: f = 1, .75, .5, .25, 0 (sum 2.5), lam = 50/2.5 = 20
+#                              -> 30, 25, 20, 15, 10
+#   L=3, gamma=2, lo=8, T=44:   f = 1, .25, 0 (sum 1.25), lam = 20/1.25 = 16 -> 24, 12, 8
+#   L=3, gamma=1, lo=10, hi=40, T=90: unclipped 50, 30, 10 exceeds hi; x_0 = 40 and
+#                              10 + lam/2 = 40 (lam = 60) -> 40, 40, 10
+#   L=3, gamma=1, lo=10, T=40:  lam = 20/3 -> 16.67, 13.33, 10; floors sum 39, the extra
+#                              slot goes to the largest remainder (layer 0) -> 17, 13, 10
+#   L=1: the one layer takes the total
+PYRAMID_CASES = [
+    (5, 100, 10, 1000, 1.0, [30, 25, 20, 15, 10]),
+    (3, 44, 8, 1000, 2.0, [24, 12, 8]),
+    (3, 90, 10, 40, 1.0, [40, 40, 10]),
+    (3, 40, 10, 100, 1.0, [17, 13, 10]),
+    (1, 40, 10, 100, 1.0, [40]),
+]
+
+
+@pytest.mark.parametrize("L,T,lo,hi,gamma,expect", PYRAMID_CASES)
+def test_pyramid_hand_derived(L, T, lo, hi, gamma, expect):
+    assert oracle.pyramid_budgets(L, T, lo, hi, gamma) == expect
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_pyramid_properties(seed):
+    rng = np.random.default_rng(seed)
+    L = int(rng.integers(2, 40))
+    lo = int(rng.integers(1, 100))
+    hi = lo + int(rng.integers(0, 5000))
+    T = int(rng.integers(L * lo, (L - 1) * hi + lo + 1))  # the top layer stays at lo
+    gamma = float(rng.choice([0.5, 0.8, 1.0, 2.0]))
+    b = oracle.pyramid_budgets(L, T, lo, hi, gamma)
+    assert sum(b) == T and all(lo <= x <= hi for x in b)
+    assert all(b[i] >= b[i + 1] for i in range(L - 1))  # non-increasing with depth
+    if L * lo < T and b[0] < hi:
+        assert b[-1] == lo  # the top layer sits at C_min unless every layer is clipped
+
+
+def test_pyramid_infeasible():
+    with pytest.raises(ValueError):
+        oracle.pyramid_budgets(4, 30, 10, 100, 1.0)
+    with pytest.raises(ValueError):
+        oracle.pyramid_budgets(4, 500, 10, 100, 1.0)
+    with pytest.raises(ValueError):  # above (L-1)*hi + lo: the top layer cannot leave lo
+        oracle.pyramid_budgets(4, 311, 10, 100, 1.0)
+    assert oracle.pyramid_budgets(4, 310, 10, 100, 1.0) == [100, 100, 100, 10]

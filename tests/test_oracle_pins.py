@@ -190,3 +190,45 @@ def test_sizes_match_the_pages_formulas():
     assert 32 * 131072 * 4 == 16 * 2 ** 20
     # naive intermediates w x n x d per query head at w = 8, bf16: 8 GiB (~9 GB)
     assert 8 * 131072 * 128 * 32 * 2 == 8 * 2 ** 30
+
+
+# ---- mode 2: the aggregated window attention score (PyramidKV page, "Observation Window
+# and Aggregated Attention Eviction": S_j = sum over the window rows and heads of A_{h,w,j})
+
+
+@pytest.mark.parametrize("G,W,d,n", [(1, 1, 64, 40), (4, 8, 64, 200), (2, 16, 128, 90)])
+def test_attention_sum_totals_the_number_of_rows(G, W, d, n):
+    # every row's attention weights over its visible keys sum to one
+    rng = np.random.default_rng(G * 100 + W)
+    q, k, v = make_unit(rng, G, W, d, n, qscale=2.0)
+    out = run_oracle(q, k, v, G, W, d, n, mode=2)
+    assert abs(out["score"][0, 0].sum() - G * W) < 1e-10 * G * W
+
+
+def test_attention_sum_of_one_row_is_torch_softmax():
+    rng = np.random.default_rng(5)
+    d, n = 64, 150
+    q, k, v = make_unit(rng, 1, 1, d, n, qscale=3.0)
+    out = run_oracle(q, k, v, 1, 1, d, n, mode=2, rows=True)
+    logits = torch.from_numpy(bits_f64(k.reshape(n, d)) @ bits_f64(q.reshape(d)) / math.sqrt(d))
+    ref = torch.softmax(logits, dim=0).numpy()
+    np.testing.assert_allclose(out["score"][0, 0], ref, rtol=1e-12, atol=1e-15)
+    # the isolated term of mode 2 is the argmax pair's weight
+    assert out["jstar"][0] == int(np.argmax(ref))
+    assert abs(out["dom"][0] - ref.max()) < 1e-14
+
+
+def test_attention_sum_is_causal_and_linear_in_rows():
+    # row i of a window sees keys 0..n-W+i: the unit's score is the sum of its single rows
+    rng = np.random.default_rng(11)
+    G, W, d, n = 2, 4, 64, 60
+    q, k, v = make_unit(rng, G, W, d, n)
+    full = run_oracle(q, k, v, G, W, d, n, mode=2)["score"][0, 0]
+    acc = np.zeros(n)
+    for h in range(G):
+        for i in range(W):
+            qi = q.reshape(G, W, d)[h, i]
+            logits = bits_f64(k.reshape(n, d))[: n - W + i + 1] @ bits_f64(qi) / math.sqrt(d)
+            e = np.exp(logits - logits.max())
+            acc[: n - W + i + 1] += e / e.sum()
+    np.testing.assert_allclose(full, acc, rtol=1e-12, atol=1e-15)
