@@ -80,6 +80,9 @@ extern "C" {
 
 #define KVSCORE_MODE_L2 0 /* sum_i c_ij * ||a_i - v_j||          (default) */
 #define KVSCORE_MODE_SQ 1 /* sum_i (c_ij * ||a_i - v_j||)^2      ("squared" variant) */
+#define KVSCORE_MODE_ATTN 2 /* sum_i p_ij: the aggregated window attention score
+                               (PyramidKV page, "Observation Window and Aggregated
+                               Attention Eviction"; SnapKV's ranking) */
 
 #define KVSCORE_MAX_SEQS 64   /* sequences per call */
 #define KVSCORE_MAX_ROWS 1024 /* G*W query rows per unit */
@@ -98,7 +101,7 @@ typedef struct kvscore_problem {
   const int64_t* cu_seqlens; /* HOST array [S+1]: 0 = cu[0] < cu[1] < ... ; n_s = cu[s+1]-cu[s] */
   int64_t k_strides[3];      /* layer, KV-head, token strides of k in elements */
   int64_t v_strides[3];      /* same for v */
-  int32_t mode;              /* KVSCORE_MODE_L2 or KVSCORE_MODE_SQ */
+  int32_t mode;              /* KVSCORE_MODE_L2, KVSCORE_MODE_SQ or KVSCORE_MODE_ATTN */
   float softmax_scale;       /* multiplies q.k; <= 0 selects 1/sqrt(d) */
 } kvscore_problem;
 
@@ -121,7 +124,8 @@ size_t kvscore_workspace_size(const kvscore_problem* p, int32_t which);
  * For every row: s_ij = scale * q_i.k_j (j <= t_i), lse_i = ln sum_j exp(s_ij),
  * a_i = sum_j p_ij v_j, jstar_i = argmax_j s_ij (lowest j on ties), and
  * dom_i = c* ||a_i - v_j*|| with c* = p* / (1 - p*), evaluated exactly as
- * p* ||a_i^(-j*) - v_j*|| (a^(-j) = output without key j), squared in mode SQ.
+ * p* ||a_i^(-j*) - v_j*|| (a^(-j) = output without key j), squared in mode SQ; in
+ * mode ATTN, dom_i = p* (that pair's attention weight).
  * Inputs q_win, k, v (device, bf16). Outputs a, lse, jstar, dom (device).
  * workspace: device, >= kvscore_workspace_size(p, KVSCORE_WS_ATTN_FWD) bytes,
  * 256-byte aligned; contents are scratch.
@@ -134,7 +138,8 @@ int kvscore_attn_fwd(const kvscore_problem* p, const void* q_win, const void* k,
  * Score pass (DropKV page, "Methodology in Plain English", engineering paragraph):
  * for each unit, query tile qt and token j,
  *   partial[l][g][qt][cu_s + j] = sum over rows i of the tile with j <= t_i, j != jstar_i
- *       of c_ij * ||a_i - v_j||  (mode SQ: (c_ij * ||a_i - v_j||)^2),
+ *       of c_ij * ||a_i - v_j||  (mode SQ: (c_ij * ||a_i - v_j||)^2; mode ATTN: p_ij,
+ *       which reads no V, a or its norms),
  *   c_ij = p_ij / (1 - p_ij), p_ij = exp(s_ij - lse_i) recomputed from q and k,
  *   ||a_i - v_j||^2 = ||a_i||^2 - 2 a_i.v_j + ||v_j||^2 with a_i rounded to bf16.
  * Inputs: q_win, k, v (bf16), a, lse, jstar from kvscore_attn_fwd (device).
@@ -166,6 +171,20 @@ int kvscore_merge(const kvscore_problem* p, const float* partial, const int32_t*
  */
 int kvscore_budget(const double* sens, int32_t num_layers, double ratio, double gamma, int64_t total,
                    int32_t lo, int32_t hi, int32_t* budgets_out);
+
+/*
+ * Host-only PyramidKV layer schedule (PyramidKV page, "Layer-Adaptive Dynamic Budget
+ * Allocation"): b_l ~ lo + (C_max - lo) * (1 - l/(L-1))^gamma for 0-based l, with C_max
+ * chosen so that the layers share `total` (the uniform total, reallocated). A layer with
+ * factor 0 (the top one, gamma > 0) stays at lo; if some x_l = lo + lam*f_l would exceed
+ * hi, the x_l = clip(lo + lam*f_l, lo, hi) that still sum to total are used; then
+ * largest-remainder rounding (ties to the lower layer) gives sum b_l = total exactly.
+ * budgets_out: host [L]. gamma >= 0 (1 = linear decay).
+ * Errors: KVSCORE_EINVAL (bad argument), KVSCORE_EBUDGET (total < L*lo, or above
+ * what the schedule can reach: each layer with a positive factor at hi, the others at lo).
+ */
+int kvscore_budget_pyramid(int32_t num_layers, double gamma, int64_t total, int32_t lo, int32_t hi,
+                           int32_t* budgets_out);
 
 /*
  * Host-only: packed segment offsets from per-(sequence, layer) budgets.

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libkvscore.so")
 
 MODE_L2 = 0
 MODE_SQ = 1
+MODE_ATTN = 2  # aggregated window attention score (PyramidKV / SnapKV ranking)
 WS_ATTN_FWD = 0
 WS_SCORE = 1
 WS_TOPK = 2
@@ -52,7 +53,8 @@ class _Problem(ctypes.Structure):
 
 EXPORTS = (
     "kvscore_version", "kvscore_last_error", "kvscore_num_query_tiles", "kvscore_workspace_size",
-    "kvscore_attn_fwd", "kvscore_score", "kvscore_merge", "kvscore_budget", "kvscore_segment_offsets",
+    "kvscore_attn_fwd", "kvscore_score", "kvscore_merge", "kvscore_budget", "kvscore_budget_pyramid",
+    "kvscore_segment_offsets",
     "kvscore_topk", "kvscore_compact",
 )
 
@@ -78,6 +80,7 @@ def load():
         "kvscore_score": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "kvscore_merge": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
         "kvscore_budget": (ctypes.c_int, [vp, i32, ctypes.c_double, ctypes.c_double, i64, i32, i32, vp]),
+        "kvscore_budget_pyramid": (ctypes.c_int, [i32, ctypes.c_double, i64, i32, i32, vp]),
         "kvscore_segment_offsets": (ctypes.c_int, [P, vp, vp]),
         "kvscore_topk": (ctypes.c_int, [P, vp, vp, vp, vp, i32, i32, vp, sz, vp]),
         "kvscore_compact": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
@@ -222,6 +225,14 @@ def budget(sens: Sequence[float], ratio: float, gamma: float, total: int, lo: in
     g = math.inf if gamma is None else float(gamma)
     _check(load().kvscore_budget(ctypes.c_void_p(s.ctypes.data), len(s), float(ratio), g, int(total), int(lo),
                                  int(hi), ctypes.c_void_p(out.ctypes.data)))
+    return out
+
+
+def budget_pyramid(num_layers: int, gamma: float, total: int, lo: int, hi: int) -> np.ndarray:
+    """Host-only PyramidKV layer schedule for one sequence."""
+    out = np.zeros(num_layers, dtype=np.int32)
+    _check(load().kvscore_budget_pyramid(int(num_layers), float(gamma), int(total), int(lo), int(hi),
+                                         ctypes.c_void_p(out.ctypes.data)))
     return out
 
 

@@ -53,7 +53,8 @@ int make_dev(const kvscore_problem* p, kvs::Dev& d) {
   const int G = p->num_q_heads / p->num_kv_heads;
   if ((int64_t)G * p->window > KVSCORE_MAX_ROWS)
     return fail(KVSCORE_EINVAL, "G*W=%lld query rows per unit exceeds %d", (long long)G * p->window, KVSCORE_MAX_ROWS);
-  if (p->mode != KVSCORE_MODE_L2 && p->mode != KVSCORE_MODE_SQ) return fail(KVSCORE_EINVAL, "mode=%d", p->mode);
+  if (p->mode != KVSCORE_MODE_L2 && p->mode != KVSCORE_MODE_SQ && p->mode != KVSCORE_MODE_ATTN)
+    return fail(KVSCORE_EINVAL, "mode=%d", p->mode);
   if (!p->cu_seqlens) return fail(KVSCORE_EINVAL, "cu_seqlens is NULL");
   if (p->cu_seqlens[0] != 0) return fail(KVSCORE_EINVAL, "cu_seqlens[0] must be 0");
   int64_t max_n = 0;
@@ -143,6 +144,46 @@ int check_budgets(const kvscore_problem* p, const int32_t* budgets, int* max_b) 
   if (max_b) *max_b = mb;
   return ok();
 }
+
+// Largest-remainder rounding of targets x (each in [lo, hi], summing to total up to fp64
+// rounding) to integers that sum to total exactly (RippleKV Eq. 5); equal remainders go to
+// the lower layer.
+int round_to_total(const std::vector<double>& x, int64_t total, int32_t lo, int32_t hi, int32_t* out) {
+  const int L = (int)x.size();
+  std::vector<int64_t> base(L);
+  std::vector<double> rem(L);
+  int64_t assigned = 0;
+  for (int l = 0; l < L; ++l) {
+    base[l] = (int64_t)std::floor(x[l]);
+    rem[l] = x[l] - (double)base[l];
+    assigned += base[l];
+  }
+  // remainders quantised to 1e-9 before ordering: targets that are equal in exact
+  // arithmetic but differ in the last fp64 bits then tie, and ties go to the lower layer
+  std::vector<int64_t> rq(L);
+  for (int l = 0; l < L; ++l) rq[l] = (int64_t)std::llround(rem[l] * 1e9);
+  std::vector<int> order(L);
+  for (int l = 0; l < L; ++l) order[l] = l;
+  std::stable_sort(order.begin(), order.end(), [&](int i, int j) { return rq[i] > rq[j]; });
+  int64_t extra = total - assigned;
+  for (int i = 0; i < L && extra > 0; ++i) {
+    const int l = order[i];
+    if (base[l] < hi) {
+      ++base[l];
+      --extra;
+    }
+  }
+  // Rounding of the fp64 targets can leave the sum one off in either direction.
+  for (int l = L - 1; l >= 0 && extra < 0; --l)
+    if (base[l] > lo) {
+      --base[l];
+      ++extra;
+    }
+  if (extra != 0) return fail(KVSCORE_EBUDGET, "could not distribute the total");
+  for (int l = 0; l < L; ++l) out[l] = (int32_t)base[l];
+  return ok();
+}
+
 
 }  // namespace
 
@@ -275,35 +316,48 @@ int kvscore_budget(const double* sens, int32_t num_layers, double ratio, double 
     }
     for (int l = 0; l < L; ++l) x[l] = std::min(std::max(lam * w[l], (double)lo), (double)hi);
   }
-  // Largest remainder so that the integers sum to the total (Eq. 5); ties to the lower layer.
-  std::vector<int64_t> base(L);
-  std::vector<double> rem(L);
-  int64_t assigned = 0;
-  for (int l = 0; l < L; ++l) {
-    base[l] = (int64_t)std::floor(x[l]);
-    rem[l] = x[l] - (double)base[l];
-    assigned += base[l];
-  }
-  std::vector<int> order(L);
-  for (int l = 0; l < L; ++l) order[l] = l;
-  std::stable_sort(order.begin(), order.end(), [&](int i, int j) { return rem[i] > rem[j]; });
-  int64_t extra = total - assigned;
-  for (int i = 0; i < L && extra > 0; ++i) {
-    const int l = order[i];
-    if (base[l] < hi) {
-      ++base[l];
-      --extra;
+  return round_to_total(x, total, lo, hi, budgets_out);
+}
+
+int kvscore_budget_pyramid(int32_t num_layers, double gamma, int64_t total, int32_t lo, int32_t hi,
+                           int32_t* budgets_out) {
+  if (!budgets_out) return fail(KVSCORE_EINVAL, "NULL argument");
+  if (num_layers < 1) return fail(KVSCORE_EINVAL, "num_layers=%d < 1", num_layers);
+  if (!(gamma >= 0.0) || !std::isfinite(gamma)) return fail(KVSCORE_EINVAL, "gamma must be finite and >= 0");
+  if (lo < 0 || hi < lo) return fail(KVSCORE_EINVAL, "need 0 <= lo <= hi");
+  const int L = num_layers;
+  // PyramidKV curve, 0-based: f_l = (1 - l/(L-1))^gamma (the lowest layer 1, the top 0)
+  std::vector<double> f(L, 1.0);
+  if (L > 1)
+    for (int l = 0; l < L; ++l) f[l] = std::pow(1.0 - (double)l / (L - 1), gamma);
+  int64_t reach = 0;
+  for (int l = 0; l < L; ++l) reach += f[l] > 0 ? hi : lo;
+  if (total < (int64_t)L * lo || total > reach)
+    return fail(KVSCORE_EBUDGET, "total %lld outside [L*lo, %lld] (layers with factor 0 stay at lo)",
+                (long long)total, (long long)reach);
+  // x_l = clip(lo + lam * f_l, lo, hi) with sum = total: nondecreasing, piecewise linear in lam
+  auto g = [&](double lam) {
+    double t = 0;
+    for (int l = 0; l < L; ++l) t += std::min((double)lo + lam * f[l], (double)hi);
+    return t;
+  };
+  std::vector<double> bp;
+  for (int l = 0; l < L; ++l)
+    if (f[l] > 0) bp.push_back(((double)hi - lo) / f[l]);
+  std::sort(bp.begin(), bp.end());
+  double a = 0.0, lam = bp.empty() ? 0.0 : bp.back();
+  for (double b : bp) {
+    const double gb = g(b);
+    if (gb >= (double)total) {
+      const double ga = g(a);
+      lam = (gb == ga) ? a : a + ((double)total - ga) * (b - a) / (gb - ga);
+      break;
     }
+    a = b;
   }
-  // Rounding of the fp64 targets can leave the sum one off in either direction.
-  for (int l = L - 1; l >= 0 && extra < 0; --l)
-    if (base[l] > lo) {
-      --base[l];
-      ++extra;
-    }
-  if (extra != 0) return fail(KVSCORE_EBUDGET, "could not distribute the total");
-  for (int l = 0; l < L; ++l) budgets_out[l] = (int32_t)base[l];
-  return ok();
+  std::vector<double> x(L);
+  for (int l = 0; l < L; ++l) x[l] = std::min((double)lo + lam * f[l], (double)hi);
+  return round_to_total(x, total, lo, hi, budgets_out);
 }
 
 int kvscore_segment_offsets(const kvscore_problem* p, const int32_t* budgets, int64_t* offsets_out) {

@@ -189,8 +189,8 @@ def pyramid_budgets(num_layers, total, lo, hi, gamma):
 
     Reading: C_min = lo, and C_max is whatever makes sum C_l = total (the page reallocates
     the uniform total with no increase). A layer with f_l = 0 (the top one, for gamma > 0)
-    stays at lo, so totals above (L - 1) * hi + lo are infeasible. The curve f_l is taken
-    in fp64 (L = 1: f = 1);
+    stays at lo, so totals above (L - 1) * hi + lo are infeasible. The curve f_l is exact
+    for integer gamma and fp64 otherwise (L = 1: f = 1);
     from there everything is exact (``fractions.Fraction``): x_l = clip(lo + lam*f_l, lo,
     hi) with sum x_l = total (lam solved on the piecewise-linear sum), then largest-
     remainder rounding with equal remainders to the lower layer.
@@ -203,6 +203,8 @@ def pyramid_budgets(num_layers, total, lo, hi, gamma):
         raise ValueError("infeasible pyramid budget")
     if L == 1:
         f = [Fraction(1)]
+    elif float(gamma).is_integer():  # the curve is rational: take it exactly
+        f = [Fraction(L - 1 - l, L - 1) ** int(gamma) for l in range(L)]
     else:
         f = [Fraction(math.pow(1.0 - l / (L - 1), gamma)) for l in range(L)]
     lo_f, hi_f, T = Fraction(lo), Fraction(hi), Fraction(total)

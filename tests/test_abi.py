@@ -49,7 +49,7 @@ BAD = [
     dict(window=0),
     dict(window=100),  # sequence not longer than the window
     dict(cu_seqlens=[5, 100]),
-    dict(mode=2),
+    dict(mode=3),
     dict(k_strides=(2 * 100 * 128, 100 * 128, 4)),
     dict(v_strides=(2 * 100 * 128, 100 * 128 + 3, 128)),
     dict(num_q_heads=1024 * 2, num_kv_heads=1, window=2),
@@ -175,3 +175,32 @@ def test_topk_pool_and_sink_validation():
     assert "window + sinks" in api.load().kvscore_last_error().decode()
     assert _topk_rc(p, good, 11, 4) == api.EWORKSPACE  # pooling needs the workspace
     assert _topk_rc(p, good, 11, 4, ws_bytes=16) == api.EWORKSPACE  # too small
+
+
+@pytest.mark.parametrize("L,gamma,T,lo,hi", [(5, 1.0, 100, 10, 1000), (3, 2.0, 44, 8, 1000), (3, 1.0, 90, 10, 40),
+                                             (3, 1.0, 40, 10, 100), (1, 1.0, 40, 10, 100),
+                                             (32, 0.8, 32 * 6553, 64, 131072), (28, 1.0, 183500, 64, 131072)])
+def test_pyramid_budget_matches_oracle(L, gamma, T, lo, hi):
+    assert api.budget_pyramid(L, gamma, T, lo, hi).tolist() == oracle.pyramid_budgets(L, T, lo, hi, gamma)
+
+
+def test_pyramid_budget_random_against_oracle():
+    rng = np.random.default_rng(2024)
+    for _ in range(500):
+        L = int(rng.integers(1, 60))
+        lo = int(rng.integers(0, 200))
+        hi = lo + int(rng.integers(0, 10000))
+        gamma = float(rng.choice([0.0, 0.5, 0.8, 1.0, 1.5, 2.0, 3.7]))
+        f = [1.0] if L == 1 else [(1 - l / (L - 1)) ** gamma for l in range(L)]
+        T = int(rng.integers(L * lo, sum(hi if x > 0 else lo for x in f) + 1))
+        assert api.budget_pyramid(L, gamma, T, lo, hi).tolist() == oracle.pyramid_budgets(L, T, lo, hi, gamma)
+
+
+def test_pyramid_budget_errors():
+    with pytest.raises(api.KvscoreError) as e:
+        api.budget_pyramid(4, 1.0, 311, 10, 100)  # the top layer cannot leave lo
+    assert e.value.code == api.EBUDGET
+    with pytest.raises(api.KvscoreError):
+        api.budget_pyramid(4, -1.0, 100, 10, 100)
+    with pytest.raises(api.KvscoreError):
+        api.budget_pyramid(0, 1.0, 100, 10, 100)
