@@ -170,6 +170,8 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain elementwise kernel (torch.neg) over this many MiB of fp32, three "
                          "times: it reads and writes exactly that many bytes, which calibrates HBM counters")
+    ap.add_argument("--mode", choices=("l2", "sq", "attn"), default="l2",
+                    help="score: DropKV L2 shift (default), its squared variant, or the attention sum")
     ap.add_argument("--pool", type=int, default=1,
                     help="rank candidates by the score max-pooled over this odd window (1 = off)")
     ap.add_argument("--sinks", type=int, default=0, help="first tokens always kept (attention sinks)")
@@ -203,7 +205,8 @@ def main():
     t0 = time.perf_counter()
     budgets = pipeline.workload_budgets(w, args.sinks)
     budget_us = (time.perf_counter() - t0) * 1e6
-    prob = pipeline.problem_for(w, data["k"], data["v"])
+    mode = {"l2": api.MODE_L2, "sq": api.MODE_SQ, "attn": api.MODE_ATTN}[args.mode]
+    prob = pipeline.problem_for(w, data["k"], data["v"], mode)
     pipe = pipeline.Pipeline(prob, budgets, pool=args.pool, n_sink=args.sinks)
     q, k, v = data["q"], data["k"], data["v"]
     calls = [lambda: pipe.attn(q, k, v),
@@ -246,6 +249,10 @@ def main():
     value = tokens / (ms_per_step / 1e3)
 
     work = algorithmic_work(w, pipe.kept_rows, pipe.tq)
+    if args.mode == "attn":  # the attention sum streams K only and has one GEMM
+        kv = w.num_layers * w.num_kv_heads * w.total_tokens * w.head_dim * 2
+        work["score"]["bytes"] -= kv
+        work["score"]["flop"] //= 2
     if args.pool > 1:  # the pooled keys: one more read of the scores and a write of the keys
         work["topk"]["bytes"] += 8 * w.num_layers * w.num_kv_heads * w.total_tokens
     kernels = {}
@@ -276,7 +283,7 @@ def main():
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "seqlens": list(w.seqlens),
                    "num_layers": w.num_layers, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "window": w.window, "kept_rows": pipe.kept_rows,
-                   "mode": "L2", "pool": args.pool, "n_sink": args.sinks, "parallelism": "single GPU"},
+                   "mode": args.mode.upper(), "pool": args.pool, "n_sink": args.sinks, "parallelism": "single GPU"},
         "roofline": roof,
         "kernels": kernels,
         "event_ms_per_step": round(step_ms, 4),

@@ -387,7 +387,9 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
   for (int off = 32; off >= 1; off >>= 1) d2 += __shfl_xor(d2, off, 64);
   if (lane == 0) {
     const float shift = pstar * sqrtf(d2);
-    dom[ro] = (p.mode == 1) ? shift * shift : shift;
+    // the isolated pair's term in the call's score: its shift (L2), squared (SQ), or its
+    // attention weight p* (attention sum)
+    dom[ro] = (p.mode == 1) ? shift * shift : (p.mode == 2 ? pstar : shift);
     lse[ro] = (M + __log2f(1.f + lt)) * 0.69314718055994531f;
     jstar[ro] = *(const int*)stat(win, 3);
   }

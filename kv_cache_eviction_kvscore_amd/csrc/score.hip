@@ -26,7 +26,9 @@
 //   (1, 1, 1, -||a_i||^2/2 in three parts) by (-||v_j||^2/2 in three parts, 1, 1, 1);
 //   every part is an exact bf16 split, so the A.V^T accumulator is -D/2 with
 //   D = ||a - v||^2. ||v_j||^2 is summed from the tile in LDS (v_dot2_f32_bf16) one
-//   tile ahead of its use. Per pair: t = s*c1 - lse2, p = exp2(t), and
+//   tile ahead of its use. The Q.K^T chain gets an augmented k-step too: (-lse_i/scale
+//   in three bf16 parts) times (1, 1, 1), so its accumulator is ln p / scale and needs no
+//   per-row register. Per pair: p = exp2(acc * scale * log2 e), and
 //   c*sqrt(D) = sqrt(2) * p*(D/2)*rsq((D/2)*(1-p)^2): two transcendentals and six other
 //   VALU operations; the sqrt(2) (2 in mode SQ) is applied once per token. Pairs
 //   (i, j*_i) are skipped (their term comes exactly from the forward); so are keys after
@@ -139,11 +141,12 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   constexpr int RS = D * 2;               // bytes per key row
   constexpr int CPK = D / 8;              // 16-byte chunks per key row
   constexpr int TB = KT * RS;             // bytes per tensor tile
+  constexpr bool WITH_V = MODE != 2;      // the attention-sum mode reads no V, a or norms
   constexpr int IPT = KT * CPK / 64;      // DMA wave instructions per tensor tile
-  constexpr int NLD = 2 * IPT / NWAVES;   // DMA instructions per wave per tile
+  constexpr int NLD = (WITH_V ? 2 : 1) * IPT / NWAVES;  // DMA instructions per wave per tile
   constexpr int CPL = D / 32;             // chunks per lane in the ||v||^2 sum
   constexpr int PPR = 16 * RB / NKK;      // pairs of a finished block per k-step region
-  static_assert(IPT * 2 % NWAVES == 0 && (NLD == 8 || NLD == 4), "tile shape");
+  static_assert(IPT % NWAVES == 0 && (NLD == 8 || NLD == 4 || NLD == 2), "tile shape");
   static_assert(KT == NWAVES * 16, "norm pass: four lanes per key, 16 keys per wave");
   __shared__ ScoreSmem<D> sm;
 
@@ -191,6 +194,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   // -||v||^2/2 of tile it (landed, visible), into nvx[it & 1]: wave w sums keys
   // 16w..16w+15, four lanes per key (lanes key%16 + 16c), CPL chunks each.
   auto norms = [&](int it) __attribute__((always_inline)) {
+    if constexpr (!WITH_V) return;
     const char* vt = (const char*)sm.tile[it % NBUF][1];
     const int key = 16 * wave + (lane & 15), cg = lane >> 4;
     float ss = 0.f;
@@ -245,6 +249,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
     float ss;
   };
   auto norms_stage = [&](int it, int stage, NormState& st) __attribute__((always_inline)) {
+    if constexpr (!WITH_V) return;
     const int key = 16 * wave + (lane & 15), cg = lane >> 4;
     if (stage == 0) {
       const char* vt = (const char*)sm.tile[it % NBUF][1];
@@ -296,8 +301,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   }
 
   // ---- row operands (A side) of the wave's two row blocks: lane row l32, k-slots 8h..8h+7
-  bf16x8 qf[RB][NKK], af[RB][NKK], aug[RB];
-  float LS[RB][16];
+  bf16x8 qf[RB][NKK], af[RB][NKK], aug[RB], augs[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int rt = wrow0 + 32 * rb + l32;
@@ -308,7 +312,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
     for (int kk = 0; kk < NKK; ++kk) {
       bf16x8 z = {};
       qf[rb][kk] = ok ? *(const bf16x8*)(qrow + 16 * kk + 8 * h) : z;
-      af[rb][kk] = ok ? *(const bf16x8*)(arow + 16 * kk + 8 * h) : z;
+      af[rb][kk] = (ok && WITH_V) ? *(const bf16x8*)(arow + 16 * kk + 8 * h) : z;
     }
     // augmented k-step, A side: (1, 1, 1, -||a_hat||^2/2 in three parts) in slots 0..5
     bf16x8 w8 = {};
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       w8[0] = (__bf16)1.f;
       w8[1] = (__bf16)1.f;
       w8[2] = (__bf16)1.f;
-      if (ok) {
+      if (ok && WITH_V) {
         const Split3 sp = split3(-0.5f * na[rbase + rt]);
         w8[3] = sp.hi;
         w8[4] = sp.mid;
@@ -324,22 +328,38 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       }
     }
     aug[rb] = w8;
-    // row constants in the output layout: element r is row 8(r/4) + 4h + (r%4) of the block
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int ro = wrow0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-      LS[rb][r] = (computing && ro < rows_here) ? lse2[rbase + ro] : INFINITY;  // p = 0 for padding rows
+    // augmented k-step of the Q.K^T chain, A side: -lse_i/scale in three parts (slots 0..2),
+    // so the accumulator is the log-probability / scale; padding rows get -1e30 (p = 0)
+    bf16x8 s8 = {};
+    if (h == 0) {
+      const Split3 sp = split3(ok ? -lse2[rbase + rt] / c1s : -1e30f);
+      s8[0] = sp.hi;
+      s8[1] = sp.mid;
+      s8[2] = sp.lo;
     }
+    augs[rb] = s8;
+  }
+  // B side of that k-step: 1 in slots 0..2 for every key
+  bf16x8 ones3 = {};
+  if (h == 0) {
+    ones3[0] = (__bf16)1.f;
+    ones3[1] = (__bf16)1.f;
+    ones3[2] = (__bf16)1.f;
   }
   // the row operands live in AGPRs (MFMA reads them there), which leaves the VGPRs to
   // the accumulators the VALU consumes
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+a"(qf[rb][kk]), "+a"(af[rb][kk]));
-    asm volatile("" : "+a"(aug[rb]));
+    for (int kk = 0; kk < NKK; ++kk) {
+      asm volatile("" : "+a"(qf[rb][kk]));
+      if constexpr (WITH_V) asm volatile("" : "+a"(af[rb][kk]));
+    }
+    if constexpr (WITH_V) asm volatile("" : "+a"(aug[rb]));
+    asm volatile("" : "+a"(augs[rb]));
   }
-  const float out_scale = (MODE == 0) ? 1.41421356237309515f : 2.f;
+  // sqrt(2) turns sqrt(D/2) into sqrt(D); mode SQ's p^2 (D/2)/(1-p)^2 needs 2; p needs 1
+  const float out_scale = (MODE == 0) ? 1.41421356237309515f : (MODE == 1 ? 2.f : 1.f);
   // byte offset, within a tensor tile, of this lane's operand chunk (key l32, slots
   // 16kk + 8h .. +7) for k-step kk; block b adds 32 rows
   int koff[NKK];
@@ -349,11 +369,13 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   // term of one pair of a finished block: row (rb, r) of this wave, this lane's key
   auto pair_term = [&](auto masked, const BlockAcc<D>& acc, const int rb, const int r, const int key)
       __attribute__((always_inline)) {
-    const float pr = __builtin_amdgcn_exp2f(fmaf(acc.S[rb][r], c1s, -LS[rb][r]));
-    const float ax = fabsf(acc.X[rb][r]);  // D/2
+    const float pr = __builtin_amdgcn_exp2f(acc.S[rb][r] * c1s);
+    const float ax = (MODE == 2) ? 0.f : fabsf(acc.X[rb][r]);  // D/2
     const float om = 1.f - pr;
     float term;
-    if (MODE == 0) {
+    if constexpr (MODE == 2) {
+      term = pr;  // the attention weight itself
+    } else if constexpr (MODE == 0) {
       // p sqrt(D/2) / (1-p) = p (D/2) rsq((D/2)(1-p)^2); the tiny addend keeps D = 0 finite
       term = (pr * ax) * __builtin_amdgcn_rsqf(fmaf(ax * om, om, 1e-30f));
     } else {
@@ -373,15 +395,23 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
 #pragma unroll
     for (int i = 0; i < PPR; ++i) {
       const int pi = pi0 + i;
-      pr[i] = __builtin_amdgcn_exp2f(fmaf(acc.S[pi >> 4][pi & 15], c1s, -LS[pi >> 4][pi & 15]));
+      pr[i] = __builtin_amdgcn_exp2f(acc.S[pi >> 4][pi & 15] * c1s);
     }
+    if constexpr (MODE != 2) {
 #pragma unroll
-    for (int i = 0; i < PPR; ++i) {
-      const int pi = pi0 + i;
-      ax[i] = fabsf(acc.X[pi >> 4][pi & 15]);  // D/2
-      om[i] = 1.f - pr[i];
+      for (int i = 0; i < PPR; ++i) {
+        const int pi = pi0 + i;
+        ax[i] = fabsf(acc.X[pi >> 4][pi & 15]);  // D/2
+        om[i] = 1.f - pr[i];
+      }
     }
-    if (MODE == 0) {
+    if constexpr (MODE == 2) {
+#pragma unroll
+      for (int i = 0; i < PPR; ++i) {
+        w[i] = 1.f;
+        t[i] = pr[i];
+      }
+    } else if constexpr (MODE == 0) {
       // p sqrt(D/2) / (1-p) = p (D/2) rsq((D/2)(1-p)^2); the tiny addend keeps D = 0 finite
 #pragma unroll
       for (int i = 0; i < PPR; ++i) w[i] = __builtin_amdgcn_rsqf(fmaf(ax[i] * om[i], om[i], 1e-30f));
@@ -435,27 +465,32 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
                   auto&& aux) __attribute__((always_inline)) {
     BlockAcc<D> acc;
     Frag cur = f0;
-    const bf16x8 nv = *(const bf16x8*)(nvp + 8 * l32);  // this lane's key
+    bf16x8 nv = {};
+    if constexpr (WITH_V) nv = *(const bf16x8*)(nvp + 8 * l32);  // this lane's key
     float col = 0.f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       Frag nxt;
       if (kk + 1 < NKK) {
         nxt.k = *(const bf16x8*)(kt + koff[kk + 1]);
-        nxt.v = *(const bf16x8*)(kt + TB + koff[kk + 1]);
+        if constexpr (WITH_V) nxt.v = *(const bf16x8*)(kt + TB + koff[kk + 1]);
       } else {
         fnext.k = *(const bf16x8*)(kt_next + koff[0]);
-        fnext.v = *(const bf16x8*)(kt_next + TB + koff[0]);
+        if constexpr (WITH_V) fnext.v = *(const bf16x8*)(kt_next + TB + koff[0]);
       }
       if (kk == NKK / 2) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          acc.X[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aug[rb], nv, acc.X[rb], 0, 0, 0);
+        for (int rb = 0; rb < RB; ++rb) {
+          acc.S[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(augs[rb], ones3, acc.S[rb], 0, 0, 0);
+          if constexpr (WITH_V)
+            acc.X[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aug[rb], nv, acc.X[rb], 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         acc.S[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rb][kk], cur.k, kk ? acc.S[rb] : f32x16{}, 0, 0, 0);
-        acc.X[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb][kk], cur.v, kk ? acc.X[rb] : f32x16{}, 0, 0, 0);
+        if constexpr (WITH_V)
+          acc.X[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb][kk], cur.v, kk ? acc.X[rb] : f32x16{}, 0, 0, 0);
       }
       if constexpr (decltype(has_prev)::value) {
         pair_terms(masked, prev, kk * PPR, key0p + l32, col);
@@ -466,7 +501,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       // within the region: each MFMA followed by a share of the VALU work, so the matrix
       // pipe is fed while the VALU runs
 #pragma unroll
-      for (int i = 0; i < 2 * RB + (kk == NKK / 2 ? RB : 0); ++i) {
+      for (int i = 0; i < (WITH_V ? 2 : 1) * RB * (kk == NKK / 2 ? 2 : 1); ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(KVS_SCHED_MASK, KVS_SCHED_N, 0);
       }
@@ -521,7 +556,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   for (int t = 0; t < ntiles; ++t) {
     if (t + 2 < ntiles) {
       if constexpr (NLD == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else if constexpr (NLD == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -542,7 +578,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       const char* kn = tile_k(t + 1 < ntiles ? t + 1 : t);  // the next tile has landed and is visible
       if (t == 0) {
         fr.k = *(const bf16x8*)(k0 + koff[0]);
-        fr.v = *(const bf16x8*)(k0 + TB + koff[0]);
+        if constexpr (WITH_V) fr.v = *(const bf16x8*)(k0 + TB + koff[0]);
       }
       Frag f1;
       BlockAcc<D> a0;
@@ -619,16 +655,22 @@ hipError_t launch_score(const Dev& p, const void* q, const void* k, const void* 
     if (p.mode == 0)
       hipLaunchKernelGGL((score_kernel<128, 0>), gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
                          (const __bf16*)v, (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
-    else
+    else if (p.mode == 1)
       hipLaunchKernelGGL((score_kernel<128, 1>), gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
+                         (const __bf16*)v, (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
+    else
+      hipLaunchKernelGGL((score_kernel<128, 2>), gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
                          (const __bf16*)v, (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
   } else {
     hipLaunchKernelGGL(score_prep_kernel<64>, gp, dim3(256), 0, st, rows, a, lse, ahat, na, l2);
     if (p.mode == 0)
       hipLaunchKernelGGL((score_kernel<64, 0>), gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
                          (const __bf16*)v, (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
-    else
+    else if (p.mode == 1)
       hipLaunchKernelGGL((score_kernel<64, 1>), gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
+                         (const __bf16*)v, (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
+    else
+      hipLaunchKernelGGL((score_kernel<64, 2>), gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
                          (const __bf16*)v, (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
   }
   return hipGetLastError();

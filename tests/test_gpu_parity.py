@@ -180,3 +180,23 @@ def test_pool_and_sink_edges(pool, n_sink, budget):
     # more sinks than candidates (everything kept)
     w = Workload(f"pool{pool}_sink{n_sink}", 18, 1, 4, 2, 64, (200,), 32, (6,), "fixed", budget)
     _check_all(w, [0], pool=pool, n_sink=n_sink)
+
+
+# ---- attention-sum mode (PyramidKV page, "Observation Window and Aggregated Attention
+# Eviction": S_j = sum over the window rows and heads of A_{h,w,j}; SnapKV's ranking)
+
+
+def test_attention_sum_workload1():
+    _check_all(WORKLOADS[1], [0], mode=api.MODE_ATTN)
+
+
+def test_attention_sum_workload2_all_units():
+    w = WORKLOADS[2]
+    _check_all(w, list(range(w.num_layers * w.num_seqs * w.num_kv_heads)), mode=api.MODE_ATTN)
+
+
+def test_attention_sum_ragged_d64_and_pooled_workload5():
+    _check_all(EDGE[3], list(range(EDGE[3].num_layers * EDGE[3].num_seqs * EDGE[3].num_kv_heads)),
+               mode=api.MODE_ATTN)
+    w = WORKLOADS[5]
+    _check_all(w, sample_units(w, 4), mode=api.MODE_ATTN, pool=13, n_sink=4)
