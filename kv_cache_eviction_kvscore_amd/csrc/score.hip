@@ -5,24 +5,23 @@
 // derives the attention weight on the fly and expands the squared distance
 // ||a||^2 + ||v||^2 - 2<a, v> so each value tile is read once per pass; the score of
 // token j is sum_i p_ij/(1-p_ij) * ||a_i - v_j||_2 (Key Contribution 1), summed over
-// the window rows and the query heads of the KV group.
+// the window rows and the query heads of the KV group. Mode ATTN scores sum_i p_ij
+// instead (PyramidKV page, "Observation Window and Aggregated Attention Eviction").
 //
 // score_prep: a_hat = bf16(a) (the MFMA operand), ||a_hat||^2 from the rounded values
 //   (so the expansion is the exact ||a_hat - v||^2 up to fp32 rounding), lse*log2(e).
-// score_kernel: grid (key chunk, query tile, unit); up to 4 waves of 64 rows (two 32-row
-//   blocks each, one wave per SIMD). Orientation S = Q.K^T, X = A_hat.V^T (rows x keys)
-//   on v_mfma_f32_32x32x16_bf16 with the row operands held in registers. K/V tiles of 64
-//   keys go from HBM straight into LDS (global_load_lds_dwordx4, no register staging)
-//   through a ring of four buffers, so two tiles are in flight while one is computed.
-//   A tile keeps whole key rows (each DMA instruction moves four or eight full rows);
-//   the 16-byte chunks of row r are XOR-swizzled with a function of r so that the 32
-//   keys x 16 slots an MFMA operand needs are read conflict-free with ds_read_b128, and
-//   every fragment read feeds two MFMAs (one per row block). A lane owns one key column
-//   and 16 rows of each 32x32 block, so the sum over rows stays in the lane (plus one
-//   half-wave exchange); the waves' column sums are added in LDS in wave order. The
-//   VALU work of a 32-key block is scheduled between the MFMAs of the next block, so
-//   matrix cores and VALU overlap.
-//   The expansion runs on the matrix cores: one extra k-step per row block multiplies
+// score_kernel: grid (key chunk, query tile, unit); 8 waves of 32 rows, two per SIMD, so
+//   one wave's VALU work overlaps the other's MFMAs. Orientation S = Q.K^T,
+//   X = A_hat.V^T (rows x keys) on v_mfma_f32_32x32x16_bf16 with the row operands held
+//   in AGPRs and the accumulators written to VGPRs. K/V tiles of 64 keys go from HBM
+//   straight into LDS (global_load_lds_dwordx4, no register staging) through a ring of
+//   four buffers, so two tiles are in flight while one is computed. A tile keeps whole
+//   key rows (each DMA instruction moves four or eight full rows); the 16-byte chunks of
+//   row r are XOR-swizzled with a function of r so that the 32 keys x 16 slots an MFMA
+//   operand needs are read conflict-free with ds_read_b128. A lane owns one key column
+//   and 16 rows of the 32x32 block, so the sum over rows stays in the lane (plus one
+//   half-wave exchange); the waves' column sums are added in LDS in wave order.
+//   The expansion runs on the matrix cores: one extra k-step multiplies
 //   (1, 1, 1, -||a_i||^2/2 in three parts) by (-||v_j||^2/2 in three parts, 1, 1, 1);
 //   every part is an exact bf16 split, so the A.V^T accumulator is -D/2 with
 //   D = ||a - v||^2. ||v_j||^2 is summed from the tile in LDS (v_dot2_f32_bf16) one
@@ -39,25 +38,15 @@
 
 #include "kvs_internal.hpp"
 
-#ifndef KVS_SCHED
-#define KVS_SCHED 1
-#endif
-#ifndef KVS_SCHED_MASK
-#define KVS_SCHED_MASK 0x402
-#endif
-#ifndef KVS_SCHED_N
-#define KVS_SCHED_N 6
-#endif
-
 namespace kvs {
 namespace {
 
 constexpr int KT = 64;   // keys per LDS tile
 constexpr int KB = 32;   // keys per MFMA block
 constexpr int NBUF = 4;  // tile ring: computed, next (its ||v||^2 summed), two in flight
-constexpr int NWAVES = 4;
+constexpr int NWAVES = 8;                // 32 rows each: one query tile of up to 256 rows
 constexpr int NTHREADS = 64 * NWAVES;
-constexpr int RB = 2;                    // 32-row blocks per wave
+static_assert(NWAVES * 32 == kRowsPerTileMax, "a workgroup covers one query tile");
 constexpr int kMaxTilesPerChunk = 1024;  // score_chunk <= 65536
 
 template <int D>
@@ -80,9 +69,8 @@ __device__ inline int swz(int r) {
   else return (r & 7) ^ ((r >> 3) & 1);
 }
 
-template <int D>
 struct BlockAcc {
-  f32x16 S[RB], X[RB];
+  f32x16 S, X;
 };
 
 __device__ inline void dma16(const void* g, void* l) {
@@ -144,10 +132,12 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   constexpr bool WITH_V = MODE != 2;      // the attention-sum mode reads no V, a or norms
   constexpr int IPT = KT * CPK / 64;      // DMA wave instructions per tensor tile
   constexpr int NLD = (WITH_V ? 2 : 1) * IPT / NWAVES;  // DMA instructions per wave per tile
-  constexpr int CPL = D / 32;             // chunks per lane in the ||v||^2 sum
-  constexpr int PPR = 16 * RB / NKK;      // pairs of a finished block per k-step region
-  static_assert(IPT % NWAVES == 0 && (NLD == 8 || NLD == 4 || NLD == 2), "tile shape");
-  static_assert(KT == NWAVES * 16, "norm pass: four lanes per key, 16 keys per wave");
+  constexpr int PPR = 4;                  // pairs per lockstep group of the VALU work
+  constexpr int KPW = KT / NWAVES;        // keys per wave in the norm pass and the column sums
+  constexpr int LPK = 64 / KPW;           // lanes per key in the norm pass
+  constexpr int CPN = CPK / LPK;          // 16-byte chunks per lane in the norm pass
+  static_assert(IPT % NWAVES == 0 && NLD >= 1 && NLD <= 4 && (NLD & (NLD - 1)) == 0, "tile shape");
+  static_assert(KT % NWAVES == 0 && 64 % KPW == 0 && CPK % LPK == 0 && CPN >= 1, "norm pass shape");
   __shared__ ScoreSmem<D> sm;
 
   const int u = blockIdx.z, qt = blockIdx.y, ch = blockIdx.x;
@@ -160,7 +150,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   const int ntiles = (int)((c1 - c0 + KT - 1) / KT);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-  const int wrow0 = wave * 32 * RB;  // first tile row of this wave
+  const int wrow0 = wave * 32;  // first tile row of this wave
   const bool computing = wrow0 < p.RT;
   const int64_t rbase = (int64_t)u * p.R + (int64_t)qt * p.RT;  // first row of this tile (global row index)
   const int rows_here = min(p.RT, p.R - qt * p.RT);
@@ -174,10 +164,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   const __bf16* vb0 = v + l * p.vsl + g * p.vsh + p.cu[s] * p.vst;
   float* pout = partial + ((int64_t)(l * p.Hkv + g) * p.Tq + qt) * p.N + p.cu[s];
 
-  // DMA of tile it into ring buffer it % NBUF. Wave instruction f (of 2*IPT) fills the
-  // 64 chunk slots 64(f % IPT) .. +63 of tensor f / IPT: slot (row r, position c') takes
-  // chunk c' ^ swz(r) of key row r. Keys past the chunk load its last row (in bounds,
-  // unconditional); their columns are masked and never written.
+  // DMA of tile it into ring buffer it % NBUF. Wave instruction f (of NLD * NWAVES) fills
+  // the 64 chunk slots 64(f % IPT) .. +63 of tensor f / IPT: slot (row r, position c')
+  // takes chunk c' ^ swz(r) of key row r. Keys past the chunk load its last row (in
+  // bounds, unconditional); their columns are masked and never written.
   auto issue = [&](int it) __attribute__((always_inline)) {
     const int64_t t0 = c0 + (int64_t)it * KT;
 #pragma unroll
@@ -191,16 +181,36 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       dma16(src + 8 * c, &sm.tile[it % NBUF][tensor][(f % IPT) * 64 * 8]);
     }
   };
+  // the same for a full tile, from lane offsets (elements from the tile's first row)
+  // computed once
+  int doff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int f = i * NWAVES + wave;
+    const int tensor = f / IPT, slot = (f % IPT) * 64 + lane;
+    const int r = slot / CPK, c = (slot % CPK) ^ swz<D>(r);
+    doff[i] = r * (int)(tensor == 0 ? kst : vst) + 8 * c;
+  }
+  auto issue_full = [&](int it) __attribute__((always_inline)) {
+    const int64_t t0 = c0 + (int64_t)it * KT;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int f = i * NWAVES + wave;
+      const int tensor = f / IPT;
+      const __bf16* base = tensor == 0 ? kb0 + t0 * kst : vb0 + t0 * vst;
+      dma16(base + doff[i], &sm.tile[it % NBUF][tensor][(f % IPT) * 64 * 8]);
+    }
+  };
   // -||v||^2/2 of tile it (landed, visible), into nvx[it & 1]: wave w sums keys
-  // 16w..16w+15, four lanes per key (lanes key%16 + 16c), CPL chunks each.
+  // KPW*w .. KPW*w+KPW-1, LPK lanes per key (lanes key%KPW + KPW*c), CPN chunks each.
   auto norms = [&](int it) __attribute__((always_inline)) {
     if constexpr (!WITH_V) return;
     const char* vt = (const char*)sm.tile[it % NBUF][1];
-    const int key = 16 * wave + (lane & 15), cg = lane >> 4;
+    const int key = KPW * wave + (lane % KPW), cg = lane / KPW;
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      const int c = CPL * cg + e;
+    for (int e = 0; e < CPN; ++e) {
+      const int c = CPN * cg + e;
       const u32x4 w = *(const u32x4*)(vt + key * RS + ((c ^ swz<D>(key)) << 4));
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -210,79 +220,17 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
         ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
       }
     }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    if (cg == 0) {
-      const Split3 sp = split3(-0.5f * ss);
-      bf16x8 w8 = {};
-      w8[0] = sp.hi;
-      w8[1] = sp.mid;
-      w8[2] = sp.lo;
-      w8[3] = (__bf16)1.f;
-      w8[4] = (__bf16)1.f;
-      w8[5] = (__bf16)1.f;
-      *(bf16x8*)&sm.nvx[it & 1][key][0] = w8;
-    }
-  };
-
-  // The same DMA for a full tile, one instruction at a time (issued between MFMAs): lane
-  // offsets, in elements from the tile's first row, precomputed once.
-  int doff[NLD];
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int f = i * NWAVES + wave;
-    const int tensor = f / IPT, slot = (f % IPT) * 64 + lane;
-    const int r = slot / CPK, c = (slot % CPK) ^ swz<D>(r);
-    doff[i] = r * (int)(tensor == 0 ? kst : vst) + 8 * c;
-  }
-  auto issue_one = [&](int it, int i) __attribute__((always_inline)) {
-    const int f = i * NWAVES + wave;
-    const int tensor = f / IPT;
-    const int64_t t0 = c0 + (int64_t)it * KT;
-    const __bf16* base = tensor == 0 ? kb0 + t0 * kst : vb0 + t0 * vst;
-    dma16(base + doff[i], &sm.tile[it % NBUF][tensor][(f % IPT) * 64 * 8]);
-  };
-  // The norm pass split in stages (run one per MFMA region): 0 reads the chunks, 1 sums
-  // their squares, 2 combines the four lanes of a key, 3 splits and stores.
-  struct NormState {
-    u32x4 w[CPL];
-    float ss;
-  };
-  auto norms_stage = [&](int it, int stage, NormState& st) __attribute__((always_inline)) {
-    if constexpr (!WITH_V) return;
-    const int key = 16 * wave + (lane & 15), cg = lane >> 4;
-    if (stage == 0) {
-      const char* vt = (const char*)sm.tile[it % NBUF][1];
-#pragma unroll
-      for (int e = 0; e < CPL; ++e) {
-        const int c = CPL * cg + e;
-        st.w[e] = *(const u32x4*)(vt + key * RS + ((c ^ swz<D>(key)) << 4));
-      }
-    } else if (stage == 1) {
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < CPL; ++e)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const unsigned wm = st.w[e][m];  // element copied out (see norms)
-          const bf16x2 x = __builtin_bit_cast(bf16x2, wm);
-          ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
-        }
-      st.ss = ss;
-    } else if (stage == 2) {
-      st.ss += __shfl_xor(st.ss, 16, 64);
-      st.ss += __shfl_xor(st.ss, 32, 64);
-    } else if (stage == 3) {
-      const Split3 sp = split3(-0.5f * st.ss);
-      bf16x8 w8 = {};
-      w8[0] = sp.hi;
-      w8[1] = sp.mid;
-      w8[2] = sp.lo;
-      w8[3] = (__bf16)1.f;
-      w8[4] = (__bf16)1.f;
-      w8[5] = (__bf16)1.f;
-      *(bf16x8*)&sm.nvx[it & 1][key][0] = w8;  // the key's four lanes store the same entry
-    }
+    for (int off = KPW; off < 64; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    const Split3 sp = split3(-0.5f * ss);
+    bf16x8 w8 = {};
+    w8[0] = sp.hi;
+    w8[1] = sp.mid;
+    w8[2] = sp.lo;
+    w8[3] = (__bf16)1.f;
+    w8[4] = (__bf16)1.f;
+    w8[5] = (__bf16)1.f;
+    *(bf16x8*)&sm.nvx[it & 1][key][0] = w8;  // the key's lanes store the same entry
   };
 
   // ---- per-row masks in LDS, tile flags for rows whose argmax falls in this chunk
@@ -290,7 +238,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   for (int t = tid; t < 3 * NWAVES * KT; t += NTHREADS) (&sm.red[0][0][0])[t] = 0.f;  // waves that never compute add zeros
   for (int t = tid; t < kRowsPerTileMax; t += NTHREADS) {
     const bool ok = t < rows_here;
-    sm.tlim[t] = ok ? (int)(n - p.W + (qt * p.RT + t) % p.W) : -1;
+    sm.tlim[t] = ok ? (int)(n - W + (qt * p.RT + t) % W) : -1;
     sm.jst[t] = ok ? jstar[rbase + t] : -1;
   }
   issue(0);
@@ -300,22 +248,24 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
     if (js >= c0 && js < c1) sm.flag[(js - c0) / KT] = 1;
   }
 
-  // ---- row operands (A side) of the wave's two row blocks: lane row l32, k-slots 8h..8h+7
-  bf16x8 qf[RB][NKK], af[RB][NKK], aug[RB], augs[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int rt = wrow0 + 32 * rb + l32;
+  // ---- row operands (A side): lane row l32 of the wave's 32, k-slots 8h..8h+7
+  bf16x8 qf[NKK], af[NKK], aug, augs;
+  {
+    const int rt = wrow0 + l32;
     const bool ok = computing && rt < rows_here;
     const __bf16* qrow = q + (rbase + (ok ? rt : 0)) * D;
     const __bf16* arow = ahat + (rbase + (ok ? rt : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       bf16x8 z = {};
-      qf[rb][kk] = ok ? *(const bf16x8*)(qrow + 16 * kk + 8 * h) : z;
-      af[rb][kk] = (ok && WITH_V) ? *(const bf16x8*)(arow + 16 * kk + 8 * h) : z;
+      qf[kk] = ok ? *(const bf16x8*)(qrow + 16 * kk + 8 * h) : z;
+      af[kk] = (ok && WITH_V) ? *(const bf16x8*)(arow + 16 * kk + 8 * h) : z;
     }
-    // augmented k-step, A side: (1, 1, 1, -||a_hat||^2/2 in three parts) in slots 0..5
+    // augmented k-step of the A.V^T chain: (1, 1, 1, -||a_hat||^2/2 in three parts) in slots 0..5
     bf16x8 w8 = {};
+    // and of the Q.K^T chain: -lse_i/scale in three parts (slots 0..2), so the accumulator
+    // is the log-probability / scale; padding rows get -1e30 (p = 0)
+    bf16x8 s8 = {};
     if (h == 0) {
       w8[0] = (__bf16)1.f;
       w8[1] = (__bf16)1.f;
@@ -326,20 +276,15 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
         w8[4] = sp.mid;
         w8[5] = sp.lo;
       }
-    }
-    aug[rb] = w8;
-    // augmented k-step of the Q.K^T chain, A side: -lse_i/scale in three parts (slots 0..2),
-    // so the accumulator is the log-probability / scale; padding rows get -1e30 (p = 0)
-    bf16x8 s8 = {};
-    if (h == 0) {
       const Split3 sp = split3(ok ? -lse2[rbase + rt] / c1s : -1e30f);
       s8[0] = sp.hi;
       s8[1] = sp.mid;
       s8[2] = sp.lo;
     }
-    augs[rb] = s8;
+    aug = w8;
+    augs = s8;
   }
-  // B side of that k-step: 1 in slots 0..2 for every key
+  // B side of the Q.K^T k-step: 1 in slots 0..2 for every key
   bf16x8 ones3 = {};
   if (h == 0) {
     ones3[0] = (__bf16)1.f;
@@ -349,59 +294,31 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   // the row operands live in AGPRs (MFMA reads them there), which leaves the VGPRs to
   // the accumulators the VALU consumes
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      asm volatile("" : "+a"(qf[rb][kk]));
-      if constexpr (WITH_V) asm volatile("" : "+a"(af[rb][kk]));
-    }
-    if constexpr (WITH_V) asm volatile("" : "+a"(aug[rb]));
-    asm volatile("" : "+a"(augs[rb]));
+  for (int kk = 0; kk < NKK; ++kk) {
+    asm volatile("" : "+a"(qf[kk]));
+    if constexpr (WITH_V) asm volatile("" : "+a"(af[kk]));
   }
+  if constexpr (WITH_V) asm volatile("" : "+a"(aug));
+  asm volatile("" : "+a"(augs));
   // sqrt(2) turns sqrt(D/2) into sqrt(D); mode SQ's p^2 (D/2)/(1-p)^2 needs 2; p needs 1
   const float out_scale = (MODE == 0) ? 1.41421356237309515f : (MODE == 1 ? 2.f : 1.f);
   // byte offset, within a tensor tile, of this lane's operand chunk (key l32, slots
   // 16kk + 8h .. +7) for k-step kk; block b adds 32 rows
-  int koff[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) koff[kk] = l32 * RS + (((2 * kk) ^ h ^ swz<D>(l32)) << 4);
+  const int kbase = l32 * RS, khs = h ^ swz<D>(l32);
+  auto koff = [&](int kk) __attribute__((always_inline)) { return kbase + (((2 * kk) ^ khs) << 4); };
 
-  // term of one pair of a finished block: row (rb, r) of this wave, this lane's key
-  auto pair_term = [&](auto masked, const BlockAcc<D>& acc, const int rb, const int r, const int key)
-      __attribute__((always_inline)) {
-    const float pr = __builtin_amdgcn_exp2f(acc.S[rb][r] * c1s);
-    const float ax = (MODE == 2) ? 0.f : fabsf(acc.X[rb][r]);  // D/2
-    const float om = 1.f - pr;
-    float term;
-    if constexpr (MODE == 2) {
-      term = pr;  // the attention weight itself
-    } else if constexpr (MODE == 0) {
-      // p sqrt(D/2) / (1-p) = p (D/2) rsq((D/2)(1-p)^2); the tiny addend keeps D = 0 finite
-      term = (pr * ax) * __builtin_amdgcn_rsqf(fmaf(ax * om, om, 1e-30f));
-    } else {
-      term = (pr * pr * ax) * __builtin_amdgcn_rcpf(fmaf(om, om, 1e-30f));  // p^2 (D/2) / (1-p)^2
-    }
-    if constexpr (decltype(masked)::value) {
-      const int rt = wrow0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-      term = (key > sm.tlim[rt] || key == sm.jst[rt]) ? 0.f : term;
-    }
-    return term;
-  };
-  // adds the terms of pairs pi0 .. pi0+PPR-1 (pair pi = row (pi / 16, pi % 16)) to col,
-  // written stage by stage so the PPR independent chains interleave
-  auto pair_terms = [&](auto masked, const BlockAcc<D>& acc, const int pi0, const int key, float& col)
+  // adds the terms of pairs pi0 .. pi0+PPR-1 (pair = row of the output layout: element r
+  // is row 8(r/4) + 4h + (r%4)) to col, written stage by stage so the PPR independent
+  // chains interleave
+  auto pair_terms = [&](auto masked, const BlockAcc& acc, const int pi0, const int key, float& col)
       __attribute__((always_inline)) {
     float pr[PPR], ax[PPR], om[PPR], w[PPR], t[PPR];
 #pragma unroll
-    for (int i = 0; i < PPR; ++i) {
-      const int pi = pi0 + i;
-      pr[i] = __builtin_amdgcn_exp2f(acc.S[pi >> 4][pi & 15] * c1s);
-    }
+    for (int i = 0; i < PPR; ++i) pr[i] = __builtin_amdgcn_exp2f(acc.S[pi0 + i] * c1s);
     if constexpr (MODE != 2) {
 #pragma unroll
       for (int i = 0; i < PPR; ++i) {
-        const int pi = pi0 + i;
-        ax[i] = fabsf(acc.X[pi >> 4][pi & 15]);  // D/2
+        ax[i] = fabsf(acc.X[pi0 + i]);  // D/2
         om[i] = 1.f - pr[i];
       }
     }
@@ -409,7 +326,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
 #pragma unroll
       for (int i = 0; i < PPR; ++i) {
         w[i] = 1.f;
-        t[i] = pr[i];
+        t[i] = pr[i];  // the attention weight itself
       }
     } else if constexpr (MODE == 0) {
       // p sqrt(D/2) / (1-p) = p (D/2) rsq((D/2)(1-p)^2); the tiny addend keeps D = 0 finite
@@ -427,105 +344,50 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
 #pragma unroll
     for (int i = 0; i < PPR; ++i) {
       if constexpr (decltype(masked)::value) {
-        const int pi = pi0 + i, r = pi & 15;
-        const int rt = wrow0 + 32 * (pi >> 4) + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int r = pi0 + i;
+        const int rt = wrow0 + 8 * (r >> 2) + 4 * h + (r & 3);
         col += (key > sm.tlim[rt] || key == sm.jst[rt]) ? 0.f : t[i] * w[i];
       } else {
         col = fmaf(t[i], w[i], col);
       }
     }
   };
-  // a finished block's column sums (both half-waves hold the sum and write it)
-  auto store_col = [&](float col, float* red) __attribute__((always_inline)) {
-    col += __shfl_xor(col, 32, 64);
-    red[l32] = col;
-  };
-  // the VALU work of a finished block alone (the last block of the chunk)
-  auto valu = [&](auto masked, const BlockAcc<D>& acc, const int key0, float* red) __attribute__((always_inline)) {
-    float col = 0.f;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) col += pair_term(masked, acc, rb, r, key0 + l32);
-    store_col(col, red);
-  };
-  struct Frag {
-    bf16x8 k, v;
-  };
-  // The MFMAs of one 32-key block (K rows at kt, V rows at kt + TB, the block's first
-  // nvx entry at nvp; S = Q.K^T, X = -D/2), one region per k-step: its four MFMAs and the
-  // terms of PPR pairs of the previous block (prev, keys key0p.., column sums to redp),
-  // fenced so that matrix cores and VALU overlap and the PPR independent pair chains
-  // hide each other's latency. Operand chunks are read one k-step ahead; the last
-  // k-step reads the first chunks of the next block (at kt_next) into fnext. f0 holds
-  // this block's first chunks. The augmented k-step sits mid-chain, off the chain's tail.
-  // aux(kk) adds other work (DMA issue, norm stages) to region kk.
-  auto step = [&](auto masked, auto has_prev, const char* kt, const __bf16* nvp, const Frag f0,
-                  const char* kt_next, Frag& fnext, const BlockAcc<D>& prev, const int key0p, float* redp,
-                  auto&& aux) __attribute__((always_inline)) {
-    BlockAcc<D> acc;
-    Frag cur = f0;
+  // the MFMAs of 32-key block b of ring tile it: S = ln p / scale, X = -D/2
+  auto mfma_block = [&](int it, int b) __attribute__((always_inline)) {
+    const char* kt = (const char*)sm.tile[it % NBUF][0] + b * KB * RS;
+    BlockAcc acc;
     bf16x8 nv = {};
-    if constexpr (WITH_V) nv = *(const bf16x8*)(nvp + 8 * l32);  // this lane's key
-    float col = 0.f;
+    if constexpr (WITH_V) nv = *(const bf16x8*)&sm.nvx[it & 1][b * KB + l32][0];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      Frag nxt;
-      if (kk + 1 < NKK) {
-        nxt.k = *(const bf16x8*)(kt + koff[kk + 1]);
-        if constexpr (WITH_V) nxt.v = *(const bf16x8*)(kt + TB + koff[kk + 1]);
-      } else {
-        fnext.k = *(const bf16x8*)(kt_next + koff[0]);
-        if constexpr (WITH_V) fnext.v = *(const bf16x8*)(kt_next + TB + koff[0]);
+      const bf16x8 kx = *(const bf16x8*)(kt + koff(kk));
+      acc.S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kk], kx, kk ? acc.S : f32x16{}, 0, 0, 0);
+      if constexpr (WITH_V) {
+        const bf16x8 vx = *(const bf16x8*)(kt + TB + koff(kk));
+        acc.X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], vx, kk ? acc.X : f32x16{}, 0, 0, 0);
       }
-      if (kk == NKK / 2) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          acc.S[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(augs[rb], ones3, acc.S[rb], 0, 0, 0);
-          if constexpr (WITH_V)
-            acc.X[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aug[rb], nv, acc.X[rb], 0, 0, 0);
-        }
+      if (kk == NKK / 2) {  // the augmented k-steps sit mid-chain, off the chains' tails
+        acc.S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(augs, ones3, acc.S, 0, 0, 0);
+        if constexpr (WITH_V) acc.X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aug, nv, acc.X, 0, 0, 0);
       }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        acc.S[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rb][kk], cur.k, kk ? acc.S[rb] : f32x16{}, 0, 0, 0);
-        if constexpr (WITH_V)
-          acc.X[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rb][kk], cur.v, kk ? acc.X[rb] : f32x16{}, 0, 0, 0);
-      }
-      if constexpr (decltype(has_prev)::value) {
-        pair_terms(masked, prev, kk * PPR, key0p + l32, col);
-        asm volatile("" : "+v"(col));  // the region's VALU work stays in the region
-      }
-      aux(kk);
-#if KVS_SCHED
-      // within the region: each MFMA followed by a share of the VALU work, so the matrix
-      // pipe is fed while the VALU runs
-#pragma unroll
-      for (int i = 0; i < (WITH_V ? 2 : 1) * RB * (kk == NKK / 2 ? 2 : 1); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(KVS_SCHED_MASK, KVS_SCHED_N, 0);
-      }
-#endif
-      __builtin_amdgcn_sched_barrier(0);
-      if (kk + 1 < NKK) cur = nxt;
     }
-    if constexpr (decltype(has_prev)::value) store_col(col, redp);
     return acc;
   };
-  // tile it's column sums, added in wave order (the same order as the in-region flush)
-  static_assert(NWAVES == 4, "column sums add four wave rows");
-  auto flush_cols = [&](int it) __attribute__((always_inline)) {
-    if (tid < KT) {
-      const int64_t j = c0 + (int64_t)it * KT + tid;
-      if (j < c1) {
-        const float(*rd)[KT] = sm.red[it % 3];
-        pout[j] = (((rd[0][tid] + rd[1][tid]) + rd[2][tid]) + rd[3][tid]) * out_scale;
-      }
-    }
+  // a column's sum over the wave rows of red, in wave order (every flush adds the same way)
+  auto col_sum = [&](const float(*rd)[KT], int col) __attribute__((always_inline)) {
+    float acc = rd[0][col];
+#pragma unroll
+    for (int w = 1; w < NWAVES; ++w) acc += rd[w][col];
+    return acc * out_scale;
+  };
+  auto flush_share = [&](int it) __attribute__((always_inline)) {  // tile it's columns KPW*w ..
+    const int fcol = KPW * wave + (lane % KPW);
+    const int64_t j = c0 + (int64_t)it * KT + fcol;
+    if (j < c1) pout[j] = col_sum(sm.red[it % 3], fcol);  // the lanes of a column store the same value
   };
   // tile flags as bits: lane L holds tiles 32L .. 32L+31 (a chunk has at most 1024 tiles)
   static_assert(kMaxTilesPerChunk <= 32 * 64, "flag bits");
-  unsigned flagbits = 0;  // filled once the flags are visible (below)
+  unsigned flagbits = 0;
   auto special = [&](int it) __attribute__((always_inline)) {
     const int64_t t0 = c0 + (int64_t)it * KT;
     const unsigned fb = (unsigned)__builtin_amdgcn_readlane((int)flagbits, it >> 5);
@@ -536,10 +398,12 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
 
   // Ring schedule (one barrier per tile). At the top of iteration t, tiles t+1 and t+2
   // are in flight; waiting until at most NLD of this wave's DMA instructions are
-  // outstanding means tile t+1 has landed. After the barrier: buffer (t+3)%4, last read
-  // by tile t-1's MFMAs, takes tile t+3; tile t+1's norms are summed; tile t is computed
-  // from buffer t%4 with the norms summed one iteration earlier. The VALU work of a
-  // tile's second block runs in the next iteration, between the MFMAs of its first.
+  // outstanding means tile t+1 has landed. After the barrier: the column sums of tile t-1
+  // are complete and are written; buffer (t+3)%4, last read by tile t-1's MFMAs, takes
+  // tile t+3; tile t+1's norms are summed; tile t is computed from buffer t%4 with the
+  // norms summed one iteration earlier. The two waves on a SIMD (w and w + NWAVES/2) do
+  // the side work at different points of the iteration, so the SIMD's MFMA pipe keeps a
+  // wave to feed it.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 landed
   __syncthreads();
   for (int i = 0; i < 32; ++i) {
@@ -549,96 +413,47 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   norms(0);
   if (ntiles > 1) issue(1);
   if (ntiles > 2) issue(2);
-  BlockAcc<D> pend;
-  Frag fr;
-  auto tile_k = [&](int it) __attribute__((always_inline)) { return (const char*)sm.tile[it % NBUF][0]; };
-  auto key0 = [&](int it, int b) __attribute__((always_inline)) { return (int)(c0 + (int64_t)it * KT + b * KB); };
   for (int t = 0; t < ntiles; ++t) {
     if (t + 2 < ntiles) {
-      if constexpr (NLD == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else if constexpr (NLD == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      if constexpr (NLD == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else if constexpr (NLD == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
-    // fast path: the DMA of tile t+3, the column sums of tile t-2 and the norms of tile
-    // t+1 run inside the MFMA regions; it needs a previous block and a full tile t+3
-    // (gfast is uniform over the workgroup: it decides who writes tile t-2's column sums)
-    const bool gfast = t >= 1 && t + 3 < ntiles && c0 + (int64_t)(t + 4) * KT <= c1;
-    const bool fast = computing && gfast;
-    if (!fast) {
-      if (t + 3 < ntiles) issue(t + 3);
+    auto side = [&]() __attribute__((always_inline)) {
+      if (t >= 1) flush_share(t - 1);
+      if (t + 3 < ntiles) {
+        if (c0 + (int64_t)(t + 4) * KT <= c1) issue_full(t + 3);
+        else issue(t + 3);
+      }
       if (t + 1 < ntiles) norms(t + 1);
-    }
-    if (!gfast && t >= 2) flush_cols(t - 2);
+    };
+    const bool early = !computing || wave < NWAVES / 2;
+    if (early) side();
     if (computing) {
-      const char* k0 = tile_k(t);
-      const char* k1 = k0 + KB * RS;
-      const char* kn = tile_k(t + 1 < ntiles ? t + 1 : t);  // the next tile has landed and is visible
-      if (t == 0) {
-        fr.k = *(const bf16x8*)(k0 + koff[0]);
-        if constexpr (WITH_V) fr.v = *(const bf16x8*)(k0 + TB + koff[0]);
-      }
-      Frag f1;
-      BlockAcc<D> a0;
-      float* redp = sm.red[(t + 2) % 3][wave] + KB;  // tile t-1, block 1
-      float* red0 = sm.red[t % 3][wave];
-      auto none = [](int) {};
-      if (fast) {
-        // tile t-2's columns 16w .. 16w+15 by wave w (four lanes per column store the same value)
-        float fl[NWAVES];
-        const int fcol = 16 * wave + (lane & 15);
-        auto aux_a = [&](int kk) __attribute__((always_inline)) {
+      const bool sp = special(t);
 #pragma unroll
-          for (int i = 0; i < NLD; ++i)
-            if (i * NKK / NLD == kk) issue_one(t + 3, i);
-          if (kk == 0) {
+      for (int b = 0; b < KT / KB; ++b) {
+        if (b == 1 && !early) side();
+        const BlockAcc acc = mfma_block(t, b);
+        float col = 0.f;
+        const int key = (int)(c0 + (int64_t)t * KT + b * KB) + l32;
+        if (sp) {
 #pragma unroll
-            for (int w = 0; w < NWAVES; ++w) fl[w] = sm.red[(t + 1) % 3][w][fcol];
-          } else if (kk == 2) {
-            pout[c0 + (int64_t)(t - 2) * KT + fcol] = (((fl[0] + fl[1]) + fl[2]) + fl[3]) * out_scale;
-          }
-        };
-        NormState ns;
-        auto aux_b = [&](int kk) __attribute__((always_inline)) {
-          if (kk < 4) norms_stage(t + 1, kk, ns);
-        };
-        if (t >= 2) {
-          if (special(t - 1)) a0 = step(T_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp, aux_a);
-          else a0 = step(F_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp, aux_a);
-        } else {  // t == 1: no tile t-2 to flush
-          auto aux_a1 = [&](int kk) __attribute__((always_inline)) {
+          for (int pi = 0; pi < 16; pi += PPR) pair_terms(T_{}, acc, pi, key, col);
+        } else {
 #pragma unroll
-            for (int i = 0; i < NLD; ++i)
-              if (i * NKK / NLD == kk) issue_one(t + 3, i);
-          };
-          if (special(t - 1)) a0 = step(T_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp, aux_a1);
-          else a0 = step(F_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp, aux_a1);
+          for (int pi = 0; pi < 16; pi += PPR) pair_terms(F_{}, acc, pi, key, col);
         }
-        if (special(t)) pend = step(T_{}, T_{}, k1, sm.nvx[t & 1][KB], f1, kn, fr, a0, key0(t, 0), red0, aux_b);
-        else pend = step(F_{}, T_{}, k1, sm.nvx[t & 1][KB], f1, kn, fr, a0, key0(t, 0), red0, aux_b);
-      } else {
-        if (t == 0) a0 = step(F_{}, F_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, 0, redp, none);
-        else if (special(t - 1)) a0 = step(T_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp, none);
-        else a0 = step(F_{}, T_{}, k0, sm.nvx[t & 1][0], fr, k1, f1, pend, key0(t - 1, 1), redp, none);
-        if (special(t)) pend = step(T_{}, T_{}, k1, sm.nvx[t & 1][KB], f1, kn, fr, a0, key0(t, 0), red0, none);
-        else pend = step(F_{}, T_{}, k1, sm.nvx[t & 1][KB], f1, kn, fr, a0, key0(t, 0), red0, none);
+        col += __shfl_xor(col, 32, 64);  // both half-waves hold the sum and write it
+        sm.red[t % 3][wave][b * KB + l32] = col;
       }
-    } else if (gfast && t >= 2) {  // this wave's share of tile t-2's column sums
-      const int fcol = 16 * wave + (lane & 15);
-      const float(*rd)[KT] = sm.red[(t + 1) % 3];
-      pout[c0 + (int64_t)(t - 2) * KT + fcol] = (((rd[0][fcol] + rd[1][fcol]) + rd[2][fcol]) + rd[3][fcol]) * out_scale;
     }
-  }
-  if (computing) {
-    float* red1 = sm.red[(ntiles - 1) % 3][wave] + KB;
-    if (special(ntiles - 1)) valu(T_{}, pend, key0(ntiles - 1, 1), red1);
-    else valu(F_{}, pend, key0(ntiles - 1, 1), red1);
   }
   __syncthreads();
-  if (ntiles >= 2) flush_cols(ntiles - 2);
-  flush_cols(ntiles - 1);
+  flush_share(ntiles - 1);
 }
 
 }  // namespace
@@ -650,28 +465,20 @@ hipError_t launch_score(const Dev& p, const void* q, const void* k, const void* 
   float* na = (float*)((char*)ws + (size_t)rows * p.d * 2);
   float* l2 = na + rows;
   const dim3 gp((unsigned)((rows + 3) / 4)), gs(p.score_chunks, p.Tq, p.U);
+  auto run = [&](auto kern) {
+    hipLaunchKernelGGL(kern, gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                       (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
+  };
   if (p.d == 128) {
     hipLaunchKernelGGL(score_prep_kernel<128>, gp, dim3(256), 0, st, rows, a, lse, ahat, na, l2);
-    if (p.mode == 0)
-      hipLaunchKernelGGL((score_kernel<128, 0>), gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
-                         (const __bf16*)v, (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
-    else if (p.mode == 1)
-      hipLaunchKernelGGL((score_kernel<128, 1>), gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
-                         (const __bf16*)v, (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
-    else
-      hipLaunchKernelGGL((score_kernel<128, 2>), gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
-                         (const __bf16*)v, (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
+    if (p.mode == 0) run(score_kernel<128, 0>);
+    else if (p.mode == 1) run(score_kernel<128, 1>);
+    else run(score_kernel<128, 2>);
   } else {
     hipLaunchKernelGGL(score_prep_kernel<64>, gp, dim3(256), 0, st, rows, a, lse, ahat, na, l2);
-    if (p.mode == 0)
-      hipLaunchKernelGGL((score_kernel<64, 0>), gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
-                         (const __bf16*)v, (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
-    else if (p.mode == 1)
-      hipLaunchKernelGGL((score_kernel<64, 1>), gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
-                         (const __bf16*)v, (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
-    else
-      hipLaunchKernelGGL((score_kernel<64, 2>), gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
-                         (const __bf16*)v, (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
+    if (p.mode == 0) run(score_kernel<64, 0>);
+    else if (p.mode == 1) run(score_kernel<64, 1>);
+    else run(score_kernel<64, 2>);
   }
   return hipGetLastError();
 }
