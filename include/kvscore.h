@@ -99,7 +99,7 @@ typedef struct kvscore_problem {
   int32_t head_dim;          /* d: 64 or 128 */
   int32_t window;            /* W >= 1; every sequence must be longer than W */
   const int64_t* cu_seqlens; /* HOST array [S+1]: 0 = cu[0] < cu[1] < ... ; n_s = cu[s+1]-cu[s] */
-  int64_t k_strides[3];      /* layer, KV-head, token strides of k in elements */
+  int64_t k_strides[3];      /* layer, KV-head, token strides of k in elements (token stride < 2^22) */
   int64_t v_strides[3];      /* same for v */
   int32_t mode;              /* KVSCORE_MODE_L2, KVSCORE_MODE_SQ or KVSCORE_MODE_ATTN */
   float softmax_scale;       /* multiplies q.k; <= 0 selects 1/sqrt(d) */

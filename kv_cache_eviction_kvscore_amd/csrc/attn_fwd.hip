@@ -9,41 +9,64 @@
 // pair's exact shift p* * ||a^(-j*) - v_j*|| (the identity of the same section:
 // c * ||a - v_j|| = p * ||a^(-j) - v_j||).
 //
-// Pass 1 (fwd_partial): grid (key chunk, query tile, unit). 8 waves; a computing wave
-// owns 32 rows, one row per lane (both half-waves hold the row). S^T = K.Q^T on
-// v_mfma_f32_32x32x16_bf16 and O^T += V^T.P^T on v_mfma_f32_32x32x16_f16; K/V tiles of
-// 64 keys are staged in LDS (registers prefetch the next tile), V converted to fp16
-// there (exact for |v| < 65504); V^T fragments come from ds_read_tr16_b64. P enters the
-// product in fp16 (unit roundoff 2^-11, eight times finer than bf16: with few keys per
-// row the rounding of P does not average out, and a^(-j*) feeds the isolated term),
-// pre-scaled by 2^14 so probabilities down to ~4e-9 stay normal; the scale is folded
-// into the exp2 argument and removed once at the end.
+// Pass 1 (fwd_partial): grid (key chunk, query tile, unit). 8 waves, two per SIMD; a
+// computing wave owns 32 rows, one row per lane (both half-waves hold the row).
+// S^T = K.Q^T on v_mfma_f32_32x32x16_bf16 and O^T += V^T.P^T on v_mfma_f32_32x32x16_f16.
+// K/V tiles of 64 keys go from HBM straight into LDS (global_load_lds_dwordx4) through
+// a ring of four buffers, two tiles in flight while one is computed; the 16-byte chunks
+// of each row are XOR-swizzled with a function of the row so that the K operand reads
+// (ds_read_b128) and the V^T transpose reads (ds_read_tr16_b64) are conflict-free. One
+// tile ahead of its use, V is converted to fp16 in place (exact for |v| < 65504). P
+// enters the product in fp16 (unit roundoff 2^-11, eight times finer than bf16: with
+// few keys per row the rounding of P does not average out, and a^(-j*) feeds the
+// isolated term), pre-scaled by 2^14 so probabilities down to ~4e-9 stay normal; the
+// scale is folded into the exp2 argument and removed once at the end.
 // Online softmax in the log2 domain. When a row's running max moves to a key of the
-// current tile, the previous argmax's value row (kept in LDS, weight 1 at the old
-// max) is folded into the rest and the new one is copied in.
+// current tile, the previous argmax's value row (held in the lane's registers, weight 1
+// at the old max) is folded into the rest and the new one is read from the tile.
 // Pass 2 (fwd_combine): one wave per row merges the chunks' (m, l_rest, acc_rest, j*,
 // v*) in ascending chunk order and writes a, lse, j*, and the isolated term.
+#include <type_traits>
+
 #include "kvs_internal.hpp"
 
 namespace kvs {
 namespace {
 
-constexpr int KT = 64;    // keys per compute sub-tile
-constexpr int KL = 64;    // keys per LDS tile (one barrier pair, prefetched one tile ahead)
-constexpr int KPAD = 8;   // bf16 padding per K row in LDS (b128 reads: 8 lanes hit distinct banks)
-constexpr int VPAD = 16;  // bf16 padding per V row in LDS (transpose reads: 4 keys x 32 B distinct banks)
-constexpr int SPAD = 4;   // bf16 padding per v* row
-constexpr int NTHREADS = 512;
+constexpr int KT = 64;     // keys per tile
+constexpr int NBUF = 4;    // tile ring: computed, next (converted to fp16 now), two in flight
+constexpr int NWAVES = 8;  // 32 rows each
+constexpr int NTHREADS = 64 * NWAVES;
+static_assert(NWAVES * 32 == kRowsPerTileMax, "a workgroup covers one query tile");
 constexpr float kPScale = 16384.f;     // 2^14: P is carried as 2^14 * p in the rest sums
 constexpr float kPScaleLog2 = 14.f;
 constexpr float kPUnscale = 1.f / 16384.f;
+constexpr float kSlack = 1.5f;  // log2 units the rest's max may exceed its reference: 2^15.5 < fp16 max
 
 template <int D>
 struct FwdSmem {
-  alignas(16) __bf16 k[KL][D + KPAD];  // 16-byte alignment lets the tile reads be ds_read_b128
-  alignas(16) _Float16 v[KL][D + VPAD];
-  alignas(16) _Float16 vstar[kRowsPerTileMax][D + SPAD];
+  // [buffer][tensor K, V][key][D]: K in bf16, V in bf16 as it lands and fp16 once converted
+  alignas(16) unsigned short tile[NBUF][2][KT * D];
 };
+
+// position of 16-byte chunk c of row r is c ^ swz(r).
+// K (read as the A operand: 32 rows at one chunk index): sixteen consecutive rows hit
+// sixteen different bank groups (D=64: eight rows within 128 bytes), swz(r + 32) = swz(r).
+template <int D>
+__device__ inline int swz_k(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return (r & 7) ^ ((r >> 3) & 1);
+}
+// V (read transposed: a half-wave takes 4 consecutive rows r0..r0+3, r0 = 0 mod 4, at the
+// 4 chunks 4b..4b+3): the rows' 64-byte groups must cover 256 distinct bytes of banks.
+// D=128 rows are 256 bytes: rows differ in bits 2-3 of the chunk index. D=64 rows are 128
+// bytes (rows r, r+2 share banks): rows r0 and r0+2 differ in bit 2.
+template <int D>
+__device__ inline int swz_v(int r) {
+  if constexpr (D == 128) return (r & 3) << 2;
+  else return ((r >> 1) & 1) << 2;
+}
+
 
 // 8 bf16 -> 8 fp16 (exact in fp16's normal range; saturating towards zero beyond it)
 __device__ inline u32x4 bf16x8_to_f16x8(u32x4 u) {
@@ -57,6 +80,12 @@ __device__ inline u32x4 bf16x8_to_f16x8(u32x4 u) {
   return u32x4{r[0], r[1], r[2], r[3]};
 }
 
+// wait until at most N of this wave's vector memory instructions are outstanding
+template <int N>
+__device__ inline void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ inline float wave_shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
 __device__ inline int wave_shfl_xor_i(int x, int m) { return __shfl_xor(x, m, 64); }
 
@@ -64,11 +93,13 @@ template <int D>
 __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf16* __restrict__ q,
                                                                const __bf16* __restrict__ k,
                                                                const __bf16* __restrict__ v, float* __restrict__ ws) {
-  constexpr int NKK = D / 16;  // k-steps of the QK^T contraction
-  constexpr int NDB = D / 32;  // 32-wide d blocks of O^T
-  constexpr int CPR = D / 8;   // 16-byte chunks per row
-  constexpr int NST = KL * CPR / NTHREADS;  // 16-byte chunks per thread per tensor
-  static_assert(NST >= 1, "tile too small for the block");
+  constexpr int NKK = D / 16;              // k-steps of the QK^T contraction
+  constexpr int NDB = D / 32;              // 32-wide d blocks of O^T
+  constexpr int CPK = D / 8;               // 16-byte chunks per row
+  constexpr int RS = D * 2;                // bytes per row
+  constexpr int IPT = KT * CPK / 64;       // DMA wave instructions per tensor tile
+  constexpr int NLD = 2 * IPT / NWAVES;    // DMA instructions per wave per tile
+  static_assert(IPT % NWAVES == 0 && (NLD == 2 || NLD == 4), "tile shape");
   __shared__ FwdSmem<D> sm;
 
   const int u = blockIdx.z, qt = blockIdx.y, ch = blockIdx.x;
@@ -78,13 +109,18 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
   const int64_t c0 = (int64_t)ch * p.fwd_chunk;
   if (c0 >= n) return;  // uniform: this sequence has fewer chunks
   const int64_t c1 = (n < c0 + p.fwd_chunk) ? n : c0 + p.fwd_chunk;
+  const int ntiles = (int)((c1 - c0 + KT - 1) / KT);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const bool computing = wave * 32 < p.RT;
   const int row_t = wave * 32 + l32;
   const int row = qt * p.RT + row_t;
   const bool row_ok = computing && row < p.R;
   const int64_t tlim = row_ok ? n - p.W + (row % p.W) : n - 1;  // last key the row sees
+  const int W = p.W;
+  const float c1s = p.c1;
+  const int64_t kst = p.kst, vst = p.vst;
 
   bf16x8 qf[NKK];
   {
@@ -95,29 +131,153 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       qf[kk] = row_ok ? *(const bf16x8*)(qrow + 16 * kk + 8 * h) : z;
     }
   }
+  // retire the row operand loads here, where the compiler sees it: its wait tracking does not
+  // see the DMA waits below and would otherwise wait for every load in flight inside the loop
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   float m = -INFINITY, m2 = -INFINITY, lrest = 0.f;
   int jst = -1;
   f32x16 o[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  for (int db = 0; db < NDB; ++db) {
+    o[db] = f32x16{};
+  }
+  // value row of the running argmax (fp16), the lane's dims 32db + 8qq + 4h + {0..3}
+  f16x4 vs[NDB][4];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      vs[db][qq] = f16x4{};
+    }
 
   const __bf16* kb0 = k + l * p.ksl + g * p.ksh + p.cu[s] * p.kst;
   const __bf16* vb0 = v + l * p.vsl + g * p.vsh + p.cu[s] * p.vst;
 
-  // one 64-key sub-tile starting at key t0, LDS rows lb..lb+63
-  auto compute_tile = [&](const int64_t t0, const int lb) {
+  // DMA of tile it into ring buffer it % NBUF. Wave instruction f (of NLD * NWAVES) fills
+  // the 64 chunk positions 64(f % IPT) .. +63 of tensor f / IPT: position (row r, c')
+  // takes chunk c' ^ swz(r) of row r. Keys past the chunk load its last row (in bounds,
+  // unconditional); the tile that holds them is masked.
+  constexpr int TBYTES = KT * D * 2;  // bytes per tensor tile
+  const unsigned smb = lds_offset(&sm.tile[0][0][0]);
+  auto issue = [&](int it) __attribute__((always_inline)) {
+    const int64_t t0 = c0 + (int64_t)it * KT;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int f = i * NWAVES + wave;
+      const int tensor = f / IPT, slot = (f % IPT) * 64 + lane;
+      const int r = slot / CPK;
+      const int c = (slot % CPK) ^ (tensor == 0 ? swz_k<D>(r) : swz_v<D>(r));
+      const int rr = (t0 + r < c1) ? r : (int)(c1 - 1 - t0);  // rows past the chunk load its last
+      const __bf16* base = tensor == 0 ? kb0 + t0 * kst : vb0 + t0 * vst;
+      lds_dma16(base, (unsigned)(rr * (int)(tensor == 0 ? kst : vst) + 8 * c) * 2u,
+                smb + (unsigned)(((it % NBUF) * 2 + tensor) * TBYTES + (f % IPT) * 1024));
+    }
+  };
+  // the same for a tile inside the chunk, from lane byte offsets (from the tile's first row)
+  // computed once
+  unsigned doff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int f = i * NWAVES + wave;
+    const int tensor = f / IPT, slot = (f % IPT) * 64 + lane;
+    const int r = slot / CPK;
+    const int c = (slot % CPK) ^ (tensor == 0 ? swz_k<D>(r) : swz_v<D>(r));
+    doff[i] = (unsigned)(r * (int)(tensor == 0 ? kst : vst) + 8 * c) * 2u;
+  }
+  auto issue_full = [&](int it) __attribute__((always_inline)) {
+    const int64_t t0 = c0 + (int64_t)it * KT;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int f = i * NWAVES + wave;
+      const __bf16* base = (f / IPT) == 0 ? kb0 + t0 * kst : vb0 + t0 * vst;
+      lds_dma16(base, doff[i], smb + (unsigned)(((it % NBUF) * 2 + f / IPT) * TBYTES + (f % IPT) * 1024));
+    }
+  };
+  // V of tile it from bf16 to fp16, in place: each lane converts the chunks its own DMA
+  // instructions wrote, so it needs only its own loads to have landed
+  auto convert_own = [&](int it) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int f = i * NWAVES + wave;
+      if (f / IPT == 1) {
+        u32x4* c = (u32x4*)&sm.tile[it % NBUF][1][((f % IPT) * 64 + lane) * 8];
+        *c = bf16x8_to_f16x8(*c);
+      }
+    }
+  };
+  auto issue_any = [&](int it) __attribute__((always_inline)) {
+    if (c0 + (int64_t)(it + 1) * KT <= c1) issue_full(it);
+    else issue(it);
+  };
+  // instruction i of this wave's share of tile it, alone
+  auto issue_one = [&](int it, auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
+    const int f = i * NWAVES + wave;
+    const int tensor = f / IPT;
+    const int64_t t0 = c0 + (int64_t)it * KT;
+    const unsigned dst = smb + (unsigned)(((it % NBUF) * 2 + tensor) * TBYTES + (f % IPT) * 1024);
+    const __bf16* base = tensor == 0 ? kb0 + t0 * kst : vb0 + t0 * vst;
+    if (t0 + KT <= c1) {
+      lds_dma16(base, doff[i], dst);
+    } else {
+      const int slot = (f % IPT) * 64 + lane;
+      const int r = slot / CPK;
+      const int c = (slot % CPK) ^ (tensor == 0 ? swz_k<D>(r) : swz_v<D>(r));
+      const int rr = (t0 + r < c1) ? r : (int)(c1 - 1 - t0);
+      lds_dma16(base, (unsigned)(rr * (int)(tensor == 0 ? kst : vst) + 8 * c) * 2u, dst);
+    }
+  };
+  // byte offset of the lane's K operand chunk (key l32, slots 16kk + 8h .. +7)
+  const int kbase = l32 * RS, khs = h ^ swz_k<D>(l32);
+  auto koff = [&](int kk) __attribute__((always_inline)) { return kbase + (((2 * kk) ^ khs) << 4); };
+  // V^T operand reads: lane reads 4 dims at key row 16ks + 4h + (lane%16)/4 (+8 for the
+  // second half), dims 32db + 16((lane/16)%2) + 4(lane%4). Those rows share their low two
+  // bits, so their swizzle is one lane constant that only permutes the 64-byte d blocks
+  // (bits 2-3 of the chunk index): block db sits at lane base vtd[db], and ks, the second
+  // half and the ring slot are constant offsets.
+  int vtd[NDB];
+  {
+    const int r = 4 * h + ((lane & 15) >> 2);
+    const int x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within the 64-byte block
+    const int sw = swz_v<D>(r) >> 2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vtd[db] = r * RS + ((4 * (db ^ sw) + x) << 4) + ((lane & 1) << 3);
+  }
+  // byte offset of element (key r, dim d), d a multiple of 4, in a V tile
+  auto voff = [&](int r, int d) __attribute__((always_inline)) {
+    return r * RS + ((((d >> 3) ^ swz_v<D>(r))) << 4) + ((d & 4) << 1);
+  };
+
+  // the 64 keys of ring tile it
+  auto compute_tile = [&](const int it, auto&& hook) __attribute__((always_inline)) {
+    const int64_t t0 = c0 + (int64_t)it * KT;
+    const char* kt = (const char*)sm.tile[it % NBUF][0];
+    const char* vt = (const char*)sm.tile[it % NBUF][1];
     // ---- S^T = K Q^T for both 32-key blocks (chains interleaved): lane holds row l32 and,
     // at element r of block kb, key 32kb + 8(r/4) + 4h + (r%4). Values stay raw q.k; the
     // softmax scale enters through one FMA in front of exp2.
+    // operands one k-step ahead of their MFMAs (the scheduling barriers keep the compiler
+    // from loading all of them up front, which would cost 64 registers)
     f32x16 acc0 = {}, acc1 = {};
+    bf16x8 k0 = *(const bf16x8*)(kt + koff(0));
+    bf16x8 k1 = *(const bf16x8*)(kt + 32 * RS + koff(0));
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const bf16x8 k0 = *(const bf16x8*)&sm.k[lb + l32][16 * kk + 8 * h];
-      const bf16x8 k1 = *(const bf16x8*)&sm.k[lb + 32 + l32][16 * kk + 8 * h];
+      bf16x8 k0n = k0, k1n = k1;
+      if (kk + 1 < NKK) {
+        k0n = *(const bf16x8*)(kt + koff(kk + 1));
+        k1n = *(const bf16x8*)(kt + 32 * RS + koff(kk + 1));
+      }
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], acc1, 0, 0, 0);
+      if (kk == 0) hook(std::integral_constant<int, 0>{});
+      if (kk == NKK / 2) hook(std::integral_constant<int, 1>{});
+      __builtin_amdgcn_sched_barrier(0);
+      k0 = k0n;
+      k1 = k1n;
     }
+    hook(std::integral_constant<int, 2>{});
     float tv[32];  // element e = 16*kb + r
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -125,7 +285,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       tv[16 + r] = acc1[r];
     }
     const int trel = (int)(t0 - c0);  // tile start relative to the chunk
-    if ((t0 + KT - 1 > n - p.W) || (t0 + KT > c1)) {
+    if ((t0 + KT - 1 > n - W) || (t0 + KT > c1)) {
       const int lim = (int)((tlim < c1 - 1 ? tlim : c1 - 1) - c0);  // last key this row may use, chunk-relative
 #pragma unroll
       for (int e = 0; e < 32; ++e)
@@ -136,21 +296,27 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
     for (int e = 1; e < 32; ++e) lm = fmaxf(lm, tv[e]);
     const float mt = fmaxf(lm, wave_shfl_xor_f(lm, 32));
 
-    // Row state (raw q.k units): m = running max (key jst, value row in vstar), m2 = running
-    // max over every other key; the rest sums lrest / o are kept relative to m2, so a
-    // dominant key never pushes the rest out of fp16's range.
+    // Row state (raw q.k units): m = running max (key jst, value row in vs); m2 = the
+    // reference of the rest sums lrest / o, within kSlack log2 units of the running max
+    // over every other key (never below it by more, never above it), so a dominant key
+    // never pushes the rest out of fp16's range and a rescale is needed only when the rest's
+    // max climbs past the slack.
     const bool moved = mt > m;
     const bool any_moved = __any(moved);
     int jr = -1;          // this lane's element index of the new argmax, if it holds it
     int jt = 0x7fffffff;  // chunk-relative key of the new argmax
-    float m2n;
+    float cand = mt;      // max over the keys that join the rest in this tile
     if (any_moved) {
+      // an opaque copy of the tile max keeps the search below inside this (rarely taken)
+      // branch instead of being hoisted onto every tile
+      float mtv = mt;
+      asm volatile("" : "+v"(mtv));
       int jl = 64;
       float hi2 = -INFINITY, lo2 = -INFINITY;
       if (moved) {
         // elements run in key order within a lane: the first equal to mt is the lane's lowest key
 #pragma unroll
-        for (int e = 31; e >= 0; --e) jl = (tv[e] == mt) ? e : jl;
+        for (int e = 31; e >= 0; --e) jl = (tv[e] == mtv) ? e : jl;
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
           lo2 = __builtin_amdgcn_fmed3f(lo2, hi2, tv[e]);
@@ -163,53 +329,44 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       // tile max without the new argmax: the lane holding it contributes its second largest
       const float mt2l = moved ? ((jr >= 0) ? lo2 : hi2) : -INFINITY;
       const float mt2 = fmaxf(mt2l, wave_shfl_xor_f(mt2l, 32));
-      m2n = moved ? fmaxf(m, mt2) : fmaxf(m2, mt);  // the old max joins the rest when it moves
-    } else {
-      m2n = fmaxf(m2, mt);
+      if (moved) cand = fmaxf(m, mt2);  // the old max joins the rest when it moves
+      // the new argmax stays out of P: its logit becomes -inf (p = 0) in the lane holding it
+#pragma unroll
+      for (int e = 0; e < 32; ++e) tv[e] = (e == jr) ? -INFINITY : tv[e];
     }
-    const float mb = ((m2n == -INFINITY) ? 0.f : m2n * p.c1) - kPScaleLog2;
-
-    float pr[32];  // 2^14 * exp2(c1 * (s - m2n)); the new argmax excluded
+    const bool upd = cand * c1s > m2 * c1s + kSlack;  // -inf references always move
+    const float m2n = upd ? cand : m2;
+    const bool fold = moved && jst >= 0;  // the previous argmax joins the rest
+    if (__any(upd) || any_moved) {
+      // o = alpha o + wold v*: the rescale to the new reference and the old argmax's value
+      // row with weight exp2(c1 (m - m2n)) (2^14 scaled), in one pass over the accumulators
+      const float alpha = upd ? ((m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m2 - m2n) * c1s)) : 1.f;
+      const float wold = fold ? kPScale * __builtin_amdgcn_exp2f((m - m2n) * c1s) : 0.f;
+      lrest = fmaf(lrest, alpha, wold);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(tv[e], p.c1, -mb));
-    if (jr >= 0) {
+      for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int e = 0; e < 32; ++e) pr[e] = (e == jr) ? 0.f : pr[e];
-    }
-    // rescale the rest to the new m2
-    if (__any(m2n > m2)) {
-      const float alpha = (m2n > m2) ? ((m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m2 - m2n) * p.c1)) : 1.f;
-      lrest *= alpha;
+        for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
-    if (any_moved && moved) {
-      // the previous argmax joins the rest with weight exp2(c1 (m - m2n)) <= 1 (2^14 scaled)
-      if (jst >= 0) {
-        const float wold = kPScale * __builtin_amdgcn_exp2f((m - m2n) * p.c1);
-        lrest += wold;
+          for (int e = 0; e < 4; ++e) o[db][4 * qq + e] = fmaf(o[db][4 * qq + e], alpha, wold * (float)vs[db][qq][e]);
+      }
+      if (moved) {
+        const int jslot = jt - trel;  // new argmax's key in this tile
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
-            const f16x4 vs = *(const f16x4*)&sm.vstar[row_t][32 * db + 8 * qq + 4 * h];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[db][4 * qq + e] += wold * (float)vs[e];
+            vs[db][qq] = *(const f16x4*)(vt + voff(jslot, 32 * db + 8 * qq + 4 * h));
           }
+        jst = (int)c0 + jt;
+        m = mt;
       }
-      const int jslot = jt - trel;  // new argmax's key in this tile
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-          *(f16x4*)&sm.vstar[row_t][32 * db + 8 * qq + 4 * h] =
-              *(const f16x4*)&sm.v[lb + jslot][32 * db + 8 * qq + 4 * h];
-      jst = (int)c0 + jt;
-      m = mt;
     }
     m2 = m2n;
+    const float mb = ((m2n == -INFINITY) ? 0.f : m2n * c1s) - kPScaleLog2;
+    float pr[32];  // 2^14 * exp2(c1 * (s - m2n)) <= 2^(14 + kSlack); the new argmax excluded
+#pragma unroll
+    for (int e = 0; e < 32; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(tv[e], c1s, -mb));
 
     // ---- O^T += V^T P^T, 16 keys per k-step. B = P^T: lane (row, h) slots 8h..8h+7 =
     // its elements 8ks..8ks+7, i.e. keys 16ks+4h+{0..3} and 16ks+8+4h+{0..3}. lrest sums the
@@ -223,13 +380,10 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       for (int e = 0; e < 8; ++e) pf[e] = (_Float16)pr[8 * ks + e];
 #pragma unroll
       for (int e = 0; e < 4; ++e) ts = __builtin_amdgcn_fdot2(f16x2{pf[2 * e], pf[2 * e + 1]}, ones, ts, false);
-      const int kbase = lb + 16 * ks + 4 * h;  // first key of this lane-half's two 4-key runs
-      const int sidx = lane & 15;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int d0 = 32 * db + 16 * ((lane >> 4) & 1);
-        const _Float16* a0 = &sm.v[kbase + (sidx >> 2)][d0 + 4 * (sidx & 3)];
-        const _Float16* a1 = &sm.v[kbase + 8 + (sidx >> 2)][d0 + 4 * (sidx & 3)];
+        const char* a0 = vt + vtd[db] + 16 * ks * RS;
+        const char* a1 = a0 + 8 * RS;
         const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a0);
         const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a1);
         // whole-vector casts: per-element bit casts of the loaded i16x4 were lowered to a
@@ -238,44 +392,54 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
                                                  2, 3, 4, 5, 6, 7);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[db], 0, 0, 0);
       }
+      if (ks == 1) hook(std::integral_constant<int, 3>{});
+      if (ks == 3) hook(std::integral_constant<int, 4>{});
     }
     lrest += ts + wave_shfl_xor_f(ts, 32);
   };
 
-
-  // K/V staging: the next LDS tile is loaded into registers while this one is computed.
-  // Keys past the chunk load the chunk's last row (in bounds; the loads stay unconditional);
-  // they are masked in the sub-tile that holds them.
-  u32x4 kst[NST], vst[NST];
-#pragma unroll
-  for (int i = 0; i < NST; ++i) {
-    const int c = tid + NTHREADS * i, key = c / CPR, part = c % CPR;
-    const int64_t j = (c0 + key < c1) ? c0 + key : c1 - 1;
-    kst[i] = *(const u32x4*)(kb0 + j * p.kst + part * 8);
-    vst[i] = *(const u32x4*)(vb0 + j * p.vst + part * 8);
-  }
-  for (int64_t t0 = c0; t0 < c1; t0 += KL) {
-    __syncthreads();  // all waves are done with the previous tile
-#pragma unroll
-    for (int i = 0; i < NST; ++i) {
-      const int c = tid + NTHREADS * i, key = c / CPR, part = c % CPR;
-      *(u32x4*)&sm.k[key][part * 8] = kst[i];
-      *(u32x4*)&sm.v[key][part * 8] = bf16x8_to_f16x8(vst[i]);
-    }
+  // Ring schedule (one barrier per tile). Iteration t: after the barrier, buffer (t+3)%4
+  // (last read by tile t-1) takes tile t+3, tile t is computed, and each lane waits for its
+  // own loads of tile t+1 (tiles t+2 and the part of t+3 issued so far stay in flight) and
+  // converts its share of that tile's V, which the next barrier publishes. Three tiles are
+  // in flight while one is computed. A computing wave spreads its DMA instructions over
+  // the tile's MFMA phases (half with the S^T chain, half with the O^T chain) and converts
+  // between them: issued all at once by every wave they back up in the address unit.
+  constexpr int NS = NLD / 2;  // instructions of tile t+3 issued before the wait for t+1
+  issue(0);
+  if (ntiles > 1) issue_any(1);
+  if (ntiles > 2) issue_any(2);
+  if (ntiles > 2) vm_wait<2 * NLD>();
+  else if (ntiles > 1) vm_wait<NLD>();
+  else vm_wait<0>();
+  convert_own(0);
+  for (int t = 0; t < ntiles; ++t) {
     __syncthreads();
-    if (t0 + KL < c1) {
-#pragma unroll
-      for (int i = 0; i < NST; ++i) {
-        const int c = tid + NTHREADS * i, key = c / CPR, part = c % CPR;
-        const int64_t j = (t0 + KL + key < c1) ? t0 + KL + key : c1 - 1;
-        kst[i] = *(const u32x4*)(kb0 + j * p.kst + part * 8);
-        vst[i] = *(const u32x4*)(vb0 + j * p.vst + part * 8);
-      }
-    }
+    const bool more3 = t + 3 < ntiles, more2 = t + 2 < ntiles, more1 = t + 1 < ntiles;
+    auto wait_convert_next = [&](auto later3) __attribute__((always_inline)) {
+      if (!more1) return;
+      if (more3) vm_wait<NLD + decltype(later3)::value>();
+      else if (more2) vm_wait<NLD>();
+      else vm_wait<0>();
+      convert_own(t + 1);
+    };
     if (computing) {
-#pragma unroll
-      for (int sub = 0; sub < KL / KT; ++sub)
-        if (t0 + sub * KT < c1) compute_tile(t0 + sub * KT, sub * KT);
+      compute_tile(t, [&](auto pc) __attribute__((always_inline)) {
+        constexpr int point = decltype(pc)::value;  // 0, 1: S^T chain; 2: after it; 3, 4: O^T chain
+        if constexpr (point == 2) {
+          wait_convert_next(std::integral_constant<int, NS>{});
+        } else if (more3) {
+          if constexpr (NLD == 4) {
+            constexpr int i = point < 2 ? point : point - 1;
+            issue_one(t + 3, std::integral_constant<int, i>{});
+          } else if constexpr (point == 0 || point == 3) {
+            issue_one(t + 3, std::integral_constant<int, point == 0 ? 0 : 1>{});
+          }
+        }
+      });
+    } else {
+      if (more3) issue_any(t + 3);
+      wait_convert_next(std::integral_constant<int, NLD>{});
     }
   }
 
@@ -294,12 +458,11 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       float4 w4 = {o[db][4 * qq] * kPUnscale, o[db][4 * qq + 1] * kPUnscale, o[db][4 * qq + 2] * kPUnscale,
                    o[db][4 * qq + 3] * kPUnscale};
       *(float4*)&Ob[(size_t)row_t * D + 32 * db + 8 * qq + 4 * h] = w4;
-      *(f16x4*)&Vb[(size_t)row_t * D + 32 * db + 8 * qq + 4 * h] =
-          *(const f16x4*)&sm.vstar[row_t][32 * db + 8 * qq + 4 * h];
+      *(f16x4*)&Vb[(size_t)row_t * D + 32 * db + 8 * qq + 4 * h] = vs[db][qq];
     }
   if (h == 0) {
-    Mb[row_t] = m * p.c1;  // log2 units from here on
-    M2b[row_t] = m2 * p.c1;
+    Mb[row_t] = m * c1s;  // log2 units from here on
+    M2b[row_t] = m2 * c1s;
     Lb[row_t] = lrest * kPUnscale;
     Jb[row_t] = jst;
   }

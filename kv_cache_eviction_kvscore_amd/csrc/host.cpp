@@ -69,6 +69,9 @@ int make_dev(const kvscore_problem* p, kvs::Dev& d) {
       return fail(KVSCORE_EINVAL, "k/v strides must be non-negative multiples of 8 elements (16 bytes)");
   if (p->k_strides[2] < p->head_dim || p->v_strides[2] < p->head_dim)
     return fail(KVSCORE_EINVAL, "token stride smaller than head_dim");
+  // the kernels address a 64-token tile from its first row with 32-bit byte offsets
+  if (p->k_strides[2] >= ((int64_t)1 << 22) || p->v_strides[2] >= ((int64_t)1 << 22))
+    return fail(KVSCORE_EINVAL, "token stride must be below 2^22 elements");
 
   d = kvs::Dev{};
   d.S = p->num_seqs;

@@ -18,6 +18,25 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane L
+// reads base + off (off: its byte offset, base: the same for every lane, held in SGPRs) and
+// writes LDS bytes [lds + 16 L, lds + 16 L + 16); lds (a byte offset in LDS) must be the same
+// for every lane. Issued from inline asm so that the compiler does not treat it as an LDS
+// store: it would otherwise drain every load in flight (s_waitcnt vmcnt(0)) before each LDS
+// read it cannot prove disjoint. The caller orders it with explicit vmcnt waits and a barrier.
+__device__ inline void lds_dma16(const void* base, unsigned off, unsigned lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+// byte offset in LDS of a __shared__ object (a flat address in the LDS aperture carries the
+// offset in its low 32 bits)
+__device__ inline unsigned lds_offset(const void* p) { return (unsigned)(size_t)p; }
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
+// global stores or loads in flight (__syncthreads' release fence waits for all of them)
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 constexpr int kMaxSeqs = 64;
 constexpr int kRowsPerTileMax = 256;  // query rows one workgroup holds (8 waves x 32 rows)
 constexpr int kMergeChunk = 4096;     // tokens per merge workgroup

@@ -73,11 +73,6 @@ struct BlockAcc {
   f32x16 S, X;
 };
 
-__device__ inline void dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
-}
-
 // x as three bf16 parts (hi, mid, lo) whose sum is x to about 24 bits
 struct Split3 {
   __bf16 hi, mid, lo;
@@ -149,7 +144,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   const int64_t c1 = (n < c0 + p.score_chunk) ? n : c0 + p.score_chunk;
   const int ntiles = (int)((c1 - c0 + KT - 1) / KT);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int wrow0 = wave * 32;  // first tile row of this wave
   const bool computing = wrow0 < p.RT;
   const int64_t rbase = (int64_t)u * p.R + (int64_t)qt * p.RT;  // first row of this tile (global row index)
@@ -168,6 +164,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   // the 64 chunk slots 64(f % IPT) .. +63 of tensor f / IPT: slot (row r, position c')
   // takes chunk c' ^ swz(r) of key row r. Keys past the chunk load its last row (in
   // bounds, unconditional); their columns are masked and never written.
+  constexpr int TBYTES = KT * D * 2;  // bytes per tensor tile
+  const unsigned smb = lds_offset(&sm.tile[0][0][0]);
   auto issue = [&](int it) __attribute__((always_inline)) {
     const int64_t t0 = c0 + (int64_t)it * KT;
 #pragma unroll
@@ -175,21 +173,20 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       const int f = i * NWAVES + wave;
       const int tensor = f / IPT, slot = (f % IPT) * 64 + lane;
       const int r = slot / CPK, c = (slot % CPK) ^ swz<D>(r);
-      const int64_t j0 = t0 + r;
-      const int64_t j = j0 < c1 ? j0 : c1 - 1;
-      const __bf16* src = tensor == 0 ? kb0 + j * kst : vb0 + j * vst;
-      dma16(src + 8 * c, &sm.tile[it % NBUF][tensor][(f % IPT) * 64 * 8]);
+      const int rr = (t0 + r < c1) ? r : (int)(c1 - 1 - t0);  // rows past the chunk load its last
+      const __bf16* base = tensor == 0 ? kb0 + t0 * kst : vb0 + t0 * vst;
+      lds_dma16(base, (unsigned)(rr * (int)(tensor == 0 ? kst : vst) + 8 * c) * 2u,
+                smb + (unsigned)(((it % NBUF) * 2 + tensor) * TBYTES + (f % IPT) * 1024));
     }
   };
-  // the same for a full tile, from lane offsets (elements from the tile's first row)
-  // computed once
-  int doff[NLD];
+  // the same for a full tile, from lane byte offsets (from the tile's first row) computed once
+  unsigned doff[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int f = i * NWAVES + wave;
     const int tensor = f / IPT, slot = (f % IPT) * 64 + lane;
     const int r = slot / CPK, c = (slot % CPK) ^ swz<D>(r);
-    doff[i] = r * (int)(tensor == 0 ? kst : vst) + 8 * c;
+    doff[i] = (unsigned)(r * (int)(tensor == 0 ? kst : vst) + 8 * c) * 2u;
   }
   auto issue_full = [&](int it) __attribute__((always_inline)) {
     const int64_t t0 = c0 + (int64_t)it * KT;
@@ -198,7 +195,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       const int f = i * NWAVES + wave;
       const int tensor = f / IPT;
       const __bf16* base = tensor == 0 ? kb0 + t0 * kst : vb0 + t0 * vst;
-      dma16(base + doff[i], &sm.tile[it % NBUF][tensor][(f % IPT) * 64 * 8]);
+      lds_dma16(base, doff[i], smb + (unsigned)(((it % NBUF) * 2 + tensor) * TBYTES + (f % IPT) * 1024));
     }
   };
   // -||v||^2/2 of tile it (landed, visible), into nvx[it & 1]: wave w sums keys
@@ -421,7 +418,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    __syncthreads();
+    lds_barrier();  // the column stores of earlier tiles stay in flight
     auto side = [&]() __attribute__((always_inline)) {
       if (t >= 1) flush_share(t - 1);
       if (t + 3 < ntiles) {
