@@ -21,9 +21,13 @@ Parts and the passages they follow:
   ("delete the k smallest"), and always keep the most recent w tokens.
 * :func:`gather` -- RippleKV page, Eq. 4: the compressed cache is the (k, v)
   pairs at the retained positions.
+* :func:`decode_attention` -- decoding on that compressed cache (RippleKV Eq. 4; GraceKV
+  page, physical cache packing: one ragged cache per (layer, KV head)): plain softmax
+  attention of each new query head over its KV head's segment.
 
 Parity pins: see ``tests/test_oracle_pins.py`` (brute-force single-token removal,
-closed forms, invariants) and ``tests/test_budget_oracle.py``.
+closed forms, invariants), ``tests/test_budget_oracle.py``, ``tests/test_pool_oracle.py``
+and ``tests/test_decode_oracle.py``.
 """
 from __future__ import annotations
 
@@ -289,3 +293,55 @@ def gather(k_seg, v_seg, positions):
         ko[r] = k_seg[p]
         vo[r] = v_seg[p]
     return ko, vo
+
+
+# --------------------------------------------------------------------------- decode
+def _bf16_f64(bits):
+    """bf16 bit patterns (uint16) as fp64 values (exact)."""
+    b = np.ascontiguousarray(bits).view(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def decode_attention(q, k_cache, v_cache, offsets, *, num_layers, num_seqs, num_q_heads, num_kv_heads,
+                     scale=None):
+    """Decode attention over the packed ragged cache, in fp64.
+
+    RippleKV page, "Problem Formulation" Eq. 4: decoding continues on the compressed
+    cache, the (k, v) pairs at each layer's retained positions; GraceKV page, physical
+    cache packing: every (layer, KV head) has a cache of its own length. Segment
+    u = (l*S + s)*Hkv + g is rows offsets[u] .. offsets[u+1]-1 of k_cache / v_cache.
+    Query head h = g*G + hl of (layer l, sequence s) attends to every row of its KV
+    head's segment (all of them precede the new token):
+    out = softmax(scale * K q) V, lse = log sum_j exp(scale * k_j . q).
+
+    q: uint16 bf16 bits [L][S][Hq][d]; k_cache, v_cache: uint16 bf16 bits [rows][d];
+    offsets: int64 [U+1]. Returns (out [L][S][Hq][d], lse [L][S][Hq]) in fp64.
+    """
+    L, S, Hq, Hkv = num_layers, num_seqs, num_q_heads, num_kv_heads
+    G = Hq // Hkv
+    qf = _bf16_f64(q).reshape(L, S, Hq, -1)
+    d = qf.shape[-1]
+    kf = _bf16_f64(k_cache).reshape(-1, d)
+    vf = _bf16_f64(v_cache).reshape(-1, d)
+    off = np.asarray(offsets, dtype=np.int64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.empty((L, S, Hq, d))
+    lse = np.empty((L, S, Hq))
+    for l in range(L):
+        for s in range(S):
+            for g in range(Hkv):
+                u = (l * S + s) * Hkv + g
+                K = kf[off[u]:off[u + 1]]
+                V = vf[off[u]:off[u + 1]]
+                if len(K) == 0:
+                    raise ValueError("empty segment")
+                for hl in range(G):
+                    h = g * G + hl
+                    logits = scale * (K @ qf[l, s, h])
+                    m = logits.max()
+                    w = np.exp(logits - m)
+                    tot = w.sum()
+                    out[l, s, h] = (w @ V) / tot
+                    lse[l, s, h] = m + math.log(tot)
+    return out, lse
