@@ -17,6 +17,7 @@
  *                      max-pooled key, optionally pinning sinks) plus the W most
  *                      recent tokens, as ascending positions in a packed array.
  *   kvscore_compact    gathers the kept K and V rows into a packed ragged cache.
+ *   kvscore_decode_attn  decode attention of new query tokens over that cache.
  *
  * Sources (the web pages this library implements):
  *   DropKV: Decoupling Residual-Output Perturbation for Near-Optimal KV-Cache Eviction
@@ -224,6 +225,33 @@ int kvscore_topk(const kvscore_problem* p, const float* score, const int32_t* bu
 int kvscore_compact(const kvscore_problem* p, const void* k, const void* v, const int32_t* budgets,
                     const int64_t* seg_offsets, const int32_t* kept_pos, void* k_out, void* v_out,
                     void* stream);
+
+/*
+ * Decode attention over the packed ragged cache (RippleKV page, "Problem Formulation":
+ * during decoding every new query attends to the cached states, the retained pairs of
+ * Eq. 4 after compression; GraceKV page, physical cache packing: one cache of its own
+ * length per (layer, KV head)). For layer l, sequence s and query head h = g*G + hl, with
+ * segment u = (l*S + s)*Hkv + g = rows off[u] .. off[u+1]-1 of the cache:
+ *   out[l][s][h] = sum_r softmax_r(scale * k_r . q[l][s][h]) v_r,
+ *   lse[l][s][h] = log sum_r exp(scale * k_r . q[l][s][h]).
+ * Every row of a segment takes part (they all precede the new token; to attend to
+ * appended tokens, lay them out inside the segments). Only num_seqs, num_layers,
+ * num_q_heads, num_kv_heads (G = Hq/Hkv <= 8), head_dim (64 or 128) and softmax_scale of
+ * p are used.
+ *   q: device bf16 [L][S][Hq][d] contiguous, 16-byte aligned.
+ *   k_cache, v_cache: device bf16 [off[U]][d], 16-byte aligned (kvscore_compact's
+ *     k_out / v_out, or any cache laid out the same way).
+ *   seg_offsets_host: HOST int64 [U+1], off[0] = 0, every segment non-empty (validated;
+ *     sizes the launch). seg_offsets: its DEVICE copy.
+ *   out: device fp32 [L][S][Hq][d]; lse: device fp32 [L][S][Hq] (natural log).
+ *   workspace: device, kvscore_decode_workspace_size(p, seg_offsets_host) bytes.
+ * Deterministic: the key splits and every partial sum are merged in a fixed order.
+ * Errors: KVSCORE_EINVAL (shape, offsets, pointer or alignment), KVSCORE_EWORKSPACE.
+ */
+size_t kvscore_decode_workspace_size(const kvscore_problem* p, const int64_t* seg_offsets_host);
+int kvscore_decode_attn(const kvscore_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                        const int64_t* seg_offsets_host, const int64_t* seg_offsets, float* out, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

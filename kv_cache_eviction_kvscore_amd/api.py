@@ -55,7 +55,7 @@ EXPORTS = (
     "kvscore_version", "kvscore_last_error", "kvscore_num_query_tiles", "kvscore_workspace_size",
     "kvscore_attn_fwd", "kvscore_score", "kvscore_merge", "kvscore_budget", "kvscore_budget_pyramid",
     "kvscore_segment_offsets",
-    "kvscore_topk", "kvscore_compact",
+    "kvscore_topk", "kvscore_compact", "kvscore_decode_workspace_size", "kvscore_decode_attn",
 )
 
 _lib = None
@@ -84,6 +84,8 @@ def load():
         "kvscore_segment_offsets": (ctypes.c_int, [P, vp, vp]),
         "kvscore_topk": (ctypes.c_int, [P, vp, vp, vp, vp, i32, i32, vp, sz, vp]),
         "kvscore_compact": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "kvscore_decode_workspace_size": (sz, [P, vp]),
+        "kvscore_decode_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -276,3 +278,39 @@ def compact(p: Problem, k, v, budgets: np.ndarray, seg_off_dev, kept, k_out, v_o
     _need(v_out, R * p.head_dim, torch.bfloat16, "v_out")
     _check(load().kvscore_compact(p.ref, _ptr(k), _ptr(v), ctypes.c_void_p(b.ctypes.data), _ptr(seg_off_dev),
                                   _ptr(kept), _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+def _host_offsets(seg_off_host, units: int) -> np.ndarray:
+    off = np.ascontiguousarray(np.asarray(seg_off_host, dtype=np.int64))
+    if off.shape != (units + 1,):
+        raise ValueError(f"segment offsets: expected {units + 1} entries, got {off.shape}")
+    return off
+
+
+def decode_workspace_size(p: Problem, seg_off_host) -> int:
+    """Bytes of workspace :func:`decode_attn` needs for these segments (0 and an error on bad input)."""
+    off = _host_offsets(seg_off_host, p.units)
+    return int(load().kvscore_decode_workspace_size(p.ref, ctypes.c_void_p(off.ctypes.data)))
+
+
+def decode_attn(p: Problem, q, k_cache, v_cache, seg_off_host, seg_off_dev, out, lse, ws, stream=None):
+    """Decode attention over the packed ragged cache: q bf16 [L][S][Hq][d]; k_cache, v_cache
+    bf16 [rows][d]; segment offsets as a host array and its device copy (int64 [U+1]);
+    out fp32 [L][S][Hq][d], lse fp32 [L][S][Hq]; ws: uint8 of decode_workspace_size bytes."""
+    off = _host_offsets(seg_off_host, p.units)
+    nbytes = decode_workspace_size(p, off)
+    if nbytes == 0:  # the offsets or the shape failed validation; the message names the problem
+        _check(EINVAL)
+    rows = int(off[-1])
+    nq = p.num_layers * p.num_seqs * p.num_q_heads
+    _need(q, nq * p.head_dim, torch.bfloat16, "q")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [L][S][Hq][d]")
+    _need(k_cache, rows * p.head_dim, torch.bfloat16, "k_cache")
+    _need(v_cache, rows * p.head_dim, torch.bfloat16, "v_cache")
+    _need(seg_off_dev, p.units + 1, torch.int64, "seg_offsets")
+    _need(out, nq * p.head_dim, torch.float32, "out")
+    _need(lse, nq, torch.float32, "lse")
+    _need(ws, nbytes, torch.uint8, "workspace")
+    _check(load().kvscore_decode_attn(p.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.c_void_p(off.ctypes.data),
+                                      _ptr(seg_off_dev), _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream(stream)))

@@ -187,12 +187,52 @@ int round_to_total(const std::vector<double>& x, int64_t total, int32_t lo, int3
   return ok();
 }
 
+// Decode attention problem: the model shape of p and the packed segment offsets (host
+// copy). Only the shape fields, head_dim and softmax_scale of p are used.
+int make_decdev(const kvscore_problem* p, const int64_t* off, kvs::DecDev& d) {
+  if (!p) return fail(KVSCORE_EINVAL, "problem is NULL");
+  if (p->num_seqs < 1 || p->num_seqs > KVSCORE_MAX_SEQS) return fail(KVSCORE_EINVAL, "num_seqs out of range");
+  if (p->num_layers < 1 || p->num_kv_heads < 1 || p->num_q_heads < 1)
+    return fail(KVSCORE_EINVAL, "layers and heads must be positive");
+  if (p->num_q_heads % p->num_kv_heads) return fail(KVSCORE_EINVAL, "num_q_heads not a multiple of num_kv_heads");
+  const int G = p->num_q_heads / p->num_kv_heads;
+  if (G > kvs::kDecodeMaxGroup) return fail(KVSCORE_EINVAL, "decode takes at most %d query heads per KV head", kvs::kDecodeMaxGroup);
+  if (p->head_dim != 64 && p->head_dim != 128) return fail(KVSCORE_EINVAL, "head_dim must be 64 or 128");
+  if (!off) return fail(KVSCORE_EINVAL, "host segment offsets are NULL");
+  const int64_t U = (int64_t)p->num_layers * p->num_seqs * p->num_kv_heads;
+  if (U > 65535) return fail(KVSCORE_EINVAL, "too many segments (%lld)", (long long)U);
+  if (off[0] != 0) return fail(KVSCORE_EINVAL, "segment offsets must start at 0");
+  int64_t max_len = 0;
+  for (int64_t u = 0; u < U; ++u) {
+    const int64_t len = off[u + 1] - off[u];
+    if (len < 1) return fail(KVSCORE_EINVAL, "segment %lld is empty or offsets decrease", (long long)u);
+    max_len = std::max(max_len, len);
+  }
+  d = kvs::DecDev{};
+  d.Hq = p->num_q_heads;
+  d.Hkv = p->num_kv_heads;
+  d.G = G;
+  d.d = p->head_dim;
+  d.U = (int)U;
+  const float scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  d.c1 = (float)((double)scale * 1.4426950408889634);
+  // about 2048 workgroups in all (8 per CU), at least 256 keys per split
+  int64_t ns = std::max<int64_t>(1, (2048 + U - 1) / U);
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, max_len / 256));
+  const int64_t chunk = ((max_len + ns - 1) / ns + 63) / 64 * 64;
+  if (chunk > (int64_t)1 << 30) return fail(KVSCORE_EINVAL, "segment too long");
+  d.chunk = (int)chunk;
+  d.nsplit = (int)((max_len + chunk - 1) / chunk);
+  return ok();
+}
+
+size_t ws_decode(const kvs::DecDev& d) { return (size_t)d.U * d.nsplit * d.G * (d.d + 2) * sizeof(float); }
 
 }  // namespace
 
 extern "C" {
 
-int32_t kvscore_version(void) { return 101; }
+int32_t kvscore_version(void) { return 102; }
 
 const char* kvscore_last_error(void) { return g_err.c_str(); }
 
@@ -418,6 +458,26 @@ int kvscore_compact(const kvscore_problem* p, const void* k, const void* v, cons
   if (int rc = check_budgets(p, budgets, &max_b)) return rc;
   return launched(kvs::launch_compact(d, k, v, seg_offsets, kept_pos, k_out, v_out, max_b, (hipStream_t)stream),
                   "kvscore_compact");
+}
+
+size_t kvscore_decode_workspace_size(const kvscore_problem* p, const int64_t* seg_offsets_host) {
+  kvs::DecDev d;
+  if (make_decdev(p, seg_offsets_host, d)) return 0;
+  return ws_decode(d);
+}
+
+int kvscore_decode_attn(const kvscore_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                        const int64_t* seg_offsets_host, const int64_t* seg_offsets, float* out, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  kvs::DecDev d;
+  if (int rc = make_decdev(p, seg_offsets_host, d)) return rc;
+  if (!q || !k_cache || !v_cache || !seg_offsets || !out || !lse) return fail(KVSCORE_EINVAL, "NULL tensor argument");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(KVSCORE_EINVAL, "q/k_cache/v_cache not 16-byte aligned");
+  if (!aligned(out, 4) || !aligned(lse, 4)) return fail(KVSCORE_EINVAL, "out/lse not 4-byte aligned");
+  if (int rc = check_ws(workspace, workspace_bytes, ws_decode(d))) return rc;
+  return launched(kvs::launch_decode(d, q, k_cache, v_cache, seg_offsets, out, lse, workspace, (hipStream_t)stream),
+                  "kvscore_decode_attn");
 }
 
 }  // extern "C"

@@ -48,7 +48,7 @@ struct Dev {
   int R;       // rows per unit = G*W
   int Tq;      // query tiles per unit
   int RT;      // rows per query tile (multiple of 32, <= kRowsPerTileMax)
-  int mode;    // 0 = L2, 1 = SQ
+  int mode;    // 0 = L2, 1 = SQ, 2 = attention sum
   float scale; // multiplies q.k
   float c1;    // scale * log2(e)
   int64_t ksl, ksh, kst, vsl, vsh, vst;  // element strides
@@ -60,6 +60,15 @@ struct Dev {
   int score_chunks;                      // max score chunks over sequences
   int64_t max_n;                         // longest sequence
   int64_t cu[kMaxSeqs + 1];
+};
+
+// Decode attention over the packed ragged cache, as its kernels see it.
+struct DecDev {
+  int Hq, Hkv, G, d;
+  int U;       // segments = L*S*Hkv
+  float c1;    // softmax scale * log2(e)
+  int chunk;   // keys per split (multiple of 64)
+  int nsplit;  // splits of the longest segment
 };
 
 // unit u = (l*S + s)*Hkv + g
@@ -85,6 +94,9 @@ hipError_t launch_merge(const Dev& p, const float* partial, const int32_t* jstar
 hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off, int32_t* kept, int pool, int n_sink,
                        float* pooled, hipStream_t st);
 constexpr int kMaxPoolSize = 255;
+constexpr int kDecodeMaxGroup = 8;  // query heads per KV head the decode kernels take
+hipError_t launch_decode(const DecDev& p, const void* q, const void* k, const void* v, const int64_t* off, float* out,
+                         float* lse, void* ws, hipStream_t st);
 hipError_t launch_compact(const Dev& p, const void* k, const void* v, const int64_t* seg_off, const int32_t* kept,
                           void* k_out, void* v_out, int max_budget, hipStream_t st);
 

@@ -204,3 +204,51 @@ def test_pyramid_budget_errors():
         api.budget_pyramid(4, -1.0, 100, 10, 100)
     with pytest.raises(api.KvscoreError):
         api.budget_pyramid(0, 1.0, 100, 10, 100)
+
+
+def _decode_rc(p, off, *, q=0x1000, k=0x1000, v=0x1000, out=0x1000, lse=0x1000, ws_bytes=None):
+    lib = api.load()
+    off = np.ascontiguousarray(np.asarray(off, dtype=np.int64))
+    need = int(lib.kvscore_decode_workspace_size(p.ref, ctypes.c_void_p(off.ctypes.data)))
+    fake = ctypes.c_void_p(0x1000)
+    vp = lambda a: None if a is None else ctypes.c_void_p(a)
+    return lib.kvscore_decode_attn(p.ref, vp(q), vp(k), vp(v), ctypes.c_void_p(off.ctypes.data), fake, vp(out), vp(lse),
+                                   fake, need if ws_bytes is None else ws_bytes, None)
+
+
+def test_decode_workspace_size():
+    p = make_problem()  # L = 2, S = 1, Hkv = 2, G = 4, d = 128: four segments
+    off = np.array([0, 100, 200, 300, 400], dtype=np.int64)
+    # 100 keys per segment: one split per segment; records of (m, l, acc[d]) per query head
+    assert api.decode_workspace_size(p, off) == 4 * 1 * 4 * (128 + 2) * 4
+    long = np.array([0, 100000, 100001, 100002, 100003], dtype=np.int64)
+    ws = api.decode_workspace_size(p, long)
+    assert ws % (4 * 4 * 130 * 4) == 0 and ws > 4 * 4 * 130 * 4  # the long segment is split
+
+
+def test_decode_validation():
+    p = make_problem()
+    good = [0, 10, 20, 30, 40]
+    assert _decode_rc(p, good, ws_bytes=0) == api.EWORKSPACE
+    assert _decode_rc(p, [0, 10, 10, 30, 40]) == api.EINVAL  # empty segment
+    assert "empty" in api.load().kvscore_last_error().decode()
+    assert _decode_rc(p, [0, 10, 5, 30, 40]) == api.EINVAL  # decreasing
+    assert _decode_rc(p, [1, 10, 20, 30, 40]) == api.EINVAL  # must start at 0
+    assert _decode_rc(p, good, q=None) == api.EINVAL
+    assert _decode_rc(p, good, lse=None) == api.EINVAL
+    assert _decode_rc(p, good, k=0x1008) == api.EINVAL  # not 16-byte aligned
+    assert _decode_rc(p, good, out=0x1002) == api.EINVAL
+    assert _decode_rc(make_problem(num_q_heads=18, num_kv_heads=2), good) == api.EINVAL  # G = 9 > 8
+    assert "at most 8" in api.load().kvscore_last_error().decode()
+    assert _decode_rc(make_problem(head_dim=96), good) == api.EINVAL
+    with pytest.raises(api.KvscoreError):
+        api.decode_attn(p, None, None, None, [0, 10, 10, 30, 40], None, None, None, None)
+
+
+def test_token_stride_limit():
+    big = 1 << 22
+    p = make_problem(k_strides=(2 * 100 * big, 100 * big, big))
+    assert p.workspace_size(api.WS_SCORE) == 0
+    assert "2^22" in api.load().kvscore_last_error().decode()
+    p = make_problem(v_strides=(2 * 100 * 128, 100 * 128, big - 8))
+    assert p.workspace_size(api.WS_SCORE) > 0

@@ -19,7 +19,6 @@ import torch
 import oracle
 
 
-
 def bf16_bits(x):
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
     return t.view(torch.int16).numpy().view(np.uint16)
