@@ -29,10 +29,11 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 CALLS = ("attn_fwd", "score", "merge", "topk", "compact")
 # the kernel files whose counters a committed traffic record describes
 KERNEL_SOURCES = {"score": "score.hip", "attn_fwd": "attn_fwd.hip", "compact": "compact.hip",
-                  "topk": "topk.hip", "merge": "merge.hip"}
+                  "topk": "topk.hip", "merge": "merge.hip", "decode": "decode.hip"}
 # the kernels (by name fragment) that make up each call, for counter records
 CALL_KERNELS = {"attn_fwd": ("fwd_partial_kernel", "fwd_combine_kernel"), "score": ("score_prep_kernel", "score_kernel"),
-                "merge": ("merge_kernel",), "topk": ("topk_kernel",), "compact": ("compact_kernel",)}
+                "merge": ("merge_kernel",), "topk": ("topk_kernel",), "compact": ("compact_kernel",),
+                "decode": ("decode_partial_kernel", "decode_combine_kernel")}
 
 
 def bound_of(work: dict) -> str:
@@ -159,6 +160,45 @@ def cpu_baseline(w, data, budgets, target_s: float, max_units: int):
                       f"top-k + gather, {spent:.1f} s; tokens/s = the units' share of the prompt tokens / time"}
 
 
+def time_decode(w, prob, pipe, steps: int) -> dict:
+    """Decode attention of one new token per query head over the packed ragged cache the step
+    just compacted (not part of the step). Algorithmic bytes: every packed K and V row once,
+    the queries, the fp32 outputs and logsumexps."""
+    import numpy as np
+    import torch
+    from kv_cache_eviction_kvscore_amd import api
+    L, S, Hq, d = w.num_layers, w.num_seqs, w.num_q_heads, w.head_dim
+    g = torch.Generator().manual_seed(2024)
+    q = torch.randn((L, S, Hq, d), generator=g).to(torch.bfloat16).cuda()
+    out = torch.empty((L, S, Hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((L, S, Hq), dtype=torch.float32, device="cuda")
+    off = pipe.seg_off_host
+    ws = torch.empty(api.decode_workspace_size(prob, off), dtype=torch.uint8, device="cuda")
+    k_out, v_out = pipe.k_out[:pipe.kept_rows], pipe.v_out[:pipe.kept_rows]
+
+    def run():
+        api.decode_attn(prob, q, k_out, v_out, off, pipe.seg_off, out, lse, ws)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nq = L * S * Hq
+    nbytes = 2 * pipe.kept_rows * d * 2 + nq * d * 2 + nq * (d + 1) * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "cache_rows": pipe.kept_rows, "bytes": nbytes, "gbs": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bound": "hbm",
+            "what": "one new token per query head over the packed ragged cache the step compacted "
+                    "(kvscore_decode_attn, partial + combine), mean of the timed launches"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +206,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-attention measurement over the step's packed cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain elementwise kernel (torch.neg) over this many MiB of fp32, three "
@@ -294,6 +336,8 @@ def main():
         "budget_host_us": round(budget_us, 1),
         "pairs_per_step": work["pairs"],
     }
+    if not args.no_decode:
+        out["decode"] = time_decode(w, prob, pipe, args.steps)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on a sample of units)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, data, budgets, args.cpu_seconds, max_units=16)
