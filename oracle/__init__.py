@@ -21,13 +21,17 @@ Parts and the passages they follow:
   ("delete the k smallest"), and always keep the most recent w tokens.
 * :func:`gather` -- RippleKV page, Eq. 4: the compressed cache is the (k, v)
   pairs at the retained positions.
+* :func:`eviction_shift`, :func:`best_eviction`, :func:`decoupled_eviction` -- the joint
+  objective F(J) (the total output shift of evicting a set), its exact minimiser by
+  enumeration and DropKV's decoupled choice (DropKV page, "Methodology in Plain English";
+  the brute-force F(J_hat)/F(J*) study of its limitations paragraph).
 * :func:`decode_attention` -- decoding on that compressed cache (RippleKV Eq. 4; GraceKV
   page, physical cache packing: one ragged cache per (layer, KV head)): plain softmax
   attention of each new query head over its KV head's segment.
 
 Parity pins: see ``tests/test_oracle_pins.py`` (brute-force single-token removal,
 closed forms, invariants), ``tests/test_budget_oracle.py``, ``tests/test_pool_oracle.py``
-and ``tests/test_decode_oracle.py``.
+``tests/test_decode_oracle.py`` and ``tests/test_eviction_study.py``.
 """
 from __future__ import annotations
 
@@ -345,3 +349,61 @@ def decode_attention(q, k_cache, v_cache, offsets, *, num_layers, num_seqs, num_
                     out[l, s, h] = (w @ V) / tot
                     lse[l, s, h] = m + math.log(tot)
     return out, lse
+
+
+# --------------------------------------------------------------------------- joint objective
+def eviction_shift(q, k, v, evict, *, scale=None, squared=False):
+    """Total output shift F(J) of evicting the token set J from one unit, in fp64.
+
+    DropKV page, "Methodology in Plain English": removing tokens renormalises the softmax
+    over the survivors; the group objective is the total shift of the attention outputs, and
+    choosing the k tokens that minimise it is the NP-hard problem the decoupled score
+    approximates. Here F(J) = sum_i ||a_i - a_i^(-J)||_2 over the query rows i (squared with
+    ``squared``), a_i over every key row i sees, a_i^(-J) over those keys minus J.
+
+    q: fp64 [R][d] query rows; k, v: fp64 [n][d]; row i sees keys 0 .. n - R + i (the window
+    is the last R positions; pass R = 1 for a single query at position n - 1).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    R, d = q.shape
+    n = len(k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    keep = np.ones(n, dtype=bool)
+    keep[list(evict)] = False
+    total = 0.0
+    for i in range(R):
+        t = n - R + i
+        s = scale * (k[:t + 1] @ q[i])
+        w = np.exp(s - s.max())
+        a = (w @ v[:t + 1]) / w.sum()
+        ws = w * keep[:t + 1]
+        if ws.sum() == 0.0:
+            raise ValueError("evicting every key a row sees")
+        b = (ws @ v[:t + 1]) / ws.sum()
+        dist = float(np.linalg.norm(a - b))
+        total += dist * dist if squared else dist
+    return total
+
+
+def best_eviction(q, k, v, candidates, num_evict, *, scale=None, squared=False):
+    """Exact minimiser J* of F over every num_evict-subset of ``candidates`` (enumeration;
+    ties to the lexicographically first subset). Returns (J*, F(J*))."""
+    import itertools
+    best, best_f = None, math.inf
+    for J in itertools.combinations(sorted(candidates), num_evict):
+        f = eviction_shift(q, k, v, J, scale=scale, squared=squared)
+        if f < best_f:
+            best, best_f = J, f
+    return tuple(best), best_f
+
+
+def decoupled_eviction(score, candidates, num_evict):
+    """DropKV's decoupled choice: the num_evict candidates with the smallest individual
+    scores (ties to the lower position)."""
+    c = np.asarray(sorted(candidates))
+    sc = np.asarray(score, dtype=np.float64)[c]
+    order = c[np.lexsort((c, sc))]
+    return tuple(sorted(int(j) for j in order[:num_evict]))
