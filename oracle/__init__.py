@@ -19,6 +19,8 @@ Parts and the passages they follow:
   arithmetic after the fp64 multipliers.
 * :func:`kept_positions` -- DropKV page: keep the largest individual scores
   ("delete the k smallest"), and always keep the most recent w tokens.
+* :func:`kept_positions_heads` -- the same with head budgets chosen jointly over a layer's
+  KV heads (AdaDropKV; the rule is a reading, the pages name it without giving it).
 * :func:`gather` -- RippleKV page, Eq. 4: the compressed cache is the (k, v)
   pairs at the retained positions.
 * :func:`eviction_shift`, :func:`best_eviction`, :func:`decoupled_eviction` -- the joint
@@ -407,3 +409,32 @@ def decoupled_eviction(score, candidates, num_evict):
     sc = np.asarray(score, dtype=np.float64)[c]
     order = c[np.lexsort((c, sc))]
     return tuple(sorted(int(j) for j in order[:num_evict]))
+
+
+def kept_positions_heads(score_heads, n, window, budget, pool=1, n_sink=0):
+    """Kept positions of every KV head of one (sequence, layer) with head budgets chosen
+    jointly (AdaDropKV: AdaKV's head budget allocation on DropKV scores, DropKV page,
+    results on adaptive head budgets; the rule itself is not on the pages).
+
+    Reading: the layer keeps Hkv * budget rows in all. Every head keeps its recent window
+    [n - W, n) and its first ns = min(n_sink, n - W) positions; the remaining
+    Hkv * (budget - W - ns) slots go to the competitors (g, j), j in [ns, n - W), of all heads
+    with the largest ranking key (the score, or its max-pool as in kept_positions), ties to
+    the lower head, then the lower position. score_heads: [Hkv][>= n - W]. Returns a list of
+    Hkv ascending int32 arrays.
+    """
+    H = len(score_heads)
+    cand = n - window
+    ns = min(max(n_sink, 0), cand)
+    if budget < window + ns:
+        raise ValueError("budget smaller than the window plus the sinks")
+    keys = [pooled_scores(sc, cand, pool) if pool > 1 else np.asarray(sc[:cand], dtype=np.float64)
+            for sc in score_heads]
+    comp = [(-keys[g][j], g, j) for g in range(H) for j in range(ns, cand)]
+    comp.sort()
+    total = min(H * (budget - window - ns), H * (cand - ns))
+    chosen = [[] for _ in range(H)]
+    for _, g, j in comp[:total]:
+        chosen[g].append(j)
+    return [np.sort(np.concatenate([np.arange(ns), np.asarray(chosen[g], dtype=np.int64),
+                                    np.arange(cand, n)])).astype(np.int32) for g in range(H)]

@@ -91,3 +91,46 @@ def test_sinks_larger_than_the_prefix_and_budget_errors():
     assert kept.tolist() == list(range(10))
     with pytest.raises(ValueError):
         oracle.kept_positions(sc, 10, 4, 6, n_sink=3)  # b < W + ns
+
+
+# ---- head budgets chosen jointly over a layer's KV heads (AdaDropKV reading)
+def _heads_by_repeated_max(score_heads, n, W, b, ns):
+    """A different selection: repeatedly take the best remaining (key, -head, -position)."""
+    H, cand = len(score_heads), n - W
+    left = {(g, j) for g in range(H) for j in range(ns, cand)}
+    chosen = [[] for _ in range(H)]
+    for _ in range(min(H * (b - W - ns), len(left))):
+        g, j = max(left, key=lambda t: (float(score_heads[t[0]][t[1]]), -t[0], -t[1]))
+        left.remove((g, j))
+        chosen[g].append(j)
+    return [sorted(list(range(ns)) + chosen[g] + list(range(cand, n))) for g in range(H)]
+
+
+def test_heads_single_head_is_the_per_unit_selection():
+    rng = np.random.default_rng(31)
+    for _ in range(20):
+        n, W = int(rng.integers(10, 200)), int(rng.integers(1, 8))
+        ns = int(rng.integers(0, 4))
+        b = int(rng.integers(W + min(ns, n - W), n + 1))
+        sc = rng.standard_normal(n)
+        for pool in (1, 3):
+            assert oracle.kept_positions_heads([sc], n, W, b, pool, ns)[0].tolist() == \
+                oracle.kept_positions(sc, n, W, b, pool, ns).tolist()
+
+
+def test_heads_joint_selection_matches_repeated_max_and_keeps_the_layer_total():
+    rng = np.random.default_rng(32)
+    for trial in range(30):
+        H = int(rng.integers(1, 5))
+        n, W = int(rng.integers(8, 60)), int(rng.integers(1, 6))
+        ns = int(rng.integers(0, 3))
+        nse = min(ns, n - W)
+        b = int(rng.integers(W + nse, n + 1))
+        sc = [np.round(rng.standard_normal(n), 1) for _ in range(H)]  # coarse: many ties
+        got = oracle.kept_positions_heads(sc, n, W, b, 1, ns)
+        assert [g.tolist() for g in got] == _heads_by_repeated_max(sc, n, W, b, nse)
+        assert sum(len(g) for g in got) == H * b
+        kept = {(h, j) for h in range(H) for j in got[h] if nse <= j < n - W}
+        out = {(h, j) for h in range(H) for j in range(nse, n - W)} - kept
+        if kept and out:
+            assert min(sc[h][j] for h, j in kept) >= max(sc[h][j] for h, j in out)
