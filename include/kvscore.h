@@ -17,6 +17,8 @@
  *                      max-pooled key, optionally pinning sinks) plus the W most
  *                      recent tokens, as ascending positions in a packed array.
  *   kvscore_compact    gathers the kept K and V rows into a packed ragged cache.
+ *   kvscore_topk_heads / kvscore_compact_heads  the same with head budgets chosen jointly
+ *                      over the KV heads of a layer.
  *   kvscore_decode_attn  decode attention of new query tokens over that cache.
  *
  * Sources (the web pages this library implements):
@@ -217,6 +219,25 @@ int kvscore_topk(const kvscore_problem* p, const float* score, const int32_t* bu
                  size_t workspace_bytes, void* stream);
 
 /*
+ * Selection with head budgets chosen jointly over the KV heads of each (sequence, layer)
+ * (AdaDropKV: AdaKV's head budget allocation on the DropKV score, DropKV page, results on
+ * adaptive head budgets; the rule itself is not on the pages, this is its plainest
+ * reading). The layer keeps Hkv * b rows in all (b = budgets[s][l]); every head keeps its
+ * first ns = min(n_sink, n_s - W) positions and its W most recent ones; the remaining
+ * Hkv * (b - W - ns) slots go to the competitors (g, j), ns <= j < n_s - W, of all the
+ * layer's heads with the largest ranking key (score or max-pooled score, as in
+ * kvscore_topk), ties to the lower head, then the lower position.
+ * Arguments as kvscore_topk; seg_offsets is still the DEVICE copy of
+ * kvscore_segment_offsets(p, budgets) (it gives each layer's block). The heads' own
+ * segments are data-dependent: their offsets go to head_offsets (device int64 [U+1],
+ * inside the same blocks, head_offsets[U] = seg_offsets[U]) and their positions,
+ * ascending, to kept_pos[head_offsets[u] ..]. Consume them with kvscore_compact_heads.
+ */
+int kvscore_topk_heads(const kvscore_problem* p, const float* score, const int32_t* budgets,
+                       const int64_t* seg_offsets, int64_t* head_offsets, int32_t* kept_pos, int32_t pool,
+                       int32_t n_sink, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Compaction into the packed ragged cache (RippleKV Eq. 4): for every segment u and
  * slot r in it, k_out[off[u] + r] = k row (l, g, cu_s + kept_pos[off[u] + r]), same
  * for v; a bit-exact copy. budgets: HOST [S][L] (sizes the launch); seg_offsets,
@@ -225,6 +246,14 @@ int kvscore_topk(const kvscore_problem* p, const float* score, const int32_t* bu
 int kvscore_compact(const kvscore_problem* p, const void* k, const void* v, const int32_t* budgets,
                     const int64_t* seg_offsets, const int32_t* kept_pos, void* k_out, void* v_out,
                     void* stream);
+
+/*
+ * The same compaction for the segments of kvscore_topk_heads: head_offsets is its device
+ * output; budgets (HOST [S][L]) size the launch for segments up to min(n_s, Hkv * b).
+ */
+int kvscore_compact_heads(const kvscore_problem* p, const void* k, const void* v, const int32_t* budgets,
+                          const int64_t* head_offsets, const int32_t* kept_pos, void* k_out, void* v_out,
+                          void* stream);
 
 /*
  * Decode attention over the packed ragged cache (RippleKV page, "Problem Formulation":

@@ -55,7 +55,8 @@ EXPORTS = (
     "kvscore_version", "kvscore_last_error", "kvscore_num_query_tiles", "kvscore_workspace_size",
     "kvscore_attn_fwd", "kvscore_score", "kvscore_merge", "kvscore_budget", "kvscore_budget_pyramid",
     "kvscore_segment_offsets",
-    "kvscore_topk", "kvscore_compact", "kvscore_decode_workspace_size", "kvscore_decode_attn",
+    "kvscore_topk", "kvscore_compact", "kvscore_topk_heads", "kvscore_compact_heads",
+    "kvscore_decode_workspace_size", "kvscore_decode_attn",
 )
 
 _lib = None
@@ -84,6 +85,8 @@ def load():
         "kvscore_segment_offsets": (ctypes.c_int, [P, vp, vp]),
         "kvscore_topk": (ctypes.c_int, [P, vp, vp, vp, vp, i32, i32, vp, sz, vp]),
         "kvscore_compact": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "kvscore_topk_heads": (ctypes.c_int, [P, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp]),
+        "kvscore_compact_heads": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
         "kvscore_decode_workspace_size": (sz, [P, vp]),
         "kvscore_decode_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     }
@@ -278,6 +281,37 @@ def compact(p: Problem, k, v, budgets: np.ndarray, seg_off_dev, kept, k_out, v_o
     _need(v_out, R * p.head_dim, torch.bfloat16, "v_out")
     _check(load().kvscore_compact(p.ref, _ptr(k), _ptr(v), ctypes.c_void_p(b.ctypes.data), _ptr(seg_off_dev),
                                   _ptr(kept), _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+def topk_heads(p: Problem, score_t, budgets: np.ndarray, seg_off_dev, head_off_dev, kept, stream=None, *,
+               pool: int = 1, n_sink: int = 0, ws=None):
+    """Selection with head budgets chosen jointly over each layer's KV heads; the heads'
+    offsets go to ``head_off_dev`` (int64 [U+1], device)."""
+    b = np.ascontiguousarray(np.asarray(budgets, dtype=np.int32))
+    R = _check_segments(p, b, seg_off_dev)
+    _need(score_t, p.num_layers * p.num_kv_heads * p.total_tokens, torch.float32, "score")
+    _need(head_off_dev, p.units + 1, torch.int64, "head_offsets")
+    _need(kept, R, torch.int32, "kept_pos")
+    nbytes = 0
+    if pool > 1:
+        nbytes = p.workspace_size(WS_TOPK)
+        _need(ws, nbytes, torch.uint8, "workspace")
+    _check(load().kvscore_topk_heads(p.ref, _ptr(score_t), ctypes.c_void_p(b.ctypes.data), _ptr(seg_off_dev),
+                                     _ptr(head_off_dev), _ptr(kept), int(pool), int(n_sink),
+                                     _ptr(ws) if pool > 1 else None, nbytes, _stream(stream)))
+
+
+def compact_heads(p: Problem, k, v, budgets: np.ndarray, head_off_dev, kept, k_out, v_out, stream=None):
+    b = np.ascontiguousarray(np.asarray(budgets, dtype=np.int32))
+    R = int(segment_offsets(p, b)[-1])  # the layer totals do not change
+    _need(k, _kv_extent(p, p.c.k_strides), torch.bfloat16, "k")
+    _need(v, _kv_extent(p, p.c.v_strides), torch.bfloat16, "v")
+    _need(head_off_dev, p.units + 1, torch.int64, "head_offsets")
+    _need(kept, R, torch.int32, "kept_pos")
+    _need(k_out, R * p.head_dim, torch.bfloat16, "k_out")
+    _need(v_out, R * p.head_dim, torch.bfloat16, "v_out")
+    _check(load().kvscore_compact_heads(p.ref, _ptr(k), _ptr(v), ctypes.c_void_p(b.ctypes.data), _ptr(head_off_dev),
+                                        _ptr(kept), _ptr(k_out), _ptr(v_out), _stream(stream)))
 
 
 def _host_offsets(seg_off_host, units: int) -> np.ndarray:

@@ -226,6 +226,32 @@ int make_decdev(const kvscore_problem* p, const int64_t* off, kvs::DecDev& d) {
   return ok();
 }
 
+// Arguments of the selection entry points (both share them).
+int check_topk(const kvscore_problem* p, kvs::Dev& d, const float* score, const int32_t* budgets,
+               const int64_t* seg_offsets, const int32_t* kept_pos, int32_t pool, int32_t n_sink, void* workspace,
+               size_t workspace_bytes) {
+  if (int rc = make_dev(p, d)) return rc;
+  if (!score || !seg_offsets || !kept_pos) return fail(KVSCORE_EINVAL, "NULL tensor argument");
+  if (pool < 1 || pool > kvs::kMaxPoolSize || pool % 2 == 0)
+    return fail(KVSCORE_EINVAL, "pool=%d must be odd, in [1, %d]", pool, kvs::kMaxPoolSize);
+  if (n_sink < 0) return fail(KVSCORE_EINVAL, "n_sink=%d < 0", n_sink);
+  if (int rc = check_budgets(p, budgets, nullptr)) return rc;
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int64_t cand = p->cu_seqlens[s + 1] - p->cu_seqlens[s] - p->window;
+    const int64_t ns = std::min<int64_t>(n_sink, cand);
+    for (int l = 0; l < p->num_layers; ++l) {
+      const int32_t b = budgets[(int64_t)s * p->num_layers + l];
+      if (b < p->window + ns)
+        return fail(KVSCORE_EBUDGET, "budget[%d][%d]=%d below window + sinks (%d + %lld)", s, l, b, p->window,
+                    (long long)ns);
+    }
+  }
+  if (pool > 1) {
+    if (int rc = check_ws(workspace, workspace_bytes, ws_topk(d))) return rc;
+  }
+  return ok();
+}
+
 size_t ws_decode(const kvs::DecDev& d) { return (size_t)d.U * d.nsplit * d.G * (d.d + 2) * sizeof(float); }
 
 }  // namespace
@@ -423,28 +449,23 @@ int kvscore_topk(const kvscore_problem* p, const float* score, const int32_t* bu
                  int32_t* kept_pos, int32_t pool, int32_t n_sink, void* workspace, size_t workspace_bytes,
                  void* stream) {
   kvs::Dev d;
-  if (int rc = make_dev(p, d)) return rc;
-  if (!score || !seg_offsets || !kept_pos) return fail(KVSCORE_EINVAL, "NULL tensor argument");
-  if (pool < 1 || pool > kvs::kMaxPoolSize || pool % 2 == 0)
-    return fail(KVSCORE_EINVAL, "pool=%d must be odd, in [1, %d]", pool, kvs::kMaxPoolSize);
-  if (n_sink < 0) return fail(KVSCORE_EINVAL, "n_sink=%d < 0", n_sink);
-  if (int rc = check_budgets(p, budgets, nullptr)) return rc;
-  for (int s = 0; s < p->num_seqs; ++s) {
-    const int64_t cand = p->cu_seqlens[s + 1] - p->cu_seqlens[s] - p->window;
-    const int64_t ns = std::min<int64_t>(n_sink, cand);
-    for (int l = 0; l < p->num_layers; ++l) {
-      const int32_t b = budgets[(int64_t)s * p->num_layers + l];
-      if (b < p->window + ns)
-        return fail(KVSCORE_EBUDGET, "budget[%d][%d]=%d below window + sinks (%d + %lld)", s, l, b, p->window,
-                    (long long)ns);
-    }
-  }
-  if (pool > 1) {
-    if (int rc = check_ws(workspace, workspace_bytes, ws_topk(d))) return rc;
-  }
-  return launched(kvs::launch_topk(d, score, seg_offsets, kept_pos, pool, n_sink, (float*)workspace,
+  if (int rc = check_topk(p, d, score, budgets, seg_offsets, kept_pos, pool, n_sink, workspace, workspace_bytes))
+    return rc;
+  return launched(kvs::launch_topk(d, score, seg_offsets, kept_pos, pool, n_sink, (float*)workspace, nullptr,
                                    (hipStream_t)stream),
                   "kvscore_topk");
+}
+
+int kvscore_topk_heads(const kvscore_problem* p, const float* score, const int32_t* budgets,
+                       const int64_t* seg_offsets, int64_t* head_offsets, int32_t* kept_pos, int32_t pool,
+                       int32_t n_sink, void* workspace, size_t workspace_bytes, void* stream) {
+  kvs::Dev d;
+  if (int rc = check_topk(p, d, score, budgets, seg_offsets, kept_pos, pool, n_sink, workspace, workspace_bytes))
+    return rc;
+  if (!head_offsets) return fail(KVSCORE_EINVAL, "head_offsets is NULL");
+  return launched(kvs::launch_topk(d, score, seg_offsets, kept_pos, pool, n_sink, (float*)workspace, head_offsets,
+                                   (hipStream_t)stream),
+                  "kvscore_topk_heads");
 }
 
 int kvscore_compact(const kvscore_problem* p, const void* k, const void* v, const int32_t* budgets,
@@ -458,6 +479,26 @@ int kvscore_compact(const kvscore_problem* p, const void* k, const void* v, cons
   if (int rc = check_budgets(p, budgets, &max_b)) return rc;
   return launched(kvs::launch_compact(d, k, v, seg_offsets, kept_pos, k_out, v_out, max_b, (hipStream_t)stream),
                   "kvscore_compact");
+}
+
+int kvscore_compact_heads(const kvscore_problem* p, const void* k, const void* v, const int32_t* budgets,
+                          const int64_t* head_offsets, const int32_t* kept_pos, void* k_out, void* v_out,
+                          void* stream) {
+  kvs::Dev d;
+  if (int rc = make_dev(p, d)) return rc;
+  if (!k || !v || !head_offsets || !kept_pos || !k_out || !v_out) return fail(KVSCORE_EINVAL, "NULL tensor argument");
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16))
+    return fail(KVSCORE_EINVAL, "k/v/k_out/v_out not 16-byte aligned");
+  if (int rc = check_budgets(p, budgets, nullptr)) return rc;
+  // a head may take up to the layer's whole budget, never more than its sequence
+  int64_t max_seg = 0;
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int64_t n = p->cu_seqlens[s + 1] - p->cu_seqlens[s];
+    for (int l = 0; l < p->num_layers; ++l)
+      max_seg = std::max(max_seg, std::min<int64_t>(n, (int64_t)p->num_kv_heads * budgets[(int64_t)s * p->num_layers + l]));
+  }
+  return launched(kvs::launch_compact(d, k, v, head_offsets, kept_pos, k_out, v_out, (int)max_seg, (hipStream_t)stream),
+                  "kvscore_compact_heads");
 }
 
 size_t kvscore_decode_workspace_size(const kvscore_problem* p, const int64_t* seg_offsets_host) {

@@ -91,8 +91,10 @@ hipError_t launch_score(const Dev& p, const void* q, const void* k, const void* 
                         const float* lse, const int32_t* jstar, float* partial, void* ws, hipStream_t st);
 hipError_t launch_merge(const Dev& p, const float* partial, const int32_t* jstar, const float* dom, float* score,
                         hipStream_t st);
+// head_off != nullptr: head budgets chosen jointly per (sequence, layer), their offsets
+// written to head_off [U+1]
 hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off, int32_t* kept, int pool, int n_sink,
-                       float* pooled, hipStream_t st);
+                       float* pooled, int64_t* head_off, hipStream_t st);
 constexpr int kMaxPoolSize = 255;
 constexpr int kDecodeMaxGroup = 8;  // query heads per KV head the decode kernels take
 hipError_t launch_decode(const DecDev& p, const void* q, const void* k, const void* v, const int64_t* off, float* out,

@@ -28,9 +28,10 @@ def workload_budgets(w, n_sink: int = 0) -> np.ndarray:
 class Pipeline:
     """Owns the outputs and workspaces of one problem and runs the hot path."""
 
-    def __init__(self, prob: api.Problem, budgets: np.ndarray, device="cuda", *, pool: int = 1, n_sink: int = 0):
+    def __init__(self, prob: api.Problem, budgets: np.ndarray, device="cuda", *, pool: int = 1, n_sink: int = 0,
+                 heads: bool = False):
         self.p = prob
-        self.pool, self.n_sink = pool, n_sink
+        self.pool, self.n_sink, self.heads = pool, n_sink, heads
         self.budgets = np.ascontiguousarray(np.asarray(budgets, dtype=np.int32))
         dev = torch.device(device)
         d, rows = prob.head_dim, prob.rows
@@ -53,6 +54,8 @@ class Pipeline:
         self.k_out = torch.empty((max(R, 1), d), dtype=torch.bfloat16, device=dev)
         self.v_out = torch.empty((max(R, 1), d), dtype=torch.bfloat16, device=dev)
         self.kept_rows = R
+        # head budgets chosen jointly per layer: the heads' offsets come from the selection
+        self.head_off = torch.empty(prob.units + 1, dtype=torch.int64, device=dev) if heads else None
 
     def attn(self, q, k, v, stream=None):
         api.attn_fwd(self.p, q, k, v, self.a, self.lse, self.jstar, self.dom, self.ws_fwd, stream)
@@ -62,6 +65,11 @@ class Pipeline:
         api.merge(self.p, self.partial, self.jstar, self.dom, self.score, stream)
 
     def select(self, k, v, stream=None):
+        if self.heads:
+            api.topk_heads(self.p, self.score, self.budgets, self.seg_off, self.head_off, self.kept, stream,
+                           pool=self.pool, n_sink=self.n_sink, ws=self.ws_topk)
+            api.compact_heads(self.p, k, v, self.budgets, self.head_off, self.kept, self.k_out, self.v_out, stream)
+            return
         api.topk(self.p, self.score, self.budgets, self.seg_off, self.kept, stream, pool=self.pool,
                  n_sink=self.n_sink, ws=self.ws_topk)
         api.compact(self.p, k, v, self.budgets, self.seg_off, self.kept, self.k_out, self.v_out, stream)
@@ -75,7 +83,7 @@ class Pipeline:
         R = self.kept_rows
         return {"a": self.a, "lse": self.lse, "jstar": self.jstar, "dom": self.dom, "partial": self.partial,
                 "score": self.score, "kept": self.kept[:R], "k_out": self.k_out[:R], "v_out": self.v_out[:R],
-                "seg_off": self.seg_off_host}
+                "seg_off": self.head_off.cpu().numpy() if self.heads else self.seg_off_host}
 
 
 def problem_for(w, k: torch.Tensor, v: torch.Tensor, mode: int = api.MODE_L2) -> api.Problem:

@@ -32,7 +32,7 @@ def say(msg: str) -> None:
 
 
 def run_gpu(w: Workload, mode: int = api.MODE_L2, data=None, k_layout: str = "head_major", pool: int = 1,
-            n_sink: int = 0):
+            n_sink: int = 0, heads: bool = False):
     """Generate (or take) inputs on the GPU and run the whole pipeline once (pool > 1: rank by
     the max-pooled score; n_sink: pinned first tokens, budgets then start at W + sinks)."""
     if data is None:
@@ -43,7 +43,7 @@ def run_gpu(w: Workload, mode: int = api.MODE_L2, data=None, k_layout: str = "he
         v = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     prob = pipeline.problem_for(w, k, v, mode)
     budgets = pipeline.workload_budgets(w, n_sink)
-    pipe = pipeline.Pipeline(prob, budgets, pool=pool, n_sink=n_sink)
+    pipe = pipeline.Pipeline(prob, budgets, pool=pool, n_sink=n_sink, heads=heads)
     pipe.run(q, k, v)
     torch.cuda.synchronize()
     return dict(q=q, k=k, v=v, prob=prob, budgets=budgets, pipe=pipe, out=pipe.outputs())

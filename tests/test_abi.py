@@ -252,3 +252,24 @@ def test_token_stride_limit():
     assert "2^22" in api.load().kvscore_last_error().decode()
     p = make_problem(v_strides=(2 * 100 * 128, 100 * 128, big - 8))
     assert p.workspace_size(api.WS_SCORE) > 0
+
+
+def test_topk_heads_and_compact_heads_validation():
+    lib = api.load()
+    p = make_problem(num_seqs=2, cu_seqlens=[0, 100, 150])  # W = 16, L = 2
+    good = np.array([[40, 40], [30, 30]], dtype=np.int32)
+    fake = ctypes.c_void_p(0x1000)
+    bp = ctypes.c_void_p(good.ctypes.data)
+
+    def rc(pool=1, n_sink=0, head=fake, budgets=bp):
+        return lib.kvscore_topk_heads(p.ref, fake, budgets, fake, head, fake, pool, n_sink, None, 0, None)
+
+    assert rc(head=None) == api.EINVAL
+    assert rc(pool=2) == api.EINVAL
+    assert rc(n_sink=-1) == api.EINVAL
+    bad = np.array([[40, 40], [30, 19]], dtype=np.int32)
+    assert rc(n_sink=4, budgets=ctypes.c_void_p(bad.ctypes.data)) == api.EBUDGET
+    assert rc(pool=11) == api.EWORKSPACE
+    assert lib.kvscore_compact_heads(p.ref, fake, fake, bp, None, fake, fake, fake, None) == api.EINVAL
+    assert lib.kvscore_compact_heads(p.ref, fake, fake, bp, fake, fake, ctypes.c_void_p(0x1004), fake,
+                                     None) == api.EINVAL  # k_out misaligned
