@@ -172,12 +172,13 @@ def time_decode(w, prob, pipe, steps: int) -> dict:
     q = torch.randn((L, S, Hq, d), generator=g).to(torch.bfloat16).cuda()
     out = torch.empty((L, S, Hq, d), dtype=torch.float32, device="cuda")
     lse = torch.empty((L, S, Hq), dtype=torch.float32, device="cuda")
-    off = pipe.seg_off_host
+    off_dev = pipe.head_off if pipe.heads else pipe.seg_off  # the heads' own segments in --heads mode
+    off = off_dev.cpu().numpy()
     ws = torch.empty(api.decode_workspace_size(prob, off), dtype=torch.uint8, device="cuda")
     k_out, v_out = pipe.k_out[:pipe.kept_rows], pipe.v_out[:pipe.kept_rows]
 
     def run():
-        api.decode_attn(prob, q, k_out, v_out, off, pipe.seg_off, out, lse, ws)
+        api.decode_attn(prob, q, k_out, v_out, off, off_dev, out, lse, ws)
 
     for _ in range(3):
         run()
@@ -217,6 +218,8 @@ def main():
     ap.add_argument("--pool", type=int, default=1,
                     help="rank candidates by the score max-pooled over this odd window (1 = off)")
     ap.add_argument("--sinks", type=int, default=0, help="first tokens always kept (attention sinks)")
+    ap.add_argument("--heads", action="store_true",
+                    help="head budgets chosen jointly over each layer's KV heads (kvscore_topk_heads)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of this script "
                          "into HBM bytes per launch, written to --traffic-out")
@@ -249,7 +252,7 @@ def main():
     budget_us = (time.perf_counter() - t0) * 1e6
     mode = {"l2": api.MODE_L2, "sq": api.MODE_SQ, "attn": api.MODE_ATTN}[args.mode]
     prob = pipeline.problem_for(w, data["k"], data["v"], mode)
-    pipe = pipeline.Pipeline(prob, budgets, pool=args.pool, n_sink=args.sinks)
+    pipe = pipeline.Pipeline(prob, budgets, pool=args.pool, n_sink=args.sinks, heads=args.heads)
     q, k, v = data["q"], data["k"], data["v"]
     calls = [lambda: pipe.attn(q, k, v),
              lambda: api.score(prob, q, k, v, pipe.a, pipe.lse, pipe.jstar, pipe.partial, pipe.ws_score),
@@ -257,6 +260,11 @@ def main():
              lambda: api.topk(prob, pipe.score, pipe.budgets, pipe.seg_off, pipe.kept, pool=args.pool,
                               n_sink=args.sinks, ws=pipe.ws_topk),
              lambda: api.compact(prob, k, v, pipe.budgets, pipe.seg_off, pipe.kept, pipe.k_out, pipe.v_out)]
+    if args.heads:
+        calls[3] = lambda: api.topk_heads(prob, pipe.score, pipe.budgets, pipe.seg_off, pipe.head_off, pipe.kept,
+                                          pool=args.pool, n_sink=args.sinks, ws=pipe.ws_topk)
+        calls[4] = lambda: api.compact_heads(prob, k, v, pipe.budgets, pipe.head_off, pipe.kept, pipe.k_out,
+                                             pipe.v_out)
 
     if args.calibrate_copy_mib:
         src = torch.randn(args.calibrate_copy_mib * (1 << 18), device="cuda")
@@ -325,7 +333,8 @@ def main():
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "seqlens": list(w.seqlens),
                    "num_layers": w.num_layers, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "window": w.window, "kept_rows": pipe.kept_rows,
-                   "mode": args.mode.upper(), "pool": args.pool, "n_sink": args.sinks, "parallelism": "single GPU"},
+                   "mode": args.mode.upper(), "pool": args.pool, "n_sink": args.sinks,
+                   "head_budgets": "joint per layer" if args.heads else "uniform", "parallelism": "single GPU"},
         "roofline": roof,
         "kernels": kernels,
         "event_ms_per_step": round(step_ms, 4),
