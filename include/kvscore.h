@@ -93,6 +93,7 @@ extern "C" {
 #define KVSCORE_WS_ATTN_FWD 0
 #define KVSCORE_WS_SCORE 1
 #define KVSCORE_WS_TOPK 2
+#define KVSCORE_WS_TOPK_HEADS 3
 
 typedef struct kvscore_problem {
   int32_t num_seqs;          /* S, 1..KVSCORE_MAX_SEQS */
@@ -227,7 +228,11 @@ int kvscore_topk(const kvscore_problem* p, const float* score, const int32_t* bu
  * Hkv * (b - W - ns) slots go to the competitors (g, j), ns <= j < n_s - W, of all the
  * layer's heads with the largest ranking key (score or max-pooled score, as in
  * kvscore_topk), ties to the lower head, then the lower position.
- * Arguments as kvscore_topk; seg_offsets is still the DEVICE copy of
+ * workspace: device, kvscore_workspace_size(p, KVSCORE_WS_TOPK_HEADS) bytes, 256-byte
+ * aligned: the select's scratch (per-layer state, per-chunk histograms and counts), then
+ * the pooled keys; with pool = 1 only the scratch part (that size minus
+ * kvscore_workspace_size(p, KVSCORE_WS_TOPK)) is needed. Calls on one stream reuse it.
+ * The other arguments as kvscore_topk; seg_offsets is still the DEVICE copy of
  * kvscore_segment_offsets(p, budgets) (it gives each layer's block). The heads' own
  * segments are data-dependent: their offsets go to head_offsets (device int64 [U+1],
  * inside the same blocks, head_offsets[U] = seg_offsets[U]) and their positions,

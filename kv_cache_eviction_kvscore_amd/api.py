@@ -25,6 +25,7 @@ MODE_ATTN = 2  # aggregated window attention score (PyramidKV / SnapKV ranking)
 WS_ATTN_FWD = 0
 WS_SCORE = 1
 WS_TOPK = 2
+WS_TOPK_HEADS = 3
 OK, EINVAL, EWORKSPACE, EBUDGET, EDEVICE = 0, 1, 2, 3, 4
 ERRORS = {EINVAL: "EINVAL", EWORKSPACE: "EWORKSPACE", EBUDGET: "EBUDGET", EDEVICE: "EDEVICE"}
 
@@ -286,19 +287,20 @@ def compact(p: Problem, k, v, budgets: np.ndarray, seg_off_dev, kept, k_out, v_o
 def topk_heads(p: Problem, score_t, budgets: np.ndarray, seg_off_dev, head_off_dev, kept, stream=None, *,
                pool: int = 1, n_sink: int = 0, ws=None):
     """Selection with head budgets chosen jointly over each layer's KV heads; the heads'
-    offsets go to ``head_off_dev`` (int64 [U+1], device)."""
+    offsets go to ``head_off_dev`` (int64 [U+1], device). ``ws``: uint8 device tensor of
+    WS_TOPK_HEADS bytes (without the pooled-keys part when pool == 1)."""
     b = np.ascontiguousarray(np.asarray(budgets, dtype=np.int32))
     R = _check_segments(p, b, seg_off_dev)
     _need(score_t, p.num_layers * p.num_kv_heads * p.total_tokens, torch.float32, "score")
     _need(head_off_dev, p.units + 1, torch.int64, "head_offsets")
     _need(kept, R, torch.int32, "kept_pos")
-    nbytes = 0
-    if pool > 1:
-        nbytes = p.workspace_size(WS_TOPK)
-        _need(ws, nbytes, torch.uint8, "workspace")
+    nbytes = p.workspace_size(WS_TOPK_HEADS)
+    if pool == 1:
+        nbytes -= p.workspace_size(WS_TOPK)  # the pooled keys are not needed
+    _need(ws, nbytes, torch.uint8, "workspace")
     _check(load().kvscore_topk_heads(p.ref, _ptr(score_t), ctypes.c_void_p(b.ctypes.data), _ptr(seg_off_dev),
-                                     _ptr(head_off_dev), _ptr(kept), int(pool), int(n_sink),
-                                     _ptr(ws) if pool > 1 else None, nbytes, _stream(stream)))
+                                     _ptr(head_off_dev), _ptr(kept), int(pool), int(n_sink), _ptr(ws), nbytes,
+                                     _stream(stream)))
 
 
 def compact_heads(p: Problem, k, v, budgets: np.ndarray, head_off_dev, kept, k_out, v_out, stream=None):

@@ -246,9 +246,6 @@ int check_topk(const kvscore_problem* p, kvs::Dev& d, const float* score, const 
                     (long long)ns);
     }
   }
-  if (pool > 1) {
-    if (int rc = check_ws(workspace, workspace_bytes, ws_topk(d))) return rc;
-  }
   return ok();
 }
 
@@ -278,6 +275,8 @@ size_t kvscore_workspace_size(const kvscore_problem* p, int32_t which) {
       return ws_score(d);
     case KVSCORE_WS_TOPK:
       return ws_topk(d);
+    case KVSCORE_WS_TOPK_HEADS:
+      return kvs::heads_ws_bytes(d) + ws_topk(d);
     default:
       fail(KVSCORE_EINVAL, "unknown workspace kind %d", which);
       return 0;
@@ -451,7 +450,10 @@ int kvscore_topk(const kvscore_problem* p, const float* score, const int32_t* bu
   kvs::Dev d;
   if (int rc = check_topk(p, d, score, budgets, seg_offsets, kept_pos, pool, n_sink, workspace, workspace_bytes))
     return rc;
-  return launched(kvs::launch_topk(d, score, seg_offsets, kept_pos, pool, n_sink, (float*)workspace, nullptr,
+  if (pool > 1) {
+    if (int rc = check_ws(workspace, workspace_bytes, ws_topk(d))) return rc;
+  }
+  return launched(kvs::launch_topk(d, score, seg_offsets, kept_pos, pool, n_sink, (float*)workspace, nullptr, nullptr,
                                    (hipStream_t)stream),
                   "kvscore_topk");
 }
@@ -463,8 +465,11 @@ int kvscore_topk_heads(const kvscore_problem* p, const float* score, const int32
   if (int rc = check_topk(p, d, score, budgets, seg_offsets, kept_pos, pool, n_sink, workspace, workspace_bytes))
     return rc;
   if (!head_offsets) return fail(KVSCORE_EINVAL, "head_offsets is NULL");
-  return launched(kvs::launch_topk(d, score, seg_offsets, kept_pos, pool, n_sink, (float*)workspace, head_offsets,
-                                   (hipStream_t)stream),
+  // scratch of the joint select first, the pooled keys (pool > 1) after it
+  const size_t hb = kvs::heads_ws_bytes(d);
+  if (int rc = check_ws(workspace, workspace_bytes, hb + (pool > 1 ? ws_topk(d) : 0))) return rc;
+  return launched(kvs::launch_topk(d, score, seg_offsets, kept_pos, pool, n_sink, (float*)((char*)workspace + hb),
+                                   head_offsets, workspace, (hipStream_t)stream),
                   "kvscore_topk_heads");
 }
 

@@ -226,102 +226,264 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
   emit_segment(sm, kept + off0, b, sel, T, need_eq, sc, n, cand, ns);
 }
 
-// Head budgets chosen jointly: one workgroup per (sequence, layer). The layer keeps
-// Hkv * b rows (b = the segment length seg_off gives its heads); every head keeps its sinks
-// and window; the Hkv * (b - W - ns) other slots go to the largest keys over all heads'
-// competitors, ties to the lower head, then the lower position. Writes the heads' offsets
-// (inside the layer's block of seg_off) to head_off and their positions to kept.
-__global__ __launch_bounds__(NT) void topk_heads_kernel(Dev p, const float* __restrict__ score, int n_sink,
-                                                       const int64_t* __restrict__ seg_off,
-                                                       int64_t* __restrict__ head_off, int32_t* __restrict__ kept) {
-  __shared__ SelectSmem sm;
-  const int blk = blockIdx.x;  // l*S + s
-  const int l = blk / p.S, s = blk % p.S;
-  const int H = p.Hkv;
-  const int u0 = blk * H;
+// Head budgets chosen jointly over the KV heads of each (sequence, layer) "group": the
+// group keeps Hkv * b rows (b = the segment length seg_off gives its heads); every head
+// keeps its sinks and window; the Hkv * (b - W - ns) other slots go to the largest keys over
+// all heads' competitors, ties to the lower head, then the lower position. The radix select
+// runs over many workgroups: each takes HCH competitors of one head and writes its own
+// histogram; a per-group kernel sums them in a fixed order and picks the digit. No atomics,
+// so every count is exact and the result deterministic.
+constexpr int HCH = 8192;  // competitors per histogram workgroup
+
+struct HeadsState {  // per group
+  long long kr;       // rank still to place inside the current prefix
+  long long need_eq;  // keys equal to T taken (after the last pass)
+  unsigned prefix;    // T after the last pass
+  int sel;            // 0: no competitor kept, 1: all, 2: radix select
+  int ns;             // sinks of the group's sequence
+  int pad;
+};
+
+__device__ inline void group_of(const Dev& p, int grp, int& l, int& s) {
+  l = grp / p.S;
+  s = grp % p.S;
+}
+
+__global__ __launch_bounds__(64) void heads_init_kernel(Dev p, int n_sink, const int64_t* __restrict__ seg_off,
+                                                        HeadsState* __restrict__ st) {
+  const int grp = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  int l, s;
+  group_of(p, grp, l, s);
   const int64_t n = p.cu[s + 1] - p.cu[s];
   const int64_t cand = n - p.W;
   const int64_t ns = n_sink < cand ? n_sink : cand;
-  const int64_t M = cand - ns;  // competitors per head
-  const int64_t base0 = seg_off[u0];
-  const int64_t b = seg_off[u0 + 1] - base0;  // every head of the layer has the layer's budget
-  int64_t kt = (int64_t)H * (b - p.W - ns);
+  const int64_t M = cand - ns;
+  const int64_t b = seg_off[grp * p.Hkv + 1] - seg_off[grp * p.Hkv];
+  int64_t kt = (int64_t)p.Hkv * (b - p.W - ns);
   if (kt < 0) kt = 0;
-  if (kt > (int64_t)H * M) kt = (int64_t)H * M;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  auto head_sc = [&](int g) { return score + (int64_t)(l * H + g) * p.N + p.cu[s]; };
+  if (kt > (int64_t)p.Hkv * M) kt = (int64_t)p.Hkv * M;
+  HeadsState x;
+  x.kr = kt;
+  x.need_eq = 0;
+  x.prefix = 0;
+  x.sel = (kt == 0) ? 0 : (kt == (int64_t)p.Hkv * M ? 1 : 2);
+  x.ns = (int)ns;
+  x.pad = 0;
+  st[grp] = x;
+}
 
-  const int sel = (kt == 0) ? 0 : (kt == (int64_t)H * M ? 1 : 2);
-  unsigned T = 0;
-  int64_t need_eq = 0;
-  if (sel == 2)
-    radix_select(sm, [&](auto f) {
-      for (int g = 0; g < H; ++g) {
-        const float* sc = head_sc(g);
-        for (int64_t j = ns + tid; j < cand; j += NT) f(f2key(sc[j]));
-      }
-    }, kt, T, need_eq);
-
-  // per head: kept competitors k_g = (key > T) + its share of the first need_eq ties in
-  // (head, position) order; then the heads' offsets inside the layer's block
-  int64_t off = base0, ties_before = 0;
-  for (int g = 0; g < H; ++g) {
-    int64_t kg = 0, take = 0;
-    if (sel == 1) {
-      kg = M;
-    } else if (sel == 2) {
-      const float* sc = head_sc(g);
-      long long cs = 0, ce = 0;
-      for (int64_t j = ns + tid; j < cand; j += NT) {
-        const unsigned key = f2key(sc[j]);
-        cs += key > T;
-        ce += key == T;
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        cs += __shfl_xor(cs, o, 64);
-        ce += __shfl_xor(ce, o, 64);
-      }
-      if (lane == 0) {
-        sm.red[0][wave] = cs;
-        sm.red[1][wave] = ce;
-      }
-      __syncthreads();
-      long long ts = 0, te = 0;
-      for (int w = 0; w < NWAVES; ++w) {
-        ts += sm.red[0][w];
-        te += sm.red[1][w];
-      }
-      __syncthreads();  // red is rewritten for the next head
-      take = need_eq - ties_before;
-      if (take < 0) take = 0;
-      if (take > te) take = te;
-      ties_before += te;
-      kg = ts + take;
-    }
-    const int64_t bg = p.W + ns + kg;
-    if (tid == 0) head_off[u0 + g] = off;
-    emit_segment(sm, kept + off, bg, sel, T, take, head_sc(g), n, cand, ns);
-    off += bg;
+// pass `pass` of the select: histogram of the 8-bit digit of the keys of one chunk of one
+// head (unit) that match the prefix so far; whist[u][chunk][256]
+__global__ __launch_bounds__(NT) void heads_hist_kernel(Dev p, const float* __restrict__ score,
+                                                        const HeadsState* __restrict__ st, int pass, int nch,
+                                                        unsigned* __restrict__ whist) {
+  __shared__ unsigned wh[NWAVES][256];
+  const int u = blockIdx.y, c = blockIdx.x;
+  const int grp = u / p.Hkv, g = u % p.Hkv;
+  const HeadsState x = st[grp];
+  unsigned* out = whist + ((int64_t)u * nch + c) * 256;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  if (x.sel != 2) return;  // uniform
+  int l, s;
+  group_of(p, grp, l, s);
+  const int64_t cand = p.cu[s + 1] - p.cu[s] - p.W;
+  const int64_t j0 = x.ns + (int64_t)c * HCH;
+  const int64_t j1 = (j0 + HCH < cand) ? j0 + HCH : cand;
+  const int shift = 24 - 8 * pass;
+  const unsigned pmask = pass ? (0xFFFFFFFFu << (32 - 8 * pass)) : 0u;
+  for (int i = tid; i < NWAVES * 256; i += NT) (&wh[0][0])[i] = 0;
+  __syncthreads();
+  const float* sc = score + (int64_t)(l * p.Hkv + g) * p.N + p.cu[s];
+  for (int64_t j = j0 + tid; j < j1; j += NT) {
+    const unsigned key = f2key(sc[j]);
+    if ((key & pmask) == (x.prefix & pmask)) atomicAdd(&wh[wave][(key >> shift) & 255u], 1u);
   }
-  if (tid == 0 && u0 + H == p.U) head_off[p.U] = off;  // the last layer block closes the array
+  __syncthreads();
+  if (tid < 256) {
+    unsigned t = 0;
+    for (int w = 0; w < NWAVES; ++w) t += wh[w][tid];
+    out[tid] = t;  // a chunk past the head's competitors writes zeros
+  }
+}
+
+// per group: sum the chunks' histograms (heads and chunks in ascending order) and place the
+// rank: the digit where the count from the top first reaches kr
+__global__ __launch_bounds__(256) void heads_digit_kernel(Dev p, HeadsState* __restrict__ st, int pass, int nch,
+                                                          const unsigned* __restrict__ whist) {
+  __shared__ unsigned bins[256];
+  __shared__ int s_digit;
+  __shared__ long long s_above;
+  const int grp = blockIdx.x;
+  HeadsState x = st[grp];
+  if (x.sel != 2) return;  // uniform
+  const int t = threadIdx.x;
+  unsigned tot = 0;
+  for (int g = 0; g < p.Hkv; ++g) {
+    const unsigned* h = whist + (int64_t)(grp * p.Hkv + g) * nch * 256;
+    for (int c = 0; c < nch; ++c) tot += h[(int64_t)c * 256 + t];
+  }
+  bins[t] = tot;
+  __syncthreads();
+  if (t < 64) {
+    // lane L owns digits 255-4L .. 252-4L (descending)
+    unsigned c4[4], sum = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c4[e] = bins[255 - 4 * t - e];
+      sum += c4[e];
+    }
+    const int incl = wave_incl_scan((int)sum, t);
+    const int excl = incl - (int)sum;
+    if ((long long)excl < x.kr && x.kr <= (long long)incl) {
+      long long above = excl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (above + c4[e] >= x.kr) {
+          s_digit = 255 - 4 * t - e;
+          s_above = above;
+          break;
+        }
+        above += c4[e];
+      }
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    x.prefix |= (unsigned)s_digit << (24 - 8 * pass);
+    x.kr -= s_above;
+    if (pass == 3) x.need_eq = x.kr;
+    st[grp] = x;
+  }
+}
+
+// per chunk of one head: how many competitors are above T and how many equal it
+__global__ __launch_bounds__(NT) void heads_count_kernel(Dev p, const float* __restrict__ score,
+                                                         const HeadsState* __restrict__ st, int nch,
+                                                         unsigned* __restrict__ cnt) {
+  __shared__ unsigned red[2][NWAVES];
+  const int u = blockIdx.y, c = blockIdx.x;
+  const int grp = u / p.Hkv, g = u % p.Hkv;
+  const HeadsState x = st[grp];
+  if (x.sel != 2) return;  // uniform
+  int l, s;
+  group_of(p, grp, l, s);
+  const int64_t cand = p.cu[s + 1] - p.cu[s] - p.W;
+  const int64_t j0 = x.ns + (int64_t)c * HCH;
+  const int64_t j1 = (j0 + HCH < cand) ? j0 + HCH : cand;
+  const float* sc = score + (int64_t)(l * p.Hkv + g) * p.N + p.cu[s];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  unsigned cs = 0, ce = 0;
+  for (int64_t j = j0 + tid; j < j1; j += NT) {
+    const unsigned key = f2key(sc[j]);
+    cs += key > x.prefix;
+    ce += key == x.prefix;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    cs += __shfl_xor(cs, o, 64);
+    ce += __shfl_xor(ce, o, 64);
+  }
+  if (lane == 0) {
+    red[0][wave] = cs;
+    red[1][wave] = ce;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    unsigned ts = 0, te = 0;
+    for (int w = 0; w < NWAVES; ++w) {
+      ts += red[0][w];
+      te += red[1][w];
+    }
+    cnt[((int64_t)u * nch + c) * 2] = ts;
+    cnt[((int64_t)u * nch + c) * 2 + 1] = te;
+  }
+}
+
+// one workgroup per head: its kept count (above T plus its share of the first need_eq ties
+// in (head, position) order), its offset inside the group's block, then its positions
+__global__ __launch_bounds__(NT) void heads_emit_kernel(Dev p, const float* __restrict__ score,
+                                                        const HeadsState* __restrict__ st, int nch,
+                                                        const unsigned* __restrict__ cnt,
+                                                        const int64_t* __restrict__ seg_off,
+                                                        int64_t* __restrict__ head_off, int32_t* __restrict__ kept) {
+  __shared__ SelectSmem sm;
+  const int u = blockIdx.x;
+  const int grp = u / p.Hkv, g = u % p.Hkv;
+  const HeadsState x = st[grp];
+  int l, s;
+  group_of(p, grp, l, s);
+  const int64_t n = p.cu[s + 1] - p.cu[s];
+  const int64_t cand = n - p.W;
+  const int64_t ns = x.ns;
+  const int64_t M = cand - ns;
+  // the kept competitors of head h: above T plus its share of the ties
+  int64_t ties_before = 0, off = seg_off[grp * p.Hkv], kg = 0, take = 0;
+  for (int h = 0; h <= g; ++h) {
+    int64_t sure = 0, eq = 0;
+    if (x.sel == 2) {
+      for (int c = 0; c < nch; ++c) {
+        sure += cnt[((int64_t)(grp * p.Hkv + h) * nch + c) * 2];
+        eq += cnt[((int64_t)(grp * p.Hkv + h) * nch + c) * 2 + 1];
+      }
+    }
+    int64_t tk = x.need_eq - ties_before;
+    if (tk < 0) tk = 0;
+    if (tk > eq) tk = eq;
+    ties_before += eq;
+    const int64_t kh = (x.sel == 1) ? M : (x.sel == 2 ? sure + tk : 0);
+    if (h < g) off += p.W + ns + kh;
+    else {
+      kg = kh;
+      take = tk;
+    }
+  }
+  const int64_t bg = p.W + ns + kg;
+  if (threadIdx.x == 0) {
+    head_off[u] = off;
+    if (u == p.U - 1) head_off[p.U] = off + bg;
+  }
+  const float* sc = score + (int64_t)(l * p.Hkv + g) * p.N + p.cu[s];
+  emit_segment(sm, kept + off, bg, x.sel, x.prefix, take, sc, n, cand, ns);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off, int32_t* kept, int pool, int n_sink,
-                       float* pooled, int64_t* head_off, hipStream_t st) {
+                       float* pooled, int64_t* head_off, void* heads_ws, hipStream_t st) {
   const float* key = score;
   if (pool > 1) {
     const dim3 gp((unsigned)((p.max_n + PT - 1) / PT), p.U);
     hipLaunchKernelGGL(pool_kernel, gp, dim3(256), 0, st, p, score, pool, pooled);
     key = pooled;
   }
-  if (head_off)
-    hipLaunchKernelGGL(topk_heads_kernel, dim3(p.U / p.Hkv), dim3(NT), 0, st, p, key, n_sink, seg_off, head_off, kept);
-  else
+  if (!head_off) {
     hipLaunchKernelGGL(topk_kernel, dim3(p.U), dim3(NT), 0, st, p, key, n_sink, seg_off, kept);
+    return hipGetLastError();
+  }
+  // head budgets chosen jointly; scratch: states | chunk histograms | chunk counts
+  const int groups = p.U / p.Hkv;
+  const int nch = heads_chunks(p);
+  HeadsState* hs = (HeadsState*)heads_ws;
+  unsigned* whist = (unsigned*)((char*)heads_ws + heads_state_bytes(p));
+  unsigned* cnt = whist + (size_t)p.U * nch * 256;
+  hipLaunchKernelGGL(heads_init_kernel, dim3(groups), dim3(64), 0, st, p, n_sink, seg_off, hs);
+  for (int pass = 0; pass < 4; ++pass) {
+    hipLaunchKernelGGL(heads_hist_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, pass, nch,
+                       whist);
+    hipLaunchKernelGGL(heads_digit_kernel, dim3(groups), dim3(256), 0, st, p, hs, pass, nch, (const unsigned*)whist);
+  }
+  hipLaunchKernelGGL(heads_count_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, nch, cnt);
+  hipLaunchKernelGGL(heads_emit_kernel, dim3(p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, nch,
+                     (const unsigned*)cnt, seg_off, head_off, kept);
   return hipGetLastError();
+}
+
+int heads_chunks(const Dev& p) { return (int)((p.max_n - p.W + HCH - 1) / HCH); }
+size_t heads_state_bytes(const Dev& p) { return ((size_t)(p.U / p.Hkv) * sizeof(HeadsState) + 255) / 256 * 256; }
+size_t heads_ws_bytes(const Dev& p) {
+  const size_t nch = (size_t)heads_chunks(p);
+  return heads_state_bytes(p) + ((size_t)p.U * nch * 256 * 4 + (size_t)p.U * nch * 2 * 4 + 255) / 256 * 256;
 }
 
 }  // namespace kvs

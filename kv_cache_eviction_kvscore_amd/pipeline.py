@@ -56,6 +56,9 @@ class Pipeline:
         self.kept_rows = R
         # head budgets chosen jointly per layer: the heads' offsets come from the selection
         self.head_off = torch.empty(prob.units + 1, dtype=torch.int64, device=dev) if heads else None
+        if heads:  # the joint select's scratch, then (pool > 1) the pooled keys
+            nb = prob.workspace_size(api.WS_TOPK_HEADS) - (0 if pool > 1 else prob.workspace_size(api.WS_TOPK))
+            self.ws_topk = torch.empty(nb, dtype=torch.uint8, device=dev)
 
     def attn(self, q, k, v, stream=None):
         api.attn_fwd(self.p, q, k, v, self.a, self.lse, self.jstar, self.dom, self.ws_fwd, stream)
