@@ -15,7 +15,7 @@ constexpr int kMaxRows = 1024;
 __global__ __launch_bounds__(256) void merge_kernel(Dev p, const float* __restrict__ partial,
                                                     const int32_t* __restrict__ jstar, const float* __restrict__ dom,
                                                     float* __restrict__ score) {
-  __shared__ float buf[kMergeChunk];
+  __shared__ alignas(16) float buf[kMergeChunk];
   __shared__ int js[kMaxRows];
   const int u = blockIdx.y;
   int l, s, g;
@@ -26,12 +26,38 @@ __global__ __launch_bounds__(256) void merge_kernel(Dev p, const float* __restri
   const int64_t jend = (n < j0 + kMergeChunk) ? n : j0 + kMergeChunk;
   const int tid = threadIdx.x;
   const float* pb = partial + (int64_t)(l * p.Hkv + g) * p.Tq * p.N + p.cu[s];
-  for (int i = tid; i < kMergeChunk; i += 256) {
-    const int64_t j = j0 + i;
-    float acc = 0.f;
-    if (j < jend)
-      for (int t = 0; t < p.Tq; ++t) acc += pb[(int64_t)t * p.N + j];
-    buf[i] = acc;
+  // 16-byte loads and stores when every tile row of this unit and its score row start
+  // 16-byte aligned (uniform)
+  const bool vec = ((p.cu[s] | p.N) & 3) == 0 && (((size_t)partial | (size_t)score) & 15) == 0;
+  if (vec) {
+    for (int i = 4 * tid; i < kMergeChunk; i += 4 * 256) {
+      const int64_t j = j0 + i;
+      float4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (j + 3 < jend) {
+        for (int t = 0; t < p.Tq; ++t) {
+          const float4 x = *(const float4*)(pb + (int64_t)t * p.N + j);
+          acc.x += x.x;
+          acc.y += x.y;
+          acc.z += x.z;
+          acc.w += x.w;
+        }
+      } else {
+        float a4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 4; ++e)
+          if (j + e < jend)
+            for (int t = 0; t < p.Tq; ++t) a4[e] += pb[(int64_t)t * p.N + j + e];
+        acc = float4{a4[0], a4[1], a4[2], a4[3]};
+      }
+      *(float4*)&buf[i] = acc;
+    }
+  } else {
+    for (int i = tid; i < kMergeChunk; i += 256) {
+      const int64_t j = j0 + i;
+      float acc = 0.f;
+      if (j < jend)
+        for (int t = 0; t < p.Tq; ++t) acc += pb[(int64_t)t * p.N + j];
+      buf[i] = acc;
+    }
   }
   const int64_t rb = (int64_t)u * p.R;
   for (int r = tid; r < p.R; r += 256) js[r] = jstar[rb + r];
@@ -53,9 +79,19 @@ __global__ __launch_bounds__(256) void merge_kernel(Dev p, const float* __restri
   }
   __syncthreads();
   float* out = score + (int64_t)(l * p.Hkv + g) * p.N + p.cu[s];
-  for (int i = tid; i < kMergeChunk; i += 256) {
-    const int64_t j = j0 + i;
-    if (j < jend) out[j] = buf[i];
+  if (vec) {
+    for (int i = 4 * tid; i < kMergeChunk; i += 4 * 256) {
+      const int64_t j = j0 + i;
+      if (j + 3 < jend) *(float4*)(out + j) = *(const float4*)&buf[i];
+      else
+        for (int e = 0; e < 4; ++e)
+          if (j + e < jend) out[j + e] = buf[i + e];
+    }
+  } else {
+    for (int i = tid; i < kMergeChunk; i += 256) {
+      const int64_t j = j0 + i;
+      if (j < jend) out[j] = buf[i];
+    }
   }
 }
 
