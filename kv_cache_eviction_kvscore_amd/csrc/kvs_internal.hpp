@@ -40,7 +40,7 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 constexpr int kMaxSeqs = 64;
 constexpr int kRowsPerTileMax = 256;  // query rows one workgroup holds (8 waves x 32 rows)
 constexpr int kMergeChunk = 4096;     // tokens per merge workgroup
-constexpr int kCompactRows = 64;      // packed rows per compaction workgroup
+constexpr int kCompactRows = 32;      // packed rows per compaction workgroup
 
 // Problem as the kernels see it (passed by value as a kernel argument).
 struct Dev {

@@ -27,13 +27,13 @@
 //   D = ||a - v||^2. ||v_j||^2 is summed from the tile in LDS (v_dot2_f32_bf16) one
 //   tile ahead of its use. The Q.K^T chain gets an augmented k-step too: (-lse_i/scale
 //   in three bf16 parts) times (1, 1, 1), so its accumulator is ln p / scale and needs no
-//   per-row register. Per pair: p = exp2(acc * scale * log2 e), and
-//   c*sqrt(D) = sqrt(2) * p*(D/2)*rsq((D/2)*(1-p)^2): two transcendentals and six other
-//   VALU operations; the sqrt(2) (2 in mode SQ) is applied once per token. Pairs
+//   per-row register. Per pair: 1/p = exp2(-acc * scale * log2 e), and
+//   c*sqrt(D) = sqrt(2) * sqrt(D/2) / (1/p - 1): three transcendentals and three other
+//   VALU instructions; the sqrt(2) (2 in mode SQ) is applied once per token. Pairs
 //   (i, j*_i) are skipped (their term comes exactly from the forward); so are keys after
 //   a row's position. Both masks only act on tiles flagged in LDS, others run unmasked.
-//   Every pair that is not masked has p <= 1/2 (the row's argmax is isolated), so 1 - p
-//   needs no guard.
+//   Every pair that is not masked has p <= 1/2 (the row's argmax is isolated), so
+//   1/p - 1 >= 1 needs no guard, and p = 0 gives a zero term.
 #include <type_traits>
 
 #include "kvs_internal.hpp"
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   // fields the lambdas below use, as locals: a by-reference capture of the by-value
   // argument would be re-read from kernel-argument memory with vector loads
   const int64_t kst = p.kst, vst = p.vst;
-  const float c1s = p.c1;
+  const float c1s = p.c1, nc1s = -p.c1;
   const int W = p.W;
   const __bf16* kb0 = k + l * p.ksl + g * p.ksh + p.cu[s] * p.kst;
   const __bf16* vb0 = v + l * p.vsl + g * p.vsh + p.cu[s] * p.vst;
@@ -309,43 +309,49 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   // chains interleave
   auto pair_terms = [&](auto masked, const BlockAcc& acc, const int pi0, const int key, float& col)
       __attribute__((always_inline)) {
-    float pr[PPR], ax[PPR], om[PPR], w[PPR], t[PPR];
-#pragma unroll
-    for (int i = 0; i < PPR; ++i) pr[i] = __builtin_amdgcn_exp2f(acc.S[pi0 + i] * c1s);
-    if constexpr (MODE != 2) {
-#pragma unroll
-      for (int i = 0; i < PPR; ++i) {
-        ax[i] = fabsf(acc.X[pi0 + i]);  // D/2
-        om[i] = 1.f - pr[i];
-      }
-    }
+    float x[PPR], y[PPR];  // the pair's term is x * y
     if constexpr (MODE == 2) {
 #pragma unroll
       for (int i = 0; i < PPR; ++i) {
-        w[i] = 1.f;
-        t[i] = pr[i];  // the attention weight itself
+        x[i] = __builtin_amdgcn_exp2f(acc.S[pi0 + i] * c1s);  // p itself
+        y[i] = 1.f;
       }
-    } else if constexpr (MODE == 0) {
-      // p sqrt(D/2) / (1-p) = p (D/2) rsq((D/2)(1-p)^2); the tiny addend keeps D = 0 finite
-#pragma unroll
-      for (int i = 0; i < PPR; ++i) w[i] = __builtin_amdgcn_rsqf(fmaf(ax[i] * om[i], om[i], 1e-30f));
-#pragma unroll
-      for (int i = 0; i < PPR; ++i) t[i] = pr[i] * ax[i];
     } else {
-      // p^2 (D/2) / (1-p)^2
+      // e = 1/p and r = 1/(e - 1) = p/(1-p): e >= 2 on every unmasked pair, so r is finite
+      // (0 when p underflows); a masked pair's value is never added
+      float e[PPR], r[PPR];
 #pragma unroll
-      for (int i = 0; i < PPR; ++i) w[i] = __builtin_amdgcn_rcpf(fmaf(om[i], om[i], 1e-30f));
+      for (int i = 0; i < PPR; ++i) e[i] = __builtin_amdgcn_exp2f(acc.S[pi0 + i] * nc1s);
 #pragma unroll
-      for (int i = 0; i < PPR; ++i) t[i] = pr[i] * pr[i] * ax[i];
+      for (int i = 0; i < PPR; ++i) r[i] = __builtin_amdgcn_rcpf(e[i] - 1.f);
+      if constexpr (MODE == 0) {
+        // p/(1-p) sqrt(D/2): three transcendentals and three other VALU instructions. The
+        // matrix cores leave room for about four VALU instructions of any kind per MFMA,
+        // so this beats a form with one transcendental less and three more plain ones.
+#pragma unroll
+        for (int i = 0; i < PPR; ++i) {
+          x[i] = r[i];
+          y[i] = __builtin_amdgcn_sqrtf(fabsf(acc.X[pi0 + i]));
+        }
+      } else {
+        // p^2 (D/2) / (1-p)^2
+#pragma unroll
+        for (int i = 0; i < PPR; ++i) {
+          x[i] = r[i] * r[i];
+          y[i] = fabsf(acc.X[pi0 + i]);
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < PPR; ++i) {
       if constexpr (decltype(masked)::value) {
-        const int r = pi0 + i;
-        const int rt = wrow0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        col += (key > sm.tlim[rt] || key == sm.jst[rt]) ? 0.f : t[i] * w[i];
+        const int rr = pi0 + i;
+        const int rt = wrow0 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        col += (key > sm.tlim[rt] || key == sm.jst[rt]) ? 0.f : x[i] * y[i];
+      } else if constexpr (MODE == 2) {
+        col += x[i];
       } else {
-        col = fmaf(t[i], w[i], col);
+        col = fmaf(x[i], y[i], col);
       }
     }
   };
