@@ -86,8 +86,11 @@ __device__ inline void vm_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-__device__ inline float wave_shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
-__device__ inline int wave_shfl_xor_i(int x, int m) { return __shfl_xor(x, m, 64); }
+// max over the two lanes of a row (lanes r and r + 32)
+__device__ inline float row_max(float x) {
+  const HalfPair v = wave_halves(x);
+  return fmaxf(v.lo, v.hi);
+}
 
 template <int D>
 __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf16* __restrict__ q,
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
     float lm = tv[0];
 #pragma unroll
     for (int e = 1; e < 32; ++e) lm = fmaxf(lm, tv[e]);
-    const float mt = fmaxf(lm, wave_shfl_xor_f(lm, 32));
+    const float mt = row_max(lm);
 
     // Row state (raw q.k units): m = running max (key jst, value row in vs); m2 = the
     // reference of the rest sums lrest / o, within kSlack log2 units of the running max
@@ -312,27 +315,23 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       float mtv = mt;
       asm volatile("" : "+v"(mtv));
       int jl = 64;
-      float hi2 = -INFINITY, lo2 = -INFINITY;
       if (moved) {
         // elements run in key order within a lane: the first equal to mt is the lane's lowest key
 #pragma unroll
         for (int e = 31; e >= 0; --e) jl = (tv[e] == mtv) ? e : jl;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          lo2 = __builtin_amdgcn_fmed3f(lo2, hi2, tv[e]);
-          hi2 = fmaxf(hi2, tv[e]);
-        }
       }
       const int keyl = (jl < 64) ? trel + 32 * (jl >> 4) + 8 * ((jl & 15) >> 2) + 4 * h + (jl & 3) : 0x7fffffff;
-      jt = min(keyl, wave_shfl_xor_i(keyl, 32));
+      jt = wave_halves_min(keyl);
       jr = (moved && keyl == jt) ? jl : -1;
-      // tile max without the new argmax: the lane holding it contributes its second largest
-      const float mt2l = moved ? ((jr >= 0) ? lo2 : hi2) : -INFINITY;
-      const float mt2 = fmaxf(mt2l, wave_shfl_xor_f(mt2l, 32));
-      if (moved) cand = fmaxf(m, mt2);  // the old max joins the rest when it moves
       // the new argmax stays out of P: its logit becomes -inf (p = 0) in the lane holding it
 #pragma unroll
       for (int e = 0; e < 32; ++e) tv[e] = (e == jr) ? -INFINITY : tv[e];
+      // tile max without the new argmax (the lane holding it lost that element above)
+      float l2 = tv[0];
+#pragma unroll
+      for (int e = 1; e < 32; ++e) l2 = fmaxf(l2, tv[e]);
+      const float mt2 = row_max(moved ? l2 : -INFINITY);
+      if (moved) cand = fmaxf(m, mt2);  // the old max joins the rest when it moves
     }
     const bool upd = cand * c1s > m2 * c1s + kSlack;  // -inf references always move
     const float m2n = upd ? cand : m2;
@@ -342,13 +341,13 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       // row with weight exp2(c1 (m - m2n)) (2^14 scaled), in one pass over the accumulators
       const float alpha = upd ? ((m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m2 - m2n) * c1s)) : 1.f;
       const float wold = fold ? kPScale * __builtin_amdgcn_exp2f((m - m2n) * c1s) : 0.f;
-      lrest = fmaf(lrest, alpha, wold);
+      lrest = fmaf(lrest, alpha, h == 0 ? wold : 0.f);  // the lane's half of the row sum
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[db][4 * qq + e] = fmaf(o[db][4 * qq + e], alpha, wold * (float)vs[db][qq][e]);
+          for (int e = 0; e < 4; ++e) o[db][4 * qq + e] = fmaf((float)vs[db][qq][e], wold, o[db][4 * qq + e] * alpha);
       }
       if (moved) {
         const int jslot = jt - trel;  // new argmax's key in this tile
@@ -395,7 +394,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       if (ks == 1) hook(std::integral_constant<int, 3>{});
       if (ks == 3) hook(std::integral_constant<int, 4>{});
     }
-    lrest += ts + wave_shfl_xor_f(ts, 32);
+    lrest += ts;
   };
 
   // Ring schedule (one barrier per tile). Iteration t: after the barrier, buffer (t+3)%4
@@ -460,6 +459,10 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       *(float4*)&Ob[(size_t)row_t * D + 32 * db + 8 * qq + 4 * h] = w4;
       *(f16x4*)&Vb[(size_t)row_t * D + 32 * db + 8 * qq + 4 * h] = vs[db][qq];
     }
+  {
+    const HalfPair lp = wave_halves(lrest);  // the row's two half sums
+    lrest = lp.lo + lp.hi;
+  }
   if (h == 0) {
     Mb[row_t] = m * c1s;  // log2 units from here on
     M2b[row_t] = m2 * c1s;

@@ -37,6 +37,22 @@ __device__ inline unsigned lds_offset(const void* p) { return (unsigned)(size_t)
 // global stores or loads in flight (__syncthreads' release fence waits for all of them)
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// The values of x in lanes i % 32 (lo) and i % 32 + 32 (hi), for lane i: one
+// v_permlane32_swap, a VALU exchange of the wave's halves with no LDS round trip (a
+// ds_bpermute's wait would also wait for every LDS read issued before it). A reduction
+// over (lo, hi) gives the same bits in both lanes of a pair.
+struct HalfPair {
+  float lo, hi;
+};
+__device__ inline HalfPair wave_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ inline int wave_halves_min(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return min((int)r[0], (int)r[1]);
+}
+
 constexpr int kMaxSeqs = 64;
 constexpr int kRowsPerTileMax = 256;  // query rows one workgroup holds (8 waves x 32 rows)
 constexpr int kMergeChunk = 4096;     // tokens per merge workgroup

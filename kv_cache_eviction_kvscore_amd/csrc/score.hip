@@ -217,6 +217,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
         ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
       }
     }
+    // a shuffle here, not a VALU exchange chain: this side work is off the MFMA path, and
+    // the dependent DPP / permlane steps measured slower than LDS shuffles in flight
 #pragma unroll
     for (int off = KPW; off < 64; off <<= 1) ss += __shfl_xor(ss, off, 64);
     const Split3 sp = split3(-0.5f * ss);
@@ -450,7 +452,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
 #pragma unroll
           for (int pi = 0; pi < 16; pi += PPR) pair_terms(F_{}, acc, pi, key, col);
         }
-        col += __shfl_xor(col, 32, 64);  // both half-waves hold the sum and write it
+        {
+          const HalfPair c2 = wave_halves(col);  // both half-waves hold the sum and write it
+          col = c2.lo + c2.hi;
+        }
         sm.red[t % 3][wave][b * KB + l32] = col;
       }
     }
