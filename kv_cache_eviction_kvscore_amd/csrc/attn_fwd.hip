@@ -199,14 +199,30 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
   };
   // V of tile it from bf16 to fp16, in place: each lane converts the chunks its own DMA
   // instructions wrote, so it needs only its own loads to have landed
+  // (instruction i of a wave moves V exactly when i >= NLD / 2: f = i * NWAVES + wave is
+  // then in [IPT, 2 * IPT))
   auto convert_own = [&](int it) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
+    for (int i = NLD / 2; i < NLD; ++i) {
       const int f = i * NWAVES + wave;
-      if (f / IPT == 1) {
-        u32x4* c = (u32x4*)&sm.tile[it % NBUF][1][((f % IPT) * 64 + lane) * 8];
-        *c = bf16x8_to_f16x8(*c);
-      }
+      u32x4* c = (u32x4*)&sm.tile[it % NBUF][1][((f % IPT) * 64 + lane) * 8];
+      *c = bf16x8_to_f16x8(*c);
+    }
+  };
+  // the same in two halves, so the LDS reads' latency passes under MFMAs in between
+  u32x4 cvt[NLD / 2];
+  auto convert_read = [&](int it) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = NLD / 2; i < NLD; ++i) {
+      const int f = i * NWAVES + wave;
+      cvt[i - NLD / 2] = *(const u32x4*)&sm.tile[it % NBUF][1][((f % IPT) * 64 + lane) * 8];
+    }
+  };
+  auto convert_write = [&](int it) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = NLD / 2; i < NLD; ++i) {
+      const int f = i * NWAVES + wave;
+      *(u32x4*)&sm.tile[it % NBUF][1][((f % IPT) * 64 + lane) * 8] = bf16x8_to_f16x8(cvt[i - NLD / 2]);
     }
   };
   auto issue_any = [&](int it) __attribute__((always_inline)) {
@@ -275,6 +291,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], acc1, 0, 0, 0);
       if (kk == 0) hook(std::integral_constant<int, 0>{});
+      if (kk == 1) hook(std::integral_constant<int, 5>{});
       if (kk == NKK / 2) hook(std::integral_constant<int, 1>{});
       __builtin_amdgcn_sched_barrier(0);
       k0 = k0n;
@@ -402,9 +419,10 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
   // own loads of tile t+1 (tiles t+2 and the part of t+3 issued so far stay in flight) and
   // converts its share of that tile's V, which the next barrier publishes. Three tiles are
   // in flight while one is computed. A computing wave spreads its DMA instructions over
-  // the tile's MFMA phases (half with the S^T chain, half with the O^T chain) and converts
-  // between them: issued all at once by every wave they back up in the address unit.
-  constexpr int NS = NLD / 2;  // instructions of tile t+3 issued before the wait for t+1
+  // the tile's MFMA phases (half with the S^T chain, half with the O^T chain): issued all
+  // at once by every wave they back up in the address unit. It reads its V share of tile
+  // t+1 at the second k-step of the S^T chain and writes it back converted after the
+  // chain, so the LDS round trip runs under the MFMAs.
   issue(0);
   if (ntiles > 1) issue_any(1);
   if (ntiles > 2) issue_any(2);
@@ -424,9 +442,19 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
     };
     if (computing) {
       compute_tile(t, [&](auto pc) __attribute__((always_inline)) {
-        constexpr int point = decltype(pc)::value;  // 0, 1: S^T chain; 2: after it; 3, 4: O^T chain
-        if constexpr (point == 2) {
-          wait_convert_next(std::integral_constant<int, NS>{});
+        // 0, 5, 1: S^T chain (k-steps 0, 1, NKK/2); 2: after it; 3, 4: O^T chain
+        constexpr int point = decltype(pc)::value;
+        if constexpr (point == 5) {
+          // this lane's loads of tile t+1 (t+2 and the one instruction of t+3 issued at
+          // point 0 may stay in flight), then its share of that tile's V read for conversion
+          if (more1) {
+            if (more3) vm_wait<NLD + 1>();
+            else if (more2) vm_wait<NLD>();
+            else vm_wait<0>();
+            convert_read(t + 1);
+          }
+        } else if constexpr (point == 2) {
+          if (more1) convert_write(t + 1);
         } else if (more3) {
           if constexpr (NLD == 4) {
             constexpr int i = point < 2 ? point : point - 1;
