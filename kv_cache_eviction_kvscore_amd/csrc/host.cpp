@@ -33,6 +33,11 @@ int ok() {
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
+// MI355X compute units, and the measured cost of one more round of forward workgroups per
+// CU, in keys of one unit's chunk (the prologue, the running max's warm-up, the record)
+constexpr int64_t kNumCUs = 256;
+constexpr int64_t kFwdChunkCost = 4096;
+
 int64_t next_pow2(int64_t x) {
   int64_t r = 1;
   while (r < x) r <<= 1;
@@ -97,17 +102,41 @@ int make_dev(const kvscore_problem* p, kvs::Dev& d) {
   d.U = d.L * d.S * d.Hkv;
   d.max_n = max_n;
   for (int s = 0; s <= p->num_seqs; ++s) d.cu[s] = p->cu_seqlens[s];
-  // Chunk sizes. The forward restarts its running max in every chunk (a warm-up where
-  // many rows' argmax moves), and one of its workgroups fills a CU: aim at ~2 chunks per
-  // CU. The score pass keeps no running state: ~8 chunks per CU for balance.
+  // Chunk sizes. The score pass keeps no running state: ~8 chunks per CU for balance.
   int64_t keys = 0;
   for (int s = 0; s < p->num_seqs; ++s) keys += (p->cu_seqlens[s + 1] - p->cu_seqlens[s]);
-  keys *= (int64_t)d.L * d.Hkv * d.Tq;
+  const int64_t groups_per_seq = (int64_t)d.L * d.Hkv * d.Tq;
+  keys *= groups_per_seq;
   auto chunk_for = [&](int64_t groups) {
     return (int)std::min<int64_t>(65536, std::max<int64_t>(1024, next_pow2((keys + groups - 1) / groups)));
   };
-  d.fwd_chunk = chunk_for(512);
   d.score_chunk = chunk_for(2048);
+  // One forward workgroup fills a CU, and every chunk restarts its running max (a warm-up
+  // in which many rows' argmax moves) and adds a record to combine. The chunk (a power of
+  // two of 1024 keys or more) minimises an estimated makespan in keys: rounds x chunk when
+  // every workgroup has the same length, else keys per CU + half a chunk of tail; plus
+  // kFwdChunkCost per round of workgroups.
+  {
+    int64_t best = -1, best_c = 1024;
+    for (int64_t c = 1024; c <= std::max<int64_t>(1024, next_pow2(max_n)); c *= 2) {
+      int64_t nwg = 0, lo = INT64_MAX, hi = 0;
+      for (int s = 0; s < p->num_seqs; ++s) {
+        const int64_t n = p->cu_seqlens[s + 1] - p->cu_seqlens[s];
+        nwg += (n + c - 1) / c;
+        if (n >= c) lo = std::min(lo, c), hi = std::max(hi, c);
+        if (n % c) lo = std::min(lo, n % c), hi = std::max(hi, n % c);
+      }
+      nwg *= groups_per_seq;
+      const int64_t rounds = (nwg + kNumCUs - 1) / kNumCUs, ce = std::min(c, max_n);
+      const int64_t span = (lo == hi) ? rounds * ce : std::max((keys + kNumCUs - 1) / kNumCUs, ce) + ce / 2;
+      const int64_t cost = span + kFwdChunkCost * rounds;
+      if (best < 0 || cost <= best) {  // ties go to the longer chunk
+        best = cost;
+        best_c = c;
+      }
+    }
+    d.fwd_chunk = (int)best_c;
+  }
   d.fwd_chunks = (int)((max_n + d.fwd_chunk - 1) / d.fwd_chunk);
   d.score_chunks = (int)((max_n + d.score_chunk - 1) / d.score_chunk);
   return ok();
