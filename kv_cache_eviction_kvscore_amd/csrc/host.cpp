@@ -33,10 +33,13 @@ int ok() {
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
-// MI355X compute units, and the measured cost of one more round of forward workgroups per
-// CU, in keys of one unit's chunk (the prologue, the running max's warm-up, the record)
+// MI355X compute units, and the measured cost of one more round of workgroups per CU, in
+// keys of one unit's chunk, for the forward (prologue, the running max's warm-up, one more
+// record) and the score pass (prologue); the score kernel's tile flags cap its chunk
 constexpr int64_t kNumCUs = 256;
 constexpr int64_t kFwdChunkCost = 4096;
+constexpr int64_t kScoreChunkCost = 512;
+constexpr int64_t kScoreMaxChunk = 65536;
 
 int64_t next_pow2(int64_t x) {
   int64_t r = 1;
@@ -102,23 +105,19 @@ int make_dev(const kvscore_problem* p, kvs::Dev& d) {
   d.U = d.L * d.S * d.Hkv;
   d.max_n = max_n;
   for (int s = 0; s <= p->num_seqs; ++s) d.cu[s] = p->cu_seqlens[s];
-  // Chunk sizes. The score pass keeps no running state: ~8 chunks per CU for balance.
+  // Chunk sizes: a power of two of 1024 keys or more that minimises an estimated makespan
+  // in keys: rounds x chunk when every workgroup has the same length, else keys per CU +
+  // half a chunk of tail; plus a fixed cost per round of workgroups. One workgroup of
+  // either pass fills a CU. A forward chunk restarts its running max (a warm-up in which
+  // many rows' argmax moves) and adds a record to combine; a score chunk only reloads its
+  // row operands.
   int64_t keys = 0;
   for (int s = 0; s < p->num_seqs; ++s) keys += (p->cu_seqlens[s + 1] - p->cu_seqlens[s]);
   const int64_t groups_per_seq = (int64_t)d.L * d.Hkv * d.Tq;
   keys *= groups_per_seq;
-  auto chunk_for = [&](int64_t groups) {
-    return (int)std::min<int64_t>(65536, std::max<int64_t>(1024, next_pow2((keys + groups - 1) / groups)));
-  };
-  d.score_chunk = chunk_for(2048);
-  // One forward workgroup fills a CU, and every chunk restarts its running max (a warm-up
-  // in which many rows' argmax moves) and adds a record to combine. The chunk (a power of
-  // two of 1024 keys or more) minimises an estimated makespan in keys: rounds x chunk when
-  // every workgroup has the same length, else keys per CU + half a chunk of tail; plus
-  // kFwdChunkCost per round of workgroups.
-  {
+  auto pick_chunk = [&](int64_t round_cost, int64_t cap) {
     int64_t best = -1, best_c = 1024;
-    for (int64_t c = 1024; c <= std::max<int64_t>(1024, next_pow2(max_n)); c *= 2) {
+    for (int64_t c = 1024; c <= std::min(cap, std::max<int64_t>(1024, next_pow2(max_n))); c *= 2) {
       int64_t nwg = 0, lo = INT64_MAX, hi = 0;
       for (int s = 0; s < p->num_seqs; ++s) {
         const int64_t n = p->cu_seqlens[s + 1] - p->cu_seqlens[s];
@@ -129,14 +128,16 @@ int make_dev(const kvscore_problem* p, kvs::Dev& d) {
       nwg *= groups_per_seq;
       const int64_t rounds = (nwg + kNumCUs - 1) / kNumCUs, ce = std::min(c, max_n);
       const int64_t span = (lo == hi) ? rounds * ce : std::max((keys + kNumCUs - 1) / kNumCUs, ce) + ce / 2;
-      const int64_t cost = span + kFwdChunkCost * rounds;
+      const int64_t cost = span + round_cost * rounds;
       if (best < 0 || cost <= best) {  // ties go to the longer chunk
         best = cost;
         best_c = c;
       }
     }
-    d.fwd_chunk = (int)best_c;
-  }
+    return (int)best_c;
+  };
+  d.fwd_chunk = pick_chunk(kFwdChunkCost, INT64_MAX);
+  d.score_chunk = pick_chunk(kScoreChunkCost, kScoreMaxChunk);
   d.fwd_chunks = (int)((max_n + d.fwd_chunk - 1) / d.fwd_chunk);
   d.score_chunks = (int)((max_n + d.score_chunk - 1) / d.score_chunk);
   return ok();
