@@ -32,7 +32,7 @@ KERNEL_SOURCES = {"score": "score.hip", "attn_fwd": "attn_fwd.hip", "compact": "
                   "topk": "topk.hip", "merge": "merge.hip", "decode": "decode.hip"}
 # the kernels (by name fragment) that make up each call, for counter records
 CALL_KERNELS = {"attn_fwd": ("fwd_partial_kernel", "fwd_combine_kernel"), "score": ("score_prep_kernel", "score_kernel"),
-                "merge": ("merge_kernel",), "topk": ("topk_kernel",), "compact": ("compact_kernel",),
+                "merge": ("merge_sum_kernel", "merge_isolated_kernel"), "topk": ("topk_kernel",), "compact": ("compact_kernel",),
                 "decode": ("decode_partial_kernel", "decode_combine_kernel")}
 
 

@@ -55,7 +55,7 @@ __device__ inline int wave_halves_min(int x) {
 
 constexpr int kMaxSeqs = 64;
 constexpr int kRowsPerTileMax = 256;  // query rows one workgroup holds (8 waves x 32 rows)
-constexpr int kMergeChunk = 4096;     // tokens per merge workgroup
+constexpr int kMergeChunk = 8192;     // tokens per merge workgroup
 constexpr int kCompactRows = 32;      // packed rows per compaction workgroup
 
 // Problem as the kernels see it (passed by value as a kernel argument).
