@@ -79,22 +79,56 @@ struct SelectSmem {
   long long red[2][NWAVES];
 };
 
+// LDS list of the keys that share the threshold's top byte, so the last two radix passes
+// need not read global memory again
+constexpr int kCandCap = 12288;
+struct CandSmem {
+  unsigned key[kCandCap];
+  unsigned n;
+};
+
 // Radix select of the kr-th largest key among the keys `visit` enumerates (each thread
-// calls f(key) on its share): T = that key, need_eq = how many keys equal to T are among
-// the kr largest. 4 passes of 8 bits; per-wave LDS histograms merged in wave order; the
-// digit is found by a wave scan.
+// calls f(key) on its share, all lanes of a wave together): T = that key, need_eq = how
+// many keys equal to T are among the kr largest. 4 passes of 8 bits; per-wave LDS
+// histograms merged in wave order; the digit is found by a wave scan. With cs, the second
+// pass also appends the keys whose top byte is the threshold's to cs when they fit, and
+// the third and fourth passes read that list instead (the counts, so T and need_eq, do
+// not depend on the list's order).
 template <class Visit>
-__device__ void radix_select(SelectSmem& sm, Visit visit, int64_t kr, unsigned& T, int64_t& need_eq) {
+__device__ void radix_select(SelectSmem& sm, Visit visit, int64_t kr, unsigned& T, int64_t& need_eq,
+                             CandSmem* cs = nullptr) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   unsigned prefix = 0, pmask = 0;
+  bool listed = false;  // uniform: the third and fourth passes read cs
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < NWAVES * 256; i += NT) (&sm.whist[0][0])[i] = 0;
+    const bool collect = cs && pass == 1 && sm.hist[prefix >> 24] <= (unsigned)kCandCap;
+    if (collect && tid == 0) cs->n = 0;
     __syncthreads();
-    visit([&](unsigned key) {
+    auto count = [&](unsigned key) {
       if ((key & pmask) == prefix) atomicAdd(&sm.whist[wave][(key >> shift) & 255u], 1u);
-    });
+    };
+    if (listed) {
+      for (int i = tid; i < (int)cs->n; i += NT) count(cs->key[i]);
+    } else if (collect) {
+      visit([&](unsigned key) {
+        const bool in = (key & pmask) == prefix;
+        if (in) atomicAdd(&sm.whist[wave][(key >> shift) & 255u], 1u);
+        // one slot reservation per wave, then each lane writes at its rank among the wave's
+        const unsigned long long m = __ballot(in);
+        if (m) {
+          unsigned base = 0;
+          if (lane == __ffsll((long long)m) - 1) base = atomicAdd(&cs->n, (unsigned)__popcll(m));
+          base = __shfl(base, __ffsll((long long)m) - 1, 64);
+          if (in) cs->key[base + __popcll(m & ((1ull << lane) - 1))] = key;
+        }
+      });
+    } else {
+      visit(count);
+    }
     __syncthreads();
+    listed = listed || collect;
     if (tid < 256) {
       unsigned c = 0;
       for (int w = 0; w < NWAVES; ++w) c += sm.whist[w][tid];
@@ -219,10 +253,31 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
   const int sel = (k == 0) ? 0 : (k == cand - ns ? 1 : 2);
   unsigned T = 0;
   int64_t need_eq = 0;
-  if (sel == 2)
+  if (sel == 2) {
+    __shared__ CandSmem cs;
+    const float* c0 = sc + ns;
+    const int64_t m = cand - ns;
     radix_select(sm, [&](auto f) {
-      for (int64_t j = ns + tid; j < cand; j += NT) f(f2key(sc[j]));
-    }, k, T, need_eq);
+      int64_t j0 = 0;
+      if ((((size_t)c0) & 15) == 0) {  // 16-byte loads, two in flight per thread
+        const int64_t m8 = m / (8 * NT) * (8 * NT);
+        for (int64_t j = 4 * tid; j < m8; j += 8 * NT) {
+          const float4 x = *(const float4*)(c0 + j);
+          const float4 y = *(const float4*)(c0 + j + 4 * NT);
+          f(f2key(x.x));
+          f(f2key(x.y));
+          f(f2key(x.z));
+          f(f2key(x.w));
+          f(f2key(y.x));
+          f(f2key(y.y));
+          f(f2key(y.z));
+          f(f2key(y.w));
+        }
+        j0 = m8;
+      }
+      for (int64_t j = j0 + tid; j < m; j += NT) f(f2key(c0[j]));
+    }, k, T, need_eq, &cs);
+  }
   emit_segment(sm, kept + off0, b, sel, T, need_eq, sc, n, cand, ns);
 }
 

@@ -1,0 +1,62 @@
+"""Per-unit selection on hand-made scores: GPU vs the oracle's full sort.
+
+DropKV page, "Methodology in Plain English": keep the largest scores, the recent window
+always. The selection is integer work decided on the same fp32 values on both sides, so
+every segment must equal the oracle's (a full sort on (-score, position)) exactly.
+
+The score distributions steer the radix select down both of its routes: when at most
+12288 keys share the threshold's top byte, its last two passes read an LDS list of them;
+otherwise they read the scores again. Covered: a log-uniform spread (the list), one top
+byte for every key (uniform in [2, 8)), sixteen distinct values (ties decided by position)
+in a bin too large for the list and in one that fits, all keys equal, and budgets keeping
+every competitor or none.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_eviction_kvscore_amd import api
+from parity import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _scores(kind, n, rng):
+    if kind == "log_uniform":
+        return np.exp2(rng.uniform(-60.0, 0.0, n)).astype(np.float32)
+    if kind == "one_top_byte":
+        return rng.uniform(2.0, 8.0, n).astype(np.float32)
+    if kind == "sixteen_values":
+        return (2.0 + 0.25 * rng.integers(0, 16, n)).astype(np.float32)
+    if kind == "all_equal":
+        return np.full(n, 3.0, dtype=np.float32)
+    if kind == "ties_in_list":  # a threshold bin of 8000 keys with sixteen values, over a wide spread
+        x = np.exp2(rng.uniform(-60.0, 0.0, n)).astype(np.float32)
+        x[rng.choice(n, 8000, replace=False)] = (2.0 + 0.25 * rng.integers(0, 16, 8000)).astype(np.float32)
+        return x
+    raise ValueError(kind)
+
+
+KINDS = ["log_uniform", "one_top_byte", "sixteen_values", "all_equal", "ties_in_list"]
+
+
+@pytest.mark.parametrize("budget_extra", [5000, 0, 70000])
+def test_topk_threshold_bins_both_routes(budget_extra):
+    L, S, Hkv, Hq, d, W = 1, 1, len(KINDS), len(KINDS), 128, 16
+    n = 60011  # ragged against the 4-key loads
+    rng = np.random.default_rng(budget_extra + 5)
+    p = api.Problem(num_seqs=S, num_layers=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, window=W,
+                    cu_seqlens=[0, n], k_strides=(Hkv * n * d, n * d, d), v_strides=(Hkv * n * d, n * d, d))
+    sc = np.stack([_scores(kind, n, rng) for kind in KINDS])  # [Hkv][n]
+    b = min(W + budget_extra, n)
+    budgets = np.full((S, L), b, dtype=np.int32)
+    off = api.segment_offsets(p, budgets)
+    kept = torch.full((int(off[-1]),), -7, dtype=torch.int32, device="cuda")
+    say(f"top-k on hand-made scores: n={n}, budget {b}, kinds {KINDS}")
+    api.topk(p, torch.from_numpy(sc.reshape(-1)).cuda(), budgets, torch.from_numpy(off).cuda(), kept)
+    torch.cuda.synchronize()
+    got = kept.cpu().numpy()
+    for g, kind in enumerate(KINDS):
+        ref = oracle.kept_positions(sc[g].astype(np.float64), n, W, b)
+        np.testing.assert_array_equal(got[off[g]:off[g + 1]], ref, err_msg=kind)
