@@ -79,8 +79,8 @@ struct SelectSmem {
   long long red[2][NWAVES];
 };
 
-// LDS list of the keys that share the threshold's top byte, so the last two radix passes
-// need not read global memory again
+// LDS list of the keys that share the threshold's top byte (or top two bytes), so the
+// last radix passes need not read global memory again
 constexpr int kCandCap = 12288;
 struct CandSmem {
   unsigned key[kCandCap];
@@ -91,9 +91,9 @@ struct CandSmem {
 // calls f(key) on its share, all lanes of a wave together): T = that key, need_eq = how
 // many keys equal to T are among the kr largest. 4 passes of 8 bits; per-wave LDS
 // histograms merged in wave order; the digit is found by a wave scan. With cs, the second
-// pass also appends the keys whose top byte is the threshold's to cs when they fit, and
-// the third and fourth passes read that list instead (the counts, so T and need_eq, do
-// not depend on the list's order).
+// or else the third pass also appends the keys that share the threshold's prefix so far
+// (its top byte, or its top two) to cs when they fit, and the later passes read that list
+// instead (the counts, so T and need_eq, do not depend on the list's order).
 template <class Visit>
 __device__ void radix_select(SelectSmem& sm, Visit visit, int64_t kr, unsigned& T, int64_t& need_eq,
                              CandSmem* cs = nullptr) {
@@ -103,7 +103,8 @@ __device__ void radix_select(SelectSmem& sm, Visit visit, int64_t kr, unsigned& 
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < NWAVES * 256; i += NT) (&sm.whist[0][0])[i] = 0;
-    const bool collect = cs && pass == 1 && sm.hist[prefix >> 24] <= (unsigned)kCandCap;
+    // keys with the current prefix: the last pass's count of its digit
+    const bool collect = cs && !listed && (pass == 1 || pass == 2) && sm.hist[sm.s_digit] <= (unsigned)kCandCap;
     if (collect && tid == 0) cs->n = 0;
     __syncthreads();
     auto count = [&](unsigned key) {
