@@ -79,18 +79,17 @@ __global__ __launch_bounds__(256) void merge_isolated_kernel(Dev p, const int32_
   const int64_t n = p.cu[s + 1] - p.cu[s];
   for (int r = tid; r < p.R; r += 256) {
     const int jj = js[r];
-    if (jj < 0 || jj >= n) continue;  // no argmax (or none in the sequence): nothing to add
-    bool first = true;
-    for (int r2 = 0; r2 < r; ++r2)
-      if (js[r2] == jj) {
-        first = false;
-        break;
-      }
-    if (!first) continue;
-    // branchless over LDS, so the loads pipeline (a unit's rows often share one argmax)
+    // one pass over all rows, the same for every lane (so the LDS reads pipeline): whether
+    // an earlier row has this argmax (then that row writes), and the sum over this row and
+    // the later ones that have it, in row order
+    bool earlier = false;
     float a1 = 0.f;
-    for (int r2 = r; r2 < p.R; ++r2) a1 += (js[r2] == jj) ? ds[r2] : 0.f;
-    out[jj] += a1;
+    for (int r2 = 0; r2 < p.R; ++r2) {
+      const bool same = js[r2] == jj;
+      earlier |= same && r2 < r;
+      a1 += (same && r2 >= r) ? ds[r2] : 0.f;
+    }
+    if (!earlier && jj >= 0 && jj < n) out[jj] += a1;  // no argmax in the sequence: nothing to add
   }
 }
 
