@@ -518,6 +518,52 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
   auto stat = [&](int c, int which) { return block(c) + (size_t)p.RT * D + (size_t)p.RT * D / 2 + which * p.RT + row_t; };
 
   // stat(c, 0) = m (max), 1 = m2 (max of the rest), 2 = l_rest (relative to m2), 3 = j*
+  const size_t ro = (size_t)u * p.R + row;
+  if (nch == 1) {
+    // one chunk (uniform): every load of the row at once, then the arithmetic of the
+    // general path below with win = 0, M2 = m2, w2 = 1 and no other chunk
+    const float M = *stat(0, 0), M2 = *stat(0, 1), lr = *stat(0, 2);
+    const int j0 = *(const int*)stat(0, 3);
+    const float* Oc = block(0) + (size_t)row_t * D;
+    const _Float16* Vc = (const _Float16*)(block(0) + (size_t)p.RT * D) + (size_t)row_t * D;
+    float o[PER], vs[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      o[i] = Oc[lane + 64 * i];
+      vs[i] = (float)Vc[lane + 64 * i];
+    }
+    if (j0 < 0) {  // no visible key recorded (cannot happen for valid shapes: key 0 is always visible)
+      for (int e = lane; e < D; e += 64) a[ro * D + e] = 0.f;
+      if (lane == 0) {
+        dom[ro] = 0.f;
+        lse[ro] = -INFINITY;
+        jstar[ro] = -1;
+      }
+      return;
+    }
+    const float w2 = (M2 == -INFINITY) ? 0.f : 1.f;
+    const float lrs = w2 * lr;
+    const float rel = (M2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M2 - M);
+    const float lt = rel * lrs;
+    const float pstar = 1.f / (1.f + lt);
+    float d2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const float acc = w2 * o[i];
+      a[ro * D + lane + 64 * i] = (rel * acc + vs[i]) * pstar;
+      const float df = (lrs > 0.f ? acc / lrs : vs[i]) - vs[i];
+      d2 += df * df;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) d2 += __shfl_xor(d2, off, 64);
+    if (lane == 0) {
+      const float shift = pstar * sqrtf(d2);
+      dom[ro] = (p.mode == 1) ? shift * shift : (p.mode == 2 ? pstar : shift);
+      lse[ro] = (M + __log2f(1.f + lt)) * 0.69314718055994531f;
+      jstar[ro] = j0;
+    }
+    return;
+  }
   float M = -INFINITY;
   int win = -1;
   for (int c = 0; c < nch; ++c) {
@@ -528,7 +574,6 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
       win = c;
     }
   }
-  const size_t ro = (size_t)u * p.R + row;
   if (win < 0) {  // no visible key recorded (cannot happen for valid shapes: key 0 is always visible)
     for (int e = lane; e < D; e += 64) a[ro * D + e] = 0.f;
     if (lane == 0) {
