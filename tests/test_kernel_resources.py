@@ -1,0 +1,53 @@
+"""Compiled resources of the HIP kernels, without a GPU.
+
+Every kernel is compiled for gfx950 with the library's own flags and the compiler's
+per-kernel resource report is read: no kernel may spill to scratch memory, and the kernels
+of the two streaming passes (512 threads, two waves per SIMD) must fit a wave in 256
+registers (VGPRs + AGPRs) and a workgroup in the CU's 160 KB of LDS. A change that breaks
+one of these still computes the right values, so the parity tests would not notice.
+"""
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+from kv_cache_eviction_kvscore_amd import build as kbuild
+
+SOURCES = sorted(glob.glob(os.path.join(kbuild.CSRC, "*.hip")))
+
+
+def resources(src):
+    cmd = [kbuild.HIPCC] + kbuild.CFLAGS + kbuild.EXTRA.get(os.path.basename(src), []) + [
+        "--cuda-device-only", "-c", src, "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out, cur = {}, None
+    for line in r.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            out[cur] = {}
+            continue
+        m = re.search(r"remark: ([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+)", line)
+        if m and cur:
+            out[cur][m.group(1).strip()] = int(m.group(2))
+    assert out, "no resource report"
+    return out
+
+
+@pytest.mark.parametrize("src", SOURCES, ids=[os.path.basename(s) for s in SOURCES])
+def test_no_kernel_spills(src):
+    for fn, r in resources(src).items():
+        assert r.get("ScratchSize", 0) == 0, (fn, r)
+
+
+@pytest.mark.parametrize("name", ["attn_fwd.hip", "score.hip"])
+def test_streaming_kernels_fit_two_waves_per_simd(name):
+    rep = resources(os.path.join(kbuild.CSRC, name))
+    main = {fn: r for fn, r in rep.items() if "fwd_partial_kernel" in fn or "score_kernel" in fn}
+    assert main
+    for fn, r in main.items():
+        assert r["VGPRs"] + r.get("AGPRs", 0) <= 256, (fn, r)
+        assert r["LDS Size"] <= 160 * 1024, (fn, r)
