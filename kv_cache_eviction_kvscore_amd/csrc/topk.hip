@@ -41,6 +41,21 @@ __device__ inline int wave_incl_scan(int x, int lane) {
   return x;
 }
 
+// h[bin] += 1 for every lane with in set. When those lanes share one bin (most of a radix
+// pass's first digit falls in a single bin), one lane adds their count: 64 atomics on one
+// LDS address would serialise.
+__device__ inline void hist_add(unsigned* h, bool in, unsigned bin) {
+  const unsigned long long m = __ballot(in);
+  if (!m) return;
+  const int first = __ffsll((long long)m) - 1;  // uniform
+  const unsigned b0 = (unsigned)__builtin_amdgcn_readlane((int)bin, first);
+  if (__ballot(in && bin == b0) == m) {
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&h[b0], (unsigned)__popcll(m));
+  } else if (in) {
+    atomicAdd(&h[bin], 1u);
+  }
+}
+
 constexpr int PT = 4096;  // tokens per pooling workgroup
 constexpr int kMaxPool = 255;
 
@@ -107,15 +122,13 @@ __device__ void radix_select(SelectSmem& sm, Visit visit, int64_t kr, unsigned& 
     const bool collect = cs && !listed && (pass == 1 || pass == 2) && sm.hist[sm.s_digit] <= (unsigned)kCandCap;
     if (collect && tid == 0) cs->n = 0;
     __syncthreads();
-    auto count = [&](unsigned key) {
-      if ((key & pmask) == prefix) atomicAdd(&sm.whist[wave][(key >> shift) & 255u], 1u);
-    };
+    auto count = [&](unsigned key) { hist_add(sm.whist[wave], (key & pmask) == prefix, (key >> shift) & 255u); };
     if (listed) {
       for (int i = tid; i < (int)cs->n; i += NT) count(cs->key[i]);
     } else if (collect) {
       visit([&](unsigned key) {
         const bool in = (key & pmask) == prefix;
-        if (in) atomicAdd(&sm.whist[wave][(key >> shift) & 255u], 1u);
+        hist_add(sm.whist[wave], in, (key >> shift) & 255u);
         // one slot reservation per wave, then each lane writes at its rank among the wave's
         const unsigned long long m = __ballot(in);
         if (m) {
@@ -351,9 +364,24 @@ __global__ __launch_bounds__(NT) void heads_hist_kernel(Dev p, const float* __re
   for (int i = tid; i < NWAVES * 256; i += NT) (&wh[0][0])[i] = 0;
   __syncthreads();
   const float* sc = score + (int64_t)(l * p.Hkv + g) * p.N + p.cu[s];
-  for (int64_t j = j0 + tid; j < j1; j += NT) {
-    const unsigned key = f2key(sc[j]);
-    if ((key & pmask) == (x.prefix & pmask)) atomicAdd(&wh[wave][(key >> shift) & 255u], 1u);
+  auto count = [&](float v) __attribute__((always_inline)) {
+    const unsigned key = f2key(v);
+    hist_add(wh[wave], (key & pmask) == (x.prefix & pmask), (key >> shift) & 255u);
+  };
+  static_assert(HCH == 8 * NT, "eight keys per thread");
+  const int64_t jt = j0 + 8 * tid;
+  if (j1 - j0 == HCH && (((size_t)(sc + j0)) & 15) == 0) {  // a whole aligned chunk: 16-byte loads
+    const float4 a = *(const float4*)(sc + jt), b = *(const float4*)(sc + jt + 4);
+    count(a.x);
+    count(a.y);
+    count(a.z);
+    count(a.w);
+    count(b.x);
+    count(b.y);
+    count(b.z);
+    count(b.w);
+  } else {
+    for (int64_t j = j0 + tid; j < j1; j += NT) count(sc[j]);
   }
   __syncthreads();
   if (tid < 256) {
@@ -365,23 +393,35 @@ __global__ __launch_bounds__(NT) void heads_hist_kernel(Dev p, const float* __re
 
 // per group: sum the chunks' histograms (heads and chunks in ascending order) and place the
 // rank: the digit where the count from the top first reaches kr
-__global__ __launch_bounds__(256) void heads_digit_kernel(Dev p, HeadsState* __restrict__ st, int pass, int nch,
-                                                          const unsigned* __restrict__ whist) {
+__global__ __launch_bounds__(1024) void heads_digit_kernel(Dev p, HeadsState* __restrict__ st, int pass, int nch,
+                                                           const unsigned* __restrict__ whist) {
+  __shared__ unsigned part[4][256];
   __shared__ unsigned bins[256];
   __shared__ int s_digit;
   __shared__ long long s_above;
   const int grp = blockIdx.x;
   HeadsState x = st[grp];
   if (x.sel != 2) return;  // uniform
-  const int t = threadIdx.x;
+  // bin b of histogram i (i = head * nch + chunk) is summed by the threads b + 256q for
+  // q = i % 4; integer counts, so the order of the sums does not matter
+  const int t = threadIdx.x & 255, q = threadIdx.x >> 8;
+  const int nh = p.Hkv * nch;
+  const unsigned* h0 = whist + (int64_t)grp * nh * 256 + t;
   unsigned tot = 0;
-  for (int g = 0; g < p.Hkv; ++g) {
-    const unsigned* h = whist + (int64_t)(grp * p.Hkv + g) * nch * 256;
-    for (int c = 0; c < nch; ++c) tot += h[(int64_t)c * 256 + t];
+  int i = q;
+  for (; i + 28 < nh; i += 32) {  // eight loads in flight
+    unsigned v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = h0[(int64_t)(i + 4 * e) * 256];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tot += v[e];
   }
-  bins[t] = tot;
+  for (; i < nh; i += 4) tot += h0[(int64_t)i * 256];
+  part[q][t] = tot;
   __syncthreads();
-  if (t < 64) {
+  if (threadIdx.x < 256) bins[t] = part[0][t] + part[1][t] + part[2][t] + part[3][t];
+  __syncthreads();
+  if (threadIdx.x < 64) {
     // lane L owns digits 255-4L .. 252-4L (descending)
     unsigned c4[4], sum = 0;
 #pragma unroll
@@ -405,7 +445,7 @@ __global__ __launch_bounds__(256) void heads_digit_kernel(Dev p, HeadsState* __r
     }
   }
   __syncthreads();
-  if (t == 0) {
+  if (threadIdx.x == 0) {
     x.prefix |= (unsigned)s_digit << (24 - 8 * pass);
     x.kr -= s_above;
     if (pass == 3) x.need_eq = x.kr;
@@ -527,7 +567,7 @@ hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off,
   for (int pass = 0; pass < 4; ++pass) {
     hipLaunchKernelGGL(heads_hist_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, pass, nch,
                        whist);
-    hipLaunchKernelGGL(heads_digit_kernel, dim3(groups), dim3(256), 0, st, p, hs, pass, nch, (const unsigned*)whist);
+    hipLaunchKernelGGL(heads_digit_kernel, dim3(groups), dim3(1024), 0, st, p, hs, pass, nch, (const unsigned*)whist);
   }
   hipLaunchKernelGGL(heads_count_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, nch, cnt);
   hipLaunchKernelGGL(heads_emit_kernel, dim3(p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, nch,
