@@ -192,7 +192,6 @@ __device__ void emit_segment(SelectSmem& sm, int32_t* __restrict__ out, int64_t 
   int64_t sure_base = 0, eq_base = 0;
   for (int64_t base = 0; base < n; base += 4 * NT) {
     bool sure[4], tie[4];
-    int cs = 0, ce = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t j = base + 4 * tid + e;
@@ -209,16 +208,24 @@ __device__ void emit_segment(SelectSmem& sm, int32_t* __restrict__ out, int64_t 
           tie[e] = key == T;
         }
       }
-      cs += sure[e];
-      ce += tie[e];
     }
-    const int is = wave_incl_scan(cs, lane), ie = wave_incl_scan(ce, lane);
-    if (lane == 63) {
-      sm.wsum[0][wave] = is;
-      sm.wsum[1][wave] = ie;
+    // this lane's exclusive prefix over the wave and the wave's totals, from one ballot per
+    // element slot (the flags are bits: no shuffle chain through LDS)
+    int ps = 0, pe = 0, tws = 0, twe = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned long long ms = __ballot(sure[e]), me = __ballot(tie[e]);
+      ps += __builtin_amdgcn_mbcnt_hi((unsigned)(ms >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)ms, 0u));
+      pe += __builtin_amdgcn_mbcnt_hi((unsigned)(me >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)me, 0u));
+      tws += __popcll(ms);
+      twe += __popcll(me);
+    }
+    if (lane == 0) {
+      sm.wsum[0][wave] = tws;
+      sm.wsum[1][wave] = twe;
     }
     __syncthreads();
-    int ps = is - cs, pe = ie - ce, ts = 0, te = 0;
+    int ts = 0, te = 0;
     for (int w = 0; w < NWAVES; ++w) {
       if (w < wave) {
         ps += sm.wsum[0][w];
