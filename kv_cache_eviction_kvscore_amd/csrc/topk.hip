@@ -185,12 +185,36 @@ __device__ void radix_select(SelectSmem& sm, Visit visit, int64_t kr, unsigned& 
 // Ordered stream compaction of one segment (b rows at out): positions j in [0, n), kept
 // when j < ns or j >= cand (sinks, window), or by the selection: sel 0 none, 1 all,
 // 2 key > T and the first need_eq keys equal to T (ascending position). Rounds of 4096
-// positions; a block scan gives every kept position its slot.
+// positions; ballots and a sum over the waves give every kept position its slot.
 __device__ void emit_segment(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int sel, unsigned T,
                              int64_t need_eq, const float* __restrict__ sc, int64_t n, int64_t cand, int64_t ns) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the keys of a round are loaded one round ahead, 16 bytes per lane when aligned (the row
+  // holds n keys, so a load never leaves it)
+  const bool vec = (((size_t)sc) & 15) == 0;
+  auto load = [&](int64_t base, float* x) __attribute__((always_inline)) {
+    const int64_t j = base + 4 * tid;
+    if (sel != 2 || j >= n) return;
+    if (vec && j + 4 <= n) {
+      const float4 v = *(const float4*)(sc + j);
+      x[0] = v.x;
+      x[1] = v.y;
+      x[2] = v.z;
+      x[3] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j + e < n) x[e] = sc[j + e];
+    }
+  };
+  float nx[4] = {0.f, 0.f, 0.f, 0.f};
+  load(0, nx);
   int64_t sure_base = 0, eq_base = 0;
   for (int64_t base = 0; base < n; base += 4 * NT) {
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = nx[e];
+    load(base + 4 * NT, nx);
     bool sure[4], tie[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -203,7 +227,7 @@ __device__ void emit_segment(SelectSmem& sm, int32_t* __restrict__ out, int64_t 
         } else if (sel == 1) {
           sure[e] = true;
         } else if (sel == 2) {
-          const unsigned key = f2key(sc[j]);
+          const unsigned key = f2key(x[e]);
           sure[e] = key > T;
           tie[e] = key == T;
         }
