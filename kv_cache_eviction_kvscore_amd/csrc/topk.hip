@@ -189,8 +189,8 @@ __device__ void radix_select(SelectSmem& sm, Visit visit, int64_t kr, unsigned& 
 __device__ void emit_segment(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int sel, unsigned T,
                              int64_t need_eq, const float* __restrict__ sc, int64_t n, int64_t cand, int64_t ns) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  // the keys of a round are loaded one round ahead, 16 bytes per lane when aligned (the row
-  // holds n keys, so a load never leaves it)
+  // the keys of a round are loaded three rounds ahead, 16 bytes per lane when aligned (the
+  // row holds n keys, so a load never leaves it)
   const bool vec = (((size_t)sc) & 15) == 0;
   auto load = [&](int64_t base, float* x) __attribute__((always_inline)) {
     const int64_t j = base + 4 * tid;
@@ -207,14 +207,21 @@ __device__ void emit_segment(SelectSmem& sm, int32_t* __restrict__ out, int64_t 
         if (j + e < n) x[e] = sc[j + e];
     }
   };
-  float nx[4] = {0.f, 0.f, 0.f, 0.f};
-  load(0, nx);
+  // three rounds in flight: the emit is bound by the latency of its reads
+  float nx[3][4] = {};
+  load(0, nx[0]);
+  load(4 * NT, nx[1]);
+  load(8 * NT, nx[2]);
   int64_t sure_base = 0, eq_base = 0;
   for (int64_t base = 0; base < n; base += 4 * NT) {
     float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = nx[e];
-    load(base + 4 * NT, nx);
+    for (int e = 0; e < 4; ++e) {
+      x[e] = nx[0][e];
+      nx[0][e] = nx[1][e];
+      nx[1][e] = nx[2][e];
+    }
+    load(base + 12 * NT, nx[2]);
     bool sure[4], tie[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
