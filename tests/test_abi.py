@@ -93,6 +93,30 @@ def test_query_tiles_and_workspace_sizes():
     assert p2.workspace_size(api.WS_TOPK) == p2.num_layers * p2.num_kv_heads * p2.total_tokens * 4
 
 
+def test_forward_chunks_follow_the_makespan_estimate():
+    # the forward workspace holds one record block (196 RT floats at d = 128) per (unit,
+    # query tile, key chunk); the chunk is picked per problem, so its size shows the pick
+    block = 196 * 256 * 4
+
+    def fwd_chunks(L, Hkv, seqlens):
+        n = max(seqlens)
+        cu = [0] + list(np.cumsum(seqlens))
+        p = make_problem(num_layers=L, num_q_heads=4 * Hkv, num_kv_heads=Hkv, window=64, num_seqs=len(seqlens),
+                         cu_seqlens=cu, k_strides=(Hkv * cu[-1] * 128, cu[-1] * 128, 128),
+                         v_strides=(Hkv * cu[-1] * 128, cu[-1] * 128, 128))
+        U = L * len(seqlens) * Hkv
+        ws = p.workspace_size(api.WS_ATTN_FWD)
+        assert ws % (U * block) == 0
+        return ws // (U * block), n
+
+    # 32 layers x 8 KV heads of 128K tokens: 256 units for 256 CUs, one chunk each
+    assert fwd_chunks(32, 8, [131072]) == (1, 131072)
+    # one layer x 8 heads of 32K: 8 units, so 1024-key chunks spread them over the CUs
+    assert fwd_chunks(1, 8, [32768])[0] == 32
+    # ragged lengths: shorter chunks than the longest sequence
+    assert fwd_chunks(28, 4, [131072, 65536, 40000, 12345])[0] == 4
+
+
 def test_segment_offsets_layout_and_budget_validation():
     p = make_problem(num_seqs=2, cu_seqlens=[0, 100, 150])
     b = np.array([[20, 30], [16, 50]], dtype=np.int32)  # [S][L]
