@@ -15,10 +15,12 @@
 // One 1024-thread workgroup per (layer, sequence, KV head) unit. Radix select of the
 // k-th largest key over order-preserving uint32 images of the fp32 scores (4 passes of
 // 8 bits, per-wave LDS histograms merged in wave order, digit found by a wave scan),
-// which gives the threshold T and how many elements equal to T are taken. Then an
-// ordered stream compaction in rounds of 4096 positions: a block scan of "surely
-// kept" (window, or key > T) and "tied" (key == T) counts gives every kept position
-// its slot; ties are taken by ascending position.
+// which gives the threshold T and how many elements equal to T are taken; once the keys
+// sharing the threshold's prefix fit in LDS, the remaining passes count over that list.
+// Then an ordered stream compaction in rounds of 4096 positions: prefix counts of
+// "surely kept" (window, or key > T) and "tied" (key == T) positions, from ballots within
+// a wave and LDS sums across waves, give every kept position its slot; ties are taken by
+// ascending position.
 #include "kvs_internal.hpp"
 
 namespace kvs {
