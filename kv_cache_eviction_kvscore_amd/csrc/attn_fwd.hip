@@ -13,7 +13,7 @@
 // computing wave owns 32 rows, one row per lane (both half-waves hold the row).
 // S^T = K.Q^T on v_mfma_f32_32x32x16_bf16 and O^T += V^T.P^T on v_mfma_f32_32x32x16_f16.
 // K/V tiles of 64 keys go from HBM straight into LDS (global_load_lds_dwordx4) through
-// a ring of four buffers, two tiles in flight while one is computed; the 16-byte chunks
+// a ring of four buffers, three tiles in flight while one is computed; the 16-byte chunks
 // of each row are XOR-swizzled with a function of the row so that the K operand reads
 // (ds_read_b128) and the V^T transpose reads (ds_read_tr16_b64) are conflict-free. One
 // tile ahead of its use, V is converted to fp16 in place (exact for |v| < 65504). P
@@ -21,9 +21,11 @@
 // few keys per row the rounding of P does not average out, and a^(-j*) feeds the
 // isolated term), pre-scaled by 2^14 so probabilities down to ~4e-9 stay normal; the
 // scale is folded into the exp2 argument and removed once at the end.
-// Online softmax in the log2 domain. When a row's running max moves to a key of the
-// current tile, the previous argmax's value row (held in the lane's registers, weight 1
-// at the old max) is folded into the rest and the new one is read from the tile.
+// Online softmax in the log2 domain; a row's two lanes exchange their maxima with
+// v_permlane32_swap and keep their own halves of the row sums. When a row's running max
+// moves to a key of the current tile, the previous argmax's value row (held in the lane's
+// registers, weight 1 at the old max) is folded into the rest and the new one is read
+// from the tile.
 // Pass 2 (fwd_combine): one wave per row merges the chunks' (m, l_rest, acc_rest, j*,
 // v*) in ascending chunk order and writes a, lse, j*, and the isolated term.
 #include <type_traits>
