@@ -10,12 +10,13 @@
 // by HBM, not by the matrix cores; it runs on the VALU:
 // decode_partial: grid (key split, unit), 4 waves. A group of D/8 lanes shares one key
 //   row, a lane owns 8 of its dims, so one wave load moves 64/(D/8) consecutive rows
-//   (1 KB, coalesced). q.k for the G heads of the group is a v_dot2_f32_bf16 chain on the
-//   lane's 8 dims plus a DPP reduction over the group. Every group runs its own online
-//   softmax over a strided subset of the split's keys (fp32 accumulators, log2 domain; the
-//   running max is only moved when a logit exceeds it by more than 8, so the rescale is
-//   rare), then the groups merge in the wave (shuffles) and the waves in LDS, in a fixed
-//   order. The split's (max, sum, sum p v) per head go to the workspace.
+//   (1 KB, coalesced; nontemporal, as a call reads each cached row once). q.k for the G
+//   heads of the group is a v_dot2_f32_bf16 chain on the lane's 8 dims plus a DPP
+//   reduction over the group. Every group runs its own online softmax over a strided
+//   subset of the split's keys (fp32 accumulators, log2 domain; the running max is only
+//   moved when a logit exceeds it by more than 8, so the rescale is rare), then the groups
+//   merge in the wave (shuffles) and the waves in LDS, in a fixed order. The split's
+//   (max, sum, sum p v) per head go to the workspace.
 // decode_combine: one wave per (unit, head) merges the splits in ascending order.
 #include <type_traits>
 
@@ -145,16 +146,16 @@ __global__ __launch_bounds__(NTHREADS) void decode_partial_kernel(DecDev p, cons
     u32x4 kx[UNROLL], vx[UNROLL];
 #pragma unroll
     for (int r = 0; r < UNROLL; ++r) {
-      kx[r] = *(const u32x4*)(kb + (int64_t)(j + r * NSTREAM) * D);
-      vx[r] = *(const u32x4*)(vb + (int64_t)(j + r * NSTREAM) * D);
+      kx[r] = __builtin_nontemporal_load((const u32x4*)(kb + (int64_t)(j + r * NSTREAM) * D));
+      vx[r] = __builtin_nontemporal_load((const u32x4*)(vb + (int64_t)(j + r * NSTREAM) * D));
     }
 #pragma unroll
     for (int r = 0; r < UNROLL; ++r) step(kx[r], vx[r]);
     j += UNROLL * NSTREAM;
   }
   for (; it < nsteps; ++it, j += NSTREAM) {
-    const u32x4 kx = *(const u32x4*)(kb + (int64_t)j * D);
-    const u32x4 vx = *(const u32x4*)(vb + (int64_t)j * D);
+    const u32x4 kx = __builtin_nontemporal_load((const u32x4*)(kb + (int64_t)j * D));
+    const u32x4 vx = __builtin_nontemporal_load((const u32x4*)(vb + (int64_t)j * D));
     step(kx, vx);
   }
 
