@@ -24,8 +24,10 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 // for every lane. Issued from inline asm so that the compiler does not treat it as an LDS
 // store: it would otherwise drain every load in flight (s_waitcnt vmcnt(0)) before each LDS
 // read it cannot prove disjoint. The caller orders it with explicit vmcnt waits and a barrier.
+// Nontemporal (nt): a pass reads each K/V tile once, and streams far more K/V than the
+// caches could hold until the next pass (measured 1-1.5% faster forward and score).
 __device__ inline void lds_dma16(const void* base, unsigned off, unsigned lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base),
                "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
