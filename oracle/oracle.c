@@ -27,7 +27,10 @@
  * KV head) unit the logits of every window row are materialised as a matrix, each
  * row's softmax statistics and output a_i are formed from it, and then every
  * score is a plain sum over rows of the per-pair term with the distance taken by
- * direct difference.
+ * direct difference. The one exception is each row's argmax pair: there 1 - p can
+ * round to 0 in fp64, so its term is taken from the definition itself (the output
+ * recomputed without j*, over the survivors at their own scale) and not from the
+ * closed form, which would divide by that rounded difference.
  */
 #include <math.h>
 #include <stdint.h>
@@ -91,8 +94,11 @@ static int unit_eval(const oracle_shape *sh, const uint16_t *q, const uint16_t *
   double *S = (double *)malloc(sizeof(double) * (size_t)R * n); /* logits, materialised */
   double *A = (double *)malloc(sizeof(double) * (size_t)R * d);
   double *LSE = (double *)malloc(sizeof(double) * (size_t)R);
-  if (!K || !V || !Q || !S || !A || !LSE) {
-    free(K); free(V); free(Q); free(S); free(A); free(LSE);
+  double *TERM = (double *)malloc(sizeof(double) * (size_t)R);     /* each row's argmax-pair term */
+  double *AM = (double *)malloc(sizeof(double) * (size_t)R * d);   /* a^(-j*) of each row */
+  int32_t *JS = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);    /* each row's argmax j* */
+  if (!K || !V || !Q || !S || !A || !LSE || !TERM || !AM || !JS) {
+    free(K); free(V); free(Q); free(S); free(A); free(LSE); free(TERM); free(AM); free(JS);
     return -2;
   }
   for (int64_t j = 0; j < n; ++j) {
@@ -138,7 +144,47 @@ static int unit_eval(const oracle_shape *sh, const uint16_t *q, const uint16_t *
     LSE[r] = lse;
     const double pm = exp(m - lse);
     if (pm > pmax) pmax = pm;
-    if (jstar_rows) jstar_rows[r] = (int32_t)jm;
+    JS[r] = (int32_t)jm;
+  }
+
+  /*
+   * The argmax pair of each row, by the definition of removal (DropKV page, "Methodology
+   * in Plain English"): drop j*, renormalise the softmax over the survivors and measure
+   * ||a - a^(-j*)||. The survivors' weights are taken relative to their own max, so a^(-j*)
+   * keeps full precision even where p* rounds to 1 in fp64 (the rest's total weight below
+   * 2^-53); the closed form p/(1-p)*||a - v_j|| used for the other pairs divides by 1 - p*,
+   * which cancels for this pair (every other pair has p <= 1/2). Row r sees keys 0..t with
+   * t >= n - W >= 1, so at least one key survives.
+   */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int r = 0; r < R; ++r) {
+    const int64_t t = n - W + r % W;
+    const int64_t js = JS[r];
+    const double *srow = S + (int64_t)r * n;
+    if (sh->mode == 2) { /* the argmax pair's attention weight p* */
+      TERM[r] = exp(srow[js] - LSE[r]);
+      continue;
+    }
+    double m2 = -INFINITY;
+    for (int64_t j = 0; j <= t; ++j)
+      if (j != js && srow[j] > m2) m2 = srow[j];
+    double *am = AM + (int64_t)r * d;
+    for (int c = 0; c < d; ++c) am[c] = 0.0;
+    double lrest = 0.0;
+    for (int64_t j = 0; j <= t; ++j) {
+      if (j == js) continue;
+      const double w = exp(srow[j] - m2);
+      lrest += w;
+      for (int c = 0; c < d; ++c) am[c] += w * V[j * d + c];
+    }
+    const double *ar = A + (int64_t)r * d;
+    double dist2 = 0.0;
+    for (int c = 0; c < d; ++c) {
+      const double df = ar[c] - am[c] / lrest;
+      dist2 += df * df;
+    }
+    const double shift = sqrt(dist2); /* ||a - a^(-j*)||_2 */
+    TERM[r] = (sh->mode == 1) ? shift * shift : shift;
   }
 
   /* Per-pair term and the window/head sum, one output token j at a time. */
@@ -150,6 +196,10 @@ static int unit_eval(const oracle_shape *sh, const uint16_t *q, const uint16_t *
         const int i = r % W;
         const int64_t t = n - W + i;
         if (j > t) continue; /* causal: row r never saw key j */
+        if (j == JS[r]) { /* the row's argmax pair, by removal above */
+          acc += TERM[r];
+          continue;
+        }
         const double x = S[(int64_t)r * n + j] - LSE[r];
         const double p = exp(x);
         if (sh->mode == 2) { /* attention sum (PyramidKV aggregated window score) */
@@ -171,30 +221,13 @@ static int unit_eval(const oracle_shape *sh, const uint16_t *q, const uint16_t *
     }
   }
 
-  if (dom_rows && jstar_rows) {
-    for (int r = 0; r < R; ++r) {
-      const int64_t j = jstar_rows[r];
-      const double x = S[(int64_t)r * n + j] - LSE[r];
-      if (sh->mode == 2) { /* the argmax pair's attention weight p* */
-        dom_rows[r] = exp(x);
-        continue;
-      }
-      const double c = exp(x) / (-expm1(x));
-      const double *ar = A + (int64_t)r * d;
-      double dist2 = 0.0;
-      for (int cc = 0; cc < d; ++cc) {
-        const double df = ar[cc] - V[j * d + cc];
-        dist2 += df * df;
-      }
-      const double shift = c * sqrt(dist2);
-      dom_rows[r] = (sh->mode == 1) ? shift * shift : shift;
-    }
-  }
+  if (jstar_rows) memcpy(jstar_rows, JS, sizeof(int32_t) * (size_t)R);
+  if (dom_rows) memcpy(dom_rows, TERM, sizeof(double) * (size_t)R);
   if (a_rows) memcpy(a_rows, A, sizeof(double) * (size_t)R * d);
   if (lse_rows) memcpy(lse_rows, LSE, sizeof(double) * (size_t)R);
   if (pmax_out) *pmax_out = pmax;
 
-  free(K); free(V); free(Q); free(S); free(A); free(LSE);
+  free(K); free(V); free(Q); free(S); free(A); free(LSE); free(TERM); free(AM); free(JS);
   return 0;
 }
 

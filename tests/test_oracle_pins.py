@@ -108,6 +108,30 @@ def test_two_visible_keys_closed_form():
         np.testing.assert_allclose(got, [p0 * dist, (1 - p0) * dist], rtol=1e-12)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_dominant_key_with_p_rounding_to_one(mode):
+    """One key ~60 nats above the rest: p* rounds to 1 in fp64 and 1 - p* to 0.
+
+    The argmax pair's shift is still ||a - a^(-j*)|| of brute-force removal (finite, about
+    the distance from v_j* to the survivors' average), and every other pair's is tiny.
+    """
+    rng = np.random.default_rng(21)
+    G, W, d, n = 1, 2, 8, 12
+    q, k, v = make_unit(rng, G, W, d, n)
+    qf = bits_f64(q).reshape(G * W, d)
+    kk = k.reshape(n, d)
+    kk[3] = bf16_bits(qf[0] * (60.0 * math.sqrt(d) / (qf[0] @ qf[0])))  # logit ~60 for row 0
+    out = run_oracle(q, k, v, G, W, d, n, mode=mode, rows=True)
+    assert int(out["jstar"][0]) == 3 and out["pmax"][0] == 1.0
+    ref = brute.unit_scores(qf, bits_f64(kk), bits_f64(v).reshape(n, d), W, 1.0 / math.sqrt(d), mode=mode)
+    got = out["score"][0, 0]
+    assert np.isfinite(got).all() and np.isfinite(out["dom"]).all()
+    np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-14)
+    sh = brute.removal_shifts(qf[0], bits_f64(kk)[:n - W + 1], bits_f64(v).reshape(n, d)[:n - W + 1], 1 / math.sqrt(d))
+    np.testing.assert_allclose(out["dom"][0], sh[3] ** 2 if mode == 1 else sh[3], rtol=1e-12)
+    assert sh[3] > 1.0
+
+
 def test_identical_keys_closed_form():
     """m identical visible keys: p = 1/m, a = mean(v), term_j = ||mean(v) - v_j|| / (m - 1)."""
     rng = np.random.default_rng(12)
@@ -129,7 +153,10 @@ def test_constant_values_give_zero_scores():
     q, k, _ = make_unit(rng, G, W, d, n)
     v = bf16_bits(np.tile(rng.standard_normal(d), (1, 1, n, 1)))
     got = run_oracle(q, k, v, G, W, d, n)["score"][0, 0]
-    assert np.abs(got).max() < 1e-15
+    # exactly 0; in fp64 a and a^(-j) are weighted means of n copies of v, each off by at
+    # most n*eps*|v_c| per element, and G*W rows add up
+    vn = np.linalg.norm(bits_f64(v)[0, 0, 0])
+    assert np.abs(got).max() < G * W * 2 * n * np.finfo(float).eps * vn
 
 
 def test_squared_mode_is_square_of_l2_for_one_row():
