@@ -70,18 +70,6 @@ __device__ inline int swz_v(int r) {
 }
 
 
-// 8 bf16 -> 8 fp16 (exact in fp16's normal range; saturating towards zero beyond it)
-__device__ inline u32x4 bf16x8_to_f16x8(u32x4 u) {
-  const unsigned w[4] = {u[0], u[1], u[2], u[3]};
-  unsigned r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
-    r[i] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-  }
-  return u32x4{r[0], r[1], r[2], r[3]};
-}
-
 // wait until at most N of this wave's vector memory instructions are outstanding
 template <int N>
 __device__ inline void vm_wait() {

@@ -99,8 +99,20 @@ __host__ __device__ inline void unit_coords(const Dev& p, int u, int& l, int& s,
 // Forward split record block: [RT][d] fp32 O_rest | [RT][d] fp16 v* | [RT] m | [RT] m2 | [RT] l_rest | [RT] j*
 __host__ __device__ inline size_t fwd_block_floats(int RT, int d) { return (size_t)RT * d + (size_t)RT * d / 2 + 4 * (size_t)RT; }
 
-// Score-prep workspace: [rows][d] bf16 a_hat | [rows] fp32 ||a_hat||^2 | [rows] fp32 lse*log2(e)
+// Score-prep workspace: [rows][d] fp16 a_hat | [rows] fp32 ||a_hat||^2 | [rows] fp32 lse*log2(e)
 __host__ __device__ inline size_t prep_bytes(int64_t rows, int d) { return (size_t)rows * d * 2 + (size_t)rows * 8; }
+
+// 8 bf16 -> 8 fp16 (exact in fp16's normal range; saturating towards zero beyond it)
+__device__ inline u32x4 bf16x8_to_f16x8(u32x4 u) {
+  const unsigned w[4] = {u[0], u[1], u[2], u[3]};
+  unsigned r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+    r[i] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  return u32x4{r[0], r[1], r[2], r[3]};
+}
 
 // Launchers (each .hip file owns its kernels). Return hipGetLastError() after launch.
 hipError_t launch_attn_fwd(const Dev& p, const void* q, const void* k, const void* v, float* a, float* lse,

@@ -8,11 +8,14 @@
 // the window rows and the query heads of the KV group. Mode ATTN scores sum_i p_ij
 // instead (PyramidKV page, "Observation Window and Aggregated Attention Eviction").
 //
-// score_prep: a_hat = bf16(a) (the MFMA operand), ||a_hat||^2 from the rounded values
+// score_prep: a_hat = fp16(a) (the MFMA operand), ||a_hat||^2 from the rounded values
 //   (so the expansion is the exact ||a_hat - v||^2 up to fp32 rounding), lse*log2(e).
+//   fp16, not bf16: the distance's error from rounding a is 2 (a - a_hat).(a - v), and
+//   fp16's 11-bit significand makes it eight times smaller; with bf16 a pair whose term
+//   dominates a token's score could miss a 1e-3 relative bound.
 // score_kernel: grid (key chunk, query tile, unit); 8 waves of 32 rows, two per SIMD, so
 //   one wave's VALU work overlaps the other's MFMAs. Orientation S = Q.K^T,
-//   X = A_hat.V^T (rows x keys) on v_mfma_f32_32x32x16_bf16 with the row operands held
+//   X = A_hat.V^T (rows x keys) on v_mfma_f32_32x32x16_bf16 / _f16 with the row operands held
 //   in AGPRs and the accumulators written to VGPRs. K/V tiles of 64 keys go from HBM
 //   straight into LDS (global_load_lds_dwordx4, no register staging) through a ring of
 //   four buffers, so two tiles are in flight while one is computed. A tile keeps whole
@@ -25,7 +28,8 @@
 //   (1, 1, 1, -||a_i||^2/2 in three parts) by (-||v_j||^2/2 in three parts, 1, 1, 1);
 //   every part is an exact bf16 split, so the A.V^T accumulator is -D/2 with
 //   D = ||a - v||^2. ||v_j||^2 is summed from the tile in LDS (v_dot2_f32_bf16) one
-//   tile ahead of its use. The Q.K^T chain gets an augmented k-step too: (-lse_i/scale
+//   tile ahead of its use; the same pass converts the tile's V to fp16 in place (exact in
+//   fp16's normal range) for the A_hat.V^T product. The Q.K^T chain gets an augmented k-step too: (-lse_i/scale
 //   in three bf16 parts) times (1, 1, 1), so its accumulator is ln p / scale and needs no
 //   per-row register. Per pair: 1/p = exp2(-acc * scale * log2 e), and
 //   c*sqrt(D) = sqrt(2) * sqrt(D/2) / (1/p - 1): three transcendentals and three other
@@ -88,7 +92,7 @@ __device__ inline Split3 split3(float x) {
 
 template <int D>
 __global__ __launch_bounds__(256) void score_prep_kernel(int64_t rows, const float* __restrict__ a,
-                                                         const float* __restrict__ lse, __bf16* __restrict__ ahat,
+                                                         const float* __restrict__ lse, _Float16* __restrict__ ahat,
                                                          float* __restrict__ na, float* __restrict__ lse2) {
   constexpr int PER = D / 64;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(256) void score_prep_kernel(int64_t rows, const flo
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
-    const __bf16 b = (__bf16)a[row * D + e];
+    const _Float16 b = (_Float16)a[row * D + e];  // round to nearest
     ahat[row * D + e] = b;
     const float f = (float)b;
     s += f * f;
@@ -115,7 +119,7 @@ template <int D, int MODE>
 __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __restrict__ q,
                                                          const __bf16* __restrict__ k,
                                                          const __bf16* __restrict__ v,
-                                                         const __bf16* __restrict__ ahat,
+                                                         const _Float16* __restrict__ ahat,
                                                          const float* __restrict__ na,
                                                          const float* __restrict__ lse2,
                                                          const int32_t* __restrict__ jstar,
@@ -202,13 +206,14 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   // KPW*w .. KPW*w+KPW-1, LPK lanes per key (lanes key%KPW + KPW*c), CPN chunks each.
   auto norms = [&](int it) __attribute__((always_inline)) {
     if constexpr (!WITH_V) return;
-    const char* vt = (const char*)sm.tile[it % NBUF][1];
+    char* vt = (char*)sm.tile[it % NBUF][1];
     const int key = KPW * wave + (lane % KPW), cg = lane / KPW;
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < CPN; ++e) {
       const int c = CPN * cg + e;
-      const u32x4 w = *(const u32x4*)(vt + key * RS + ((c ^ swz<D>(key)) << 4));
+      u32x4* cp = (u32x4*)(vt + key * RS + ((c ^ swz<D>(key)) << 4));
+      const u32x4 w = *cp;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         // copy the element out first: a bit_cast of a vector-element lvalue reads element 0
@@ -216,6 +221,7 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
         const bf16x2 x = __builtin_bit_cast(bf16x2, wm);
         ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
       }
+      *cp = bf16x8_to_f16x8(w);  // the A_hat.V^T product reads the tile in fp16
     }
     // a shuffle here, not a VALU exchange chain: this side work is off the MFMA path, and
     // the dependent DPP / permlane steps measured slower than LDS shuffles in flight
@@ -248,17 +254,19 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   }
 
   // ---- row operands (A side): lane row l32 of the wave's 32, k-slots 8h..8h+7
-  bf16x8 qf[NKK], af[NKK], aug, augs;
+  bf16x8 qf[NKK], aug, augs;
+  f16x8 af[NKK];
   {
     const int rt = wrow0 + l32;
     const bool ok = computing && rt < rows_here;
     const __bf16* qrow = q + (rbase + (ok ? rt : 0)) * D;
-    const __bf16* arow = ahat + (rbase + (ok ? rt : 0)) * D;
+    const _Float16* arow = ahat + (rbase + (ok ? rt : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       bf16x8 z = {};
+      f16x8 zh = {};
       qf[kk] = ok ? *(const bf16x8*)(qrow + 16 * kk + 8 * h) : z;
-      af[kk] = (ok && WITH_V) ? *(const bf16x8*)(arow + 16 * kk + 8 * h) : z;
+      af[kk] = (ok && WITH_V) ? *(const f16x8*)(arow + 16 * kk + 8 * h) : zh;
     }
     // augmented k-step of the A.V^T chain: (1, 1, 1, -||a_hat||^2/2 in three parts) in slots 0..5
     bf16x8 w8 = {};
@@ -368,8 +376,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       const bf16x8 kx = *(const bf16x8*)(kt + koff(kk));
       acc.S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kk], kx, kk ? acc.S : f32x16{}, 0, 0, 0);
       if constexpr (WITH_V) {
-        const bf16x8 vx = *(const bf16x8*)(kt + TB + koff(kk));
-        acc.X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], vx, kk ? acc.X : f32x16{}, 0, 0, 0);
+        const f16x8 vx = *(const f16x8*)(kt + TB + koff(kk));  // converted to fp16 by the norm pass
+        acc.X = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], vx, kk ? acc.X : f32x16{}, 0, 0, 0);
       }
       if (kk == NKK / 2) {  // the augmented k-steps sit mid-chain, off the chains' tails
         acc.S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(augs, ones3, acc.S, 0, 0, 0);
@@ -469,13 +477,13 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
 hipError_t launch_score(const Dev& p, const void* q, const void* k, const void* v, const float* a, const float* lse,
                         const int32_t* jstar, float* partial, void* ws, hipStream_t st) {
   const int64_t rows = (int64_t)p.U * p.R;
-  __bf16* ahat = (__bf16*)ws;
+  _Float16* ahat = (_Float16*)ws;
   float* na = (float*)((char*)ws + (size_t)rows * p.d * 2);
   float* l2 = na + rows;
   const dim3 gp((unsigned)((rows + 3) / 4)), gs(p.score_chunks, p.Tq, p.U);
   auto run = [&](auto kern) {
     hipLaunchKernelGGL(kern, gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                       (const __bf16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
+                       (const _Float16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
   };
   if (p.d == 128) {
     hipLaunchKernelGGL(score_prep_kernel<128>, gp, dim3(256), 0, st, rows, a, lse, ahat, na, l2);

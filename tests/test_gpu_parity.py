@@ -81,6 +81,24 @@ def test_edge_cases(w):
     _check_all(w, list(range(U)))
 
 
+def test_dominant_sink_one_row():
+    """One window row per head, the sink aligned with the query: p* is 1 - O(1e-19), so the
+    argmax pair's term rests on the rest sums alone (the isolated path in the forward; the
+    oracle's removal form)."""
+    w = Workload("dominant_sink_w1", 1040805, 3, 2, 2, 128, (3469, 4821, 3375), 1, (16, 28, 17), "fixed", 2104,
+                 sink=True)
+    _check_all(w, list(range(w.num_layers * w.num_seqs * w.num_kv_heads)), n_sink=4)
+
+
+def test_squared_mode_one_row_seven_heads():
+    """Mode SQ with W = 1 and 7 query heads per KV head, d = 64: few pairs per token, so one
+    pair's term can carry a token's score and its distance error is not averaged (a bf16
+    A_hat operand missed the bar here)."""
+    w = Workload("sq_w1_g7_d64", 672914, 1, 14, 2, 64, (638, 4339, 4170), 1, (26, 0, 2), "uniform", 0.452,
+                 sink=True)
+    _check_all(w, list(range(w.num_layers * w.num_seqs * w.num_kv_heads)), mode=1, pool=11, n_sink=4)
+
+
 def test_token_major_strides():
     w = small_variant(WORKLOADS[2], name="tokmajor", seqlens=(4096,), heavy_count=(20,))
     _check_all(w, [0, 3, 7], k_layout="token_major")
@@ -90,7 +108,8 @@ def _expansion_floor(w, run, u):
     """Absolute error bound of the score when the true distances vanish.
 
     The kernel forms D = ||a_hat||^2 + ||v||^2 - 2 a_hat.v (the expansion the DropKV
-    page's engineering paragraph describes) from fp32 sums of at most 2d + 16 products,
+    page's engineering paragraph describes; a_hat = a rounded to fp16) from fp32 sums of
+    at most 2d + 16 products,
     so |dD| <= 2 gamma (||a_hat||^2 + ||v||^2) with gamma = m u / (1 - m u), u = 2^-24,
     m = 2d + 16 (the textbook bound for a floating-point dot product). Since
     |sqrt(x) - sqrt(y)| <= sqrt(|x - y|), token j's score moves by at most
@@ -103,7 +122,7 @@ def _expansion_floor(w, run, u):
     n, W, G, d = w.seqlens[0], w.window, w.group, w.head_dim
     m = 2 * d + 16
     gamma = m * 2.0 ** -24 / (1 - m * 2.0 ** -24)
-    ahat = bits_f64(synth.bf16_bits(torch.from_numpy(ref["a"]).float()))
+    ahat = torch.from_numpy(ref["a"]).float().half().double().numpy()
     na = (ahat ** 2).sum(1)
     vf = bits_f64(ref["v"])
     nv = (vf ** 2).sum(1)
