@@ -46,8 +46,9 @@
  *     validation error nothing is enqueued.
  *   - Scores are deterministic: no floating-point atomics; every sum has a fixed order.
  *   - Non-finite inputs are outside the contract (results undefined, no fault). The
- *     attention forward multiplies P by V in fp16: |v| must stay below 65504 (larger
- *     magnitudes saturate).
+ *     attention forward multiplies P by V, and the score pass a by V, in fp16: |v|
+ *     must stay below 65504 (larger magnitudes saturate); entries below 2^-14 lose
+ *     precision as fp16 subnormals (absolute error <= 2^-25).
  *
  * Data layout. A unit is u = (l*S + s)*Hkv + g (layer-major); G = Hq/Hkv; a unit has
  * R = G*W query rows r = hl*W + i (hl = head within the group, i = window row), which
