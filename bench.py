@@ -57,7 +57,9 @@ def algorithmic_work(w, budgets_rows: int, tq: int):
     return {
         "attn_fwd": {"flop": 4 * d * pairs, "bytes": kv + q + rows * (d * 4 + 12)},
         "score": {"flop": 4 * d * pairs, "bytes": kv + q + rows * (d * 2 + 12) + 4 * tq * th},
-        "merge": {"flop": 0, "bytes": 4 * tq * th + 4 * th + rows * 8},
+        # one query tile: merged in place, only the isolated terms (read j*, dom; one score
+        # read and written per row); else the tile rows are summed into the score rows
+        "merge": {"flop": 0, "bytes": (4 * tq * th + 4 * th + rows * 8) if tq > 1 else rows * 16},
         "topk": {"flop": 0, "bytes": 4 * th + 4 * budgets_rows},
         "compact": {"flop": 0, "bytes": budgets_rows * (2 * 2 * d * 2 + 4)},
         "pairs": pairs,

@@ -146,7 +146,7 @@ int kvscore_attn_fwd(const kvscore_problem* p, const void* q_win, const void* k,
  *       of c_ij * ||a_i - v_j||  (mode SQ: (c_ij * ||a_i - v_j||)^2; mode ATTN: p_ij,
  *       which reads no V, a or its norms),
  *   c_ij = p_ij / (1 - p_ij), p_ij = exp(s_ij - lse_i) recomputed from q and k,
- *   ||a_i - v_j||^2 = ||a_i||^2 - 2 a_i.v_j + ||v_j||^2 with a_i rounded to bf16.
+ *   ||a_i - v_j||^2 = ||a_i||^2 - 2 a_i.v_j + ||v_j||^2 with a_i rounded to fp16.
  * Inputs: q_win, k, v (bf16), a, lse, jstar from kvscore_attn_fwd (device).
  * Output: partial (device). workspace: >= kvscore_workspace_size(p, KVSCORE_WS_SCORE).
  */
@@ -158,6 +158,9 @@ int kvscore_score(const kvscore_problem* p, const void* q_win, const void* k, co
  * Split-K merge (DropKV page, Key Contribution 3): score[l][g][j] = the Tq partials
  * summed in ascending tile order, plus the isolated argmax terms dom_r of the unit's
  * rows with jstar_r = j, summed in row order. All device pointers.
+ * With one query tile (Tq = 1) partial has score's layout, and the two may be the
+ * same buffer: the terms are then added in place and the tile sum (a copy) is skipped.
+ * Otherwise they must not overlap (KVSCORE_EINVAL when they are equal).
  */
 int kvscore_merge(const kvscore_problem* p, const float* partial, const int32_t* jstar, const float* dom,
                   float* score, void* stream);

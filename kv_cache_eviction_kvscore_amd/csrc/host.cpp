@@ -345,6 +345,8 @@ int kvscore_merge(const kvscore_problem* p, const float* partial, const int32_t*
   kvs::Dev d;
   if (int rc = make_dev(p, d)) return rc;
   if (!partial || !jstar || !dom || !score) return fail(KVSCORE_EINVAL, "NULL tensor argument");
+  if (partial == score && d.Tq != 1)
+    return fail(KVSCORE_EINVAL, "partial and score may be one buffer only with one query tile (Tq = %d)", d.Tq);
   return launched(kvs::launch_merge(d, partial, jstar, dom, score, (hipStream_t)stream), "kvscore_merge");
 }
 

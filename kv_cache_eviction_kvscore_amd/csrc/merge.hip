@@ -97,8 +97,11 @@ __global__ __launch_bounds__(256) void merge_isolated_kernel(Dev p, const int32_
 
 hipError_t launch_merge(const Dev& p, const float* partial, const int32_t* jstar, const float* dom, float* score,
                         hipStream_t st) {
-  const dim3 grid((unsigned)((p.max_n + kMergeChunk - 1) / kMergeChunk), p.U);
-  hipLaunchKernelGGL(merge_sum_kernel, grid, dim3(256), 0, st, p, partial, score);
+  // one query tile in the score buffer itself: the sum over tiles is that tile, in place
+  if (!(p.Tq == 1 && partial == score)) {
+    const dim3 grid((unsigned)((p.max_n + kMergeChunk - 1) / kMergeChunk), p.U);
+    hipLaunchKernelGGL(merge_sum_kernel, grid, dim3(256), 0, st, p, partial, score);
+  }
   hipLaunchKernelGGL(merge_isolated_kernel, dim3(p.U), dim3(256), 0, st, p, jstar, dom, score);
   return hipGetLastError();
 }

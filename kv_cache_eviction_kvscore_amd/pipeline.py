@@ -42,7 +42,10 @@ class Pipeline:
         self.jstar = torch.empty(rows, dtype=torch.int32, device=dev)
         self.dom = torch.empty(rows, dtype=torch.float32, device=dev)
         self.partial = torch.empty((L, Hkv, self.tq, N), dtype=torch.float32, device=dev)
-        self.score = torch.empty((L, Hkv, N), dtype=torch.float32, device=dev)
+        # one query tile: the partial row is the score row, and the merge adds the isolated
+        # terms in place
+        self.score = (self.partial.view(L, Hkv, N) if self.tq == 1
+                      else torch.empty((L, Hkv, N), dtype=torch.float32, device=dev))
         self.ws_fwd = torch.empty(max(1, prob.workspace_size(api.WS_ATTN_FWD)), dtype=torch.uint8, device=dev)
         self.ws_score = torch.empty(max(1, prob.workspace_size(api.WS_SCORE)), dtype=torch.uint8, device=dev)
         self.ws_topk = (torch.empty(prob.workspace_size(api.WS_TOPK), dtype=torch.uint8, device=dev)

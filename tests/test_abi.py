@@ -83,6 +83,16 @@ def test_null_tensors_and_small_workspace_rejected():
     assert rc == 1  # q not 16-byte aligned
 
 
+def test_merge_in_place_only_with_one_query_tile():
+    """partial and score may be one buffer only when there is one query tile (then the layouts
+    agree); with two tiles that is rejected before any launch."""
+    p2 = make_problem(num_q_heads=28, num_kv_heads=4, window=64)  # 448 rows -> 2 tiles
+    lib = api.load()
+    fake = 1 << 20
+    rc = lib.kvscore_merge(p2.ref, fake, fake + 4096, fake + 8192, fake, None)
+    assert rc == api.EINVAL and b"one query tile" in lib.kvscore_last_error()
+
+
 def test_query_tiles_and_workspace_sizes():
     p = make_problem()  # G*W = 64 rows
     assert p.num_query_tiles() == 1

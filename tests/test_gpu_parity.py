@@ -165,6 +165,22 @@ def test_deterministic_bitwise():
             assert torch.equal(_bits(v), first[k]), k
 
 
+def test_merge_in_place_matches_separate_buffers():
+    """With one query tile the pipeline merges in the partial buffer itself; a merge into a
+    buffer of its own must give the same bits."""
+    w = small_variant(WORKLOADS[3], name="inplace", num_layers=2, seqlens=(20000,))
+    data = synth.generate(w, "cuda")
+    run = run_gpu(w, data=data)
+    pipe, prob = run["pipe"], run["prob"]
+    assert pipe.tq == 1 and pipe.score.data_ptr() == pipe.partial.data_ptr()
+    partial = torch.empty_like(pipe.partial)
+    score = torch.full_like(pipe.score, float("nan"))
+    api.score(prob, data["q"], data["k"], data["v"], pipe.a, pipe.lse, pipe.jstar, partial, pipe.ws_score)
+    api.merge(prob, partial, pipe.jstar, pipe.dom, score)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(score), _bits(pipe.score))
+
+
 def test_softmax_scale_override():
     w = WORKLOADS[1]
     data = synth.generate(w, "cuda")
