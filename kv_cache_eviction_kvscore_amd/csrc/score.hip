@@ -14,28 +14,30 @@
 //   fp16's 11-bit significand makes it eight times smaller; with bf16 a pair whose term
 //   dominates a token's score could miss a 1e-3 relative bound.
 // score_kernel: grid (key chunk, query tile, unit); 8 waves of 32 rows, two per SIMD, so
-//   one wave's VALU work overlaps the other's MFMAs. Orientation S = Q.K^T,
-//   X = A_hat.V^T (rows x keys) on v_mfma_f32_32x32x16_bf16 / _f16 with the row operands held
-//   in AGPRs and the accumulators written to VGPRs. K/V tiles of 64 keys go from HBM
-//   straight into LDS (global_load_lds_dwordx4, no register staging) through a ring of
-//   four buffers, so two tiles are in flight while one is computed. A tile keeps whole
-//   key rows (each DMA instruction moves four or eight full rows); the 16-byte chunks of
-//   row r are XOR-swizzled with a function of r so that the 32 keys x 16 slots an MFMA
-//   operand needs are read conflict-free with ds_read_b128. A lane owns one key column
-//   and 16 rows of the 32x32 block, so the sum over rows stays in the lane (plus one
-//   half-wave exchange); the waves' column sums are added in LDS in wave order.
-//   The expansion runs on the matrix cores: one extra k-step multiplies
-//   (1, 1, 1, -||a_i||^2/2 in three parts) by (-||v_j||^2/2 in three parts, 1, 1, 1);
-//   every part is an exact bf16 split, so the A.V^T accumulator is -D/2 with
-//   D = ||a - v||^2. ||v_j||^2 is summed from the tile in LDS (v_dot2_f32_bf16) one
-//   tile ahead of its use; the same pass converts the tile's V to fp16 in place (exact in
-//   fp16's normal range) for the A_hat.V^T product. The Q.K^T chain gets an augmented k-step too: (-lse_i/scale
-//   in three bf16 parts) times (1, 1, 1), so its accumulator is ln p / scale and needs no
-//   per-row register. Per pair: 1/p = exp2(-acc * scale * log2 e), and
-//   c*sqrt(D) = sqrt(2) * sqrt(D/2) / (1/p - 1): three transcendentals and three other
-//   VALU instructions; the sqrt(2) (2 in mode SQ) is applied once per token. Pairs
-//   (i, j*_i) are skipped (their term comes exactly from the forward); so are keys after
-//   a row's position. Both masks only act on tiles flagged in LDS, others run unmasked.
+//   one wave's VALU work overlaps the other's MFMAs. Orientation S = Q.K^T on
+//   v_mfma_f32_32x32x16_bf16 and X = A_hat.V^T (rows x keys) on v_mfma_f32_32x32x16_f16,
+//   with the row operands held in AGPRs and the accumulators written to VGPRs. K/V tiles
+//   of 64 keys go from HBM straight into LDS (global_load_lds_dwordx4, no register
+//   staging) through a ring of four buffers, so two tiles are in flight while one is
+//   computed. A tile keeps whole key rows (each DMA instruction moves four or eight full
+//   rows); the 16-byte chunks of row r are XOR-swizzled with a function of r so that the
+//   32 keys x 16 slots an MFMA operand needs are read conflict-free with ds_read_b128. A
+//   lane owns one key column and 16 rows of the 32x32 block, so the sum over rows stays in
+//   the lane (plus one half-wave exchange); the waves' column sums are added in LDS in
+//   wave order.
+//   The expansion runs on the matrix cores: one extra bf16 k-step multiplies
+//   (1, 1, 1, -||a_hat_i||^2/2 in three parts) by (-||v_j||^2/2 in three parts, 1, 1, 1)
+//   into the same accumulator; every part is an exact bf16 split, so X is -D/2 with
+//   D = ||a_hat - v||^2. ||v_j||^2 is summed from the tile in LDS (v_dot2_f32_bf16) one
+//   tile ahead of its use, and the same pass converts the tile's V to fp16 in place (exact
+//   in fp16's normal range) for the A_hat.V^T product. The Q.K^T chain gets an augmented
+//   k-step too: (-lse_i/scale in three bf16 parts) times (1, 1, 1), so its accumulator is
+//   ln p / scale and needs no per-row register. Per pair: 1/p = exp2(-acc * scale *
+//   log2 e), and c*sqrt(D) = sqrt(2) * sqrt(D/2) / (1/p - 1): three transcendentals and
+//   three other VALU instructions; the sqrt(2) (2 in mode SQ) is applied once per token.
+//   Pairs (i, j*_i) are skipped (their term comes exactly from the forward); so are keys
+//   after a row's position. Both masks only act on tiles flagged in LDS, others run
+//   unmasked.
 //   Every pair that is not masked has p <= 1/2 (the row's argmax is isolated), so
 //   1/p - 1 >= 1 needs no guard, and p = 0 gives a zero term.
 #include <type_traits>
