@@ -89,11 +89,18 @@ __global__ __launch_bounds__(256) void pool_kernel(Dev p, const float* __restric
 }
 
 struct SelectSmem {
-  unsigned whist[NWAVES][256];
-  unsigned hist[256];
-  unsigned s_digit, s_above;
+  unsigned s_digit, s_above, s_count;
   int wsum[2][NWAVES];
   long long red[2][NWAVES];
+};
+
+// Radix digits: 14 bits first (sign, exponent and five mantissa bits of the score, so even
+// scores packed into a narrow range split into bins small enough for the LDS list below),
+// then 9 and 9.
+constexpr int kBits0 = 14, kBits12 = 9;
+struct HistSmem {
+  unsigned hist[1 << kBits0];
+  int tsum[NWAVES];
 };
 
 // LDS list of the keys that share the threshold's top byte (or top two bytes), so the
@@ -106,31 +113,34 @@ struct CandSmem {
 
 // Radix select of the kr-th largest key among the keys `visit` enumerates (each thread
 // calls f(key) on its share, all lanes of a wave together): T = that key, need_eq = how
-// many keys equal to T are among the kr largest. 4 passes of 8 bits; per-wave LDS
-// histograms merged in wave order; the digit is found by a wave scan. With cs, the second
-// or else the third pass also appends the keys that share the threshold's prefix so far
-// (its top byte, or its top two) to cs when they fit, and the later passes read that list
-// instead (the counts, so T and need_eq, do not depend on the list's order).
+// many keys equal to T are among the kr largest. Three passes (14, 9 and 9 bits) count
+// into one LDS histogram; the digit is found by a two-level scan over the bins in
+// descending order. With cs, the second pass also appends the keys that share the
+// threshold's top 14 bits to cs when they fit, and the last pass reads that list instead
+// (the counts, so T and need_eq, do not depend on the list's order).
 template <class Visit>
-__device__ void radix_select(SelectSmem& sm, Visit visit, int64_t kr, unsigned& T, int64_t& need_eq,
+__device__ void radix_select(SelectSmem& sm, HistSmem& hs, Visit visit, int64_t kr, unsigned& T, int64_t& need_eq,
                              CandSmem* cs = nullptr) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   unsigned prefix = 0, pmask = 0;
-  bool listed = false;  // uniform: the third and fourth passes read cs
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < NWAVES * 256; i += NT) (&sm.whist[0][0])[i] = 0;
+  bool listed = false;  // uniform: the last pass reads cs
+  for (int pass = 0; pass < 3; ++pass) {
+    const int bits = pass == 0 ? kBits0 : kBits12;
+    const int shift = pass == 0 ? 32 - kBits0 : (pass == 1 ? kBits12 : 0);
+    const int nb = 1 << bits;
+    const unsigned dmask = (unsigned)nb - 1u;
+    for (int i = tid; i < nb; i += NT) hs.hist[i] = 0;
     // keys with the current prefix: the last pass's count of its digit
-    const bool collect = cs && !listed && (pass == 1 || pass == 2) && sm.hist[sm.s_digit] <= (unsigned)kCandCap;
+    const bool collect = cs && pass == 1 && sm.s_count <= (unsigned)kCandCap;
     if (collect && tid == 0) cs->n = 0;
     __syncthreads();
-    auto count = [&](unsigned key) { hist_add(sm.whist[wave], (key & pmask) == prefix, (key >> shift) & 255u); };
+    auto count = [&](unsigned key) { hist_add(hs.hist, (key & pmask) == prefix, (key >> shift) & dmask); };
     if (listed) {
       for (int i = tid; i < (int)cs->n; i += NT) count(cs->key[i]);
     } else if (collect) {
       visit([&](unsigned key) {
         const bool in = (key & pmask) == prefix;
-        hist_add(sm.whist[wave], in, (key >> shift) & 255u);
+        hist_add(hs.hist, in, (key >> shift) & dmask);
         // one slot reservation per wave, then each lane writes at its rank among the wave's
         const unsigned long long m = __ballot(in);
         if (m) {
@@ -145,39 +155,37 @@ __device__ void radix_select(SelectSmem& sm, Visit visit, int64_t kr, unsigned& 
     }
     __syncthreads();
     listed = listed || collect;
-    if (tid < 256) {
-      unsigned c = 0;
-      for (int w = 0; w < NWAVES; ++w) c += sm.whist[w][tid];
-      sm.hist[tid] = c;
-    }
+    // thread t owns bins nb-1-per*t .. nb-per*(t+1) (descending); a scan over the threads'
+    // totals finds the thread, and that thread the bin, where the running count from the
+    // top first reaches kr
+    const int per = nb >= NT ? nb / NT : 1;
+    const bool owns = tid * per < nb;
+    unsigned tot = 0;
+    if (owns)
+      for (int e = 0; e < per; ++e) tot += hs.hist[nb - 1 - (per * tid + e)];
+    const int incl_w = wave_incl_scan((int)tot, lane);
+    if (lane == 63) hs.tsum[wave] = incl_w;
     __syncthreads();
-    if (wave == 0) {
-      // lane L owns digits 255-4L .. 252-4L (descending); find the digit where the
-      // running count from the top first reaches kr.
-      unsigned c4[4], tot = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c4[e] = sm.hist[255 - 4 * lane - e];
-        tot += c4[e];
-      }
-      const int incl = wave_incl_scan((int)tot, lane);
-      const int excl = incl - (int)tot;
-      if ((int64_t)excl < kr && kr <= (int64_t)incl) {
-        unsigned above = (unsigned)excl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if ((int64_t)(above + c4[e]) >= kr) {
-            sm.s_digit = 255u - 4u * lane - e;
-            sm.s_above = above;
-            break;
-          }
-          above += c4[e];
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += hs.tsum[w];
+    const int64_t incl = (int64_t)before + incl_w, excl = incl - (int64_t)tot;
+    if (owns && excl < kr && kr <= incl) {
+      unsigned above = (unsigned)excl;
+      for (int e = 0; e < per; ++e) {
+        const int bin = nb - 1 - (per * tid + e);
+        const unsigned c = hs.hist[bin];
+        if ((int64_t)(above + c) >= kr) {
+          sm.s_digit = (unsigned)bin;
+          sm.s_above = above;
+          sm.s_count = c;
+          break;
         }
+        above += c;
       }
     }
     __syncthreads();
     prefix |= sm.s_digit << shift;
-    pmask |= 255u << shift;
+    pmask |= dmask << shift;
     kr -= sm.s_above;
   }
   T = prefix;
@@ -309,9 +317,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
   int64_t need_eq = 0;
   if (sel == 2) {
     __shared__ CandSmem cs;
+    __shared__ HistSmem hs;
     const float* c0 = sc + ns;
     const int64_t m = cand - ns;
-    radix_select(sm, [&](auto f) {
+    radix_select(sm, hs, [&](auto f) {
       int64_t j0 = 0;
       if ((((size_t)c0) & 15) == 0) {  // 16-byte loads, two in flight per thread
         const int64_t m8 = m / (8 * NT) * (8 * NT);

@@ -5,11 +5,12 @@ always. The selection is integer work decided on the same fp32 values on both si
 every segment must equal the oracle's (a full sort on (-score, position)) exactly.
 
 The score distributions steer the radix select down both of its routes: when at most
-12288 keys share the threshold's top byte, its last two passes read an LDS list of them;
-otherwise they read the scores again. Covered: a log-uniform spread (the list), one top
-byte for every key (uniform in [2, 8)), sixteen distinct values (ties decided by position)
-in a bin too large for the list and in one that fits, all keys equal, and budgets keeping
-every competitor or none.
+12288 keys share the threshold's top 14 bits, its last pass reads an LDS list of them;
+otherwise it reads the scores again. Covered: a log-uniform spread, one top byte for every
+key (uniform in [2, 8)), sixteen distinct values (ties decided by position), ties inside a
+listed bin (all of these take the list), a narrow range whose keys all share their top 14
+bits but differ below (no list, distinct keys), all keys equal (no list, all ties), and
+budgets keeping every competitor or none.
 """
 import numpy as np
 import pytest
@@ -29,6 +30,8 @@ def _scores(kind, n, rng):
         return rng.uniform(2.0, 8.0, n).astype(np.float32)
     if kind == "sixteen_values":
         return (2.0 + 0.25 * rng.integers(0, 16, n)).astype(np.float32)
+    if kind == "narrow":  # one 14-bit bin: sign, exponent and the top five mantissa bits shared
+        return rng.uniform(2.0, 2.0625, n).astype(np.float32)
     if kind == "all_equal":
         return np.full(n, 3.0, dtype=np.float32)
     if kind == "ties_in_list":  # a threshold bin of 8000 keys with sixteen values, over a wide spread
@@ -38,7 +41,7 @@ def _scores(kind, n, rng):
     raise ValueError(kind)
 
 
-KINDS = ["log_uniform", "one_top_byte", "sixteen_values", "all_equal", "ties_in_list"]
+KINDS = ["log_uniform", "one_top_byte", "sixteen_values", "all_equal", "ties_in_list", "narrow"]
 
 
 @pytest.mark.parametrize("budget_extra", [5000, 0, 70000])
