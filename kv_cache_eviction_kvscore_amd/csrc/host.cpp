@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "../../include/kvscore.h"
+#include "kvs_budget.hpp"
 #include "kvs_internal.hpp"
 
 namespace {
@@ -178,45 +179,6 @@ int check_budgets(const kvscore_problem* p, const int32_t* budgets, int* max_b) 
   return ok();
 }
 
-// Largest-remainder rounding of targets x (each in [lo, hi], summing to total up to fp64
-// rounding) to integers that sum to total exactly (RippleKV Eq. 5); equal remainders go to
-// the lower layer.
-int round_to_total(const std::vector<double>& x, int64_t total, int32_t lo, int32_t hi, int32_t* out) {
-  const int L = (int)x.size();
-  std::vector<int64_t> base(L);
-  std::vector<double> rem(L);
-  int64_t assigned = 0;
-  for (int l = 0; l < L; ++l) {
-    base[l] = (int64_t)std::floor(x[l]);
-    rem[l] = x[l] - (double)base[l];
-    assigned += base[l];
-  }
-  // remainders quantised to 1e-9 before ordering: targets that are equal in exact
-  // arithmetic but differ in the last fp64 bits then tie, and ties go to the lower layer
-  std::vector<int64_t> rq(L);
-  for (int l = 0; l < L; ++l) rq[l] = (int64_t)std::llround(rem[l] * 1e9);
-  std::vector<int> order(L);
-  for (int l = 0; l < L; ++l) order[l] = l;
-  std::stable_sort(order.begin(), order.end(), [&](int i, int j) { return rq[i] > rq[j]; });
-  int64_t extra = total - assigned;
-  for (int i = 0; i < L && extra > 0; ++i) {
-    const int l = order[i];
-    if (base[l] < hi) {
-      ++base[l];
-      --extra;
-    }
-  }
-  // Rounding of the fp64 targets can leave the sum one off in either direction.
-  for (int l = L - 1; l >= 0 && extra < 0; --l)
-    if (base[l] > lo) {
-      --base[l];
-      ++extra;
-    }
-  if (extra != 0) return fail(KVSCORE_EBUDGET, "could not distribute the total");
-  for (int l = 0; l < L; ++l) out[l] = (int32_t)base[l];
-  return ok();
-}
-
 // Decode attention problem: the model shape of p and the packed segment offsets (host
 // copy). Only the shape fields, head_dim and softmax_scale of p are used.
 int make_decdev(const kvscore_problem* p, const int64_t* off, kvs::DecDev& d) {
@@ -379,44 +341,11 @@ int kvscore_budget(const double* sens, int32_t num_layers, double ratio, double 
   // Eq. 11: clip to [1/gamma, gamma], rescale to mean one.
   if (gamma > 0 && std::isfinite(gamma))
     for (int l = 0; l < L; ++l) w[l] = std::min(std::max(w[l], 1.0 / gamma), gamma);
-  double sum = 0.0;
-  for (int l = 0; l < L; ++l) sum += w[l];
-  const double mean = sum / L;
-  for (int l = 0; l < L; ++l) w[l] /= mean;
-  // Eq. 12 targets.
-  std::vector<double> x(L);
-  bool inside = true;
-  for (int l = 0; l < L; ++l) {
-    x[l] = (double)total / L * w[l];
-    inside = inside && x[l] >= lo && x[l] <= hi;
-  }
-  if (!inside) {
-    // x_l = clip(lam * w_l, lo, hi) with sum = total: f(lam) is nondecreasing and piecewise
-    // linear; walk its breakpoints and solve on the segment that reaches the total.
-    std::vector<double> bp;
-    for (int l = 0; l < L; ++l) {
-      bp.push_back(lo / w[l]);
-      bp.push_back(hi / w[l]);
-    }
-    std::sort(bp.begin(), bp.end());
-    auto f = [&](double lam) {
-      double t = 0;
-      for (int l = 0; l < L; ++l) t += std::min(std::max(lam * w[l], (double)lo), (double)hi);
-      return t;
-    };
-    double a = 0.0, lam = bp.back();
-    for (double b : bp) {
-      const double fb = f(b);
-      if (fb >= (double)total) {
-        const double fa = f(a);
-        lam = (fb == fa) ? a : a + ((double)total - fa) * (b - a) / (fb - fa);
-        break;
-      }
-      a = b;
-    }
-    for (int l = 0; l < L; ++l) x[l] = std::min(std::max(lam * w[l], (double)lo), (double)hi);
-  }
-  return round_to_total(x, total, lo, hi, budgets_out);
+  // Eq. 11's mean-one rescale and Eq. 12's B/|A| go into lam: x_l = clip(lam * w_l, lo, hi)
+  // with sum x_l = total (lam = total / sum w when no clip is active), rounded exactly
+  if (kvs::exact_budgets_f64(w, 0, total, lo, hi, budgets_out))
+    return fail(KVSCORE_EBUDGET, "could not distribute the total");
+  return ok();
 }
 
 int kvscore_budget_pyramid(int32_t num_layers, double gamma, int64_t total, int32_t lo, int32_t hi,
@@ -426,7 +355,9 @@ int kvscore_budget_pyramid(int32_t num_layers, double gamma, int64_t total, int3
   if (!(gamma >= 0.0) || !std::isfinite(gamma)) return fail(KVSCORE_EINVAL, "gamma must be finite and >= 0");
   if (lo < 0 || hi < lo) return fail(KVSCORE_EINVAL, "need 0 <= lo <= hi");
   const int L = num_layers;
-  // PyramidKV curve, 0-based: f_l = (1 - l/(L-1))^gamma (the lowest layer 1, the top 0)
+  // PyramidKV curve, 0-based: f_l = (1 - l/(L-1))^gamma (the lowest layer 1, the top 0);
+  // for an integer gamma (up to 4096) the curve is rational and is taken exactly, as the
+  // integers (L-1-l)^gamma, whose common denominator goes into lam
   std::vector<double> f(L, 1.0);
   if (L > 1)
     for (int l = 0; l < L; ++l) f[l] = std::pow(1.0 - (double)l / (L - 1), gamma);
@@ -435,29 +366,12 @@ int kvscore_budget_pyramid(int32_t num_layers, double gamma, int64_t total, int3
   if (total < (int64_t)L * lo || total > reach)
     return fail(KVSCORE_EBUDGET, "total %lld outside [L*lo, %lld] (layers with factor 0 stay at lo)",
                 (long long)total, (long long)reach);
-  // x_l = clip(lo + lam * f_l, lo, hi) with sum = total: nondecreasing, piecewise linear in lam
-  auto g = [&](double lam) {
-    double t = 0;
-    for (int l = 0; l < L; ++l) t += std::min((double)lo + lam * f[l], (double)hi);
-    return t;
-  };
-  std::vector<double> bp;
-  for (int l = 0; l < L; ++l)
-    if (f[l] > 0) bp.push_back(((double)hi - lo) / f[l]);
-  std::sort(bp.begin(), bp.end());
-  double a = 0.0, lam = bp.empty() ? 0.0 : bp.back();
-  for (double b : bp) {
-    const double gb = g(b);
-    if (gb >= (double)total) {
-      const double ga = g(a);
-      lam = (gb == ga) ? a : a + ((double)total - ga) * (b - a) / (gb - ga);
-      break;
-    }
-    a = b;
-  }
-  std::vector<double> x(L);
-  for (int l = 0; l < L; ++l) x[l] = std::min((double)lo + lam * f[l], (double)hi);
-  return round_to_total(x, total, lo, hi, budgets_out);
+  // x_l = clip(lo + lam * f_l, lo, hi) with sum = total
+  const bool integral = gamma == std::floor(gamma) && gamma <= 4096.0;
+  const int rc = integral ? kvs::exact_budgets_pow(L, (uint64_t)gamma, total, lo, hi, budgets_out)
+                          : kvs::exact_budgets_f64(f, lo, total, lo, hi, budgets_out);
+  if (rc) return fail(KVSCORE_EBUDGET, "could not distribute the total");
+  return ok();
 }
 
 int kvscore_segment_offsets(const kvscore_problem* p, const int32_t* budgets, int64_t* offsets_out) {

@@ -2,6 +2,7 @@
 validates arguments on the host, and its host-only budget map agrees with the oracle."""
 import ctypes
 import math
+from fractions import Fraction
 import os
 import re
 import subprocess
@@ -178,6 +179,59 @@ def test_random_budgets_match_oracle(seed):
     got = api.budget(s, r, gamma, total, lo, hi)
     ref = oracle.layer_budgets(s, r, gamma, total, lo, hi)
     assert list(got) == ref
+
+
+def test_random_budgets_match_oracle_bulk():
+    """1000 random requests, all layers' integers equal to the oracle's (exact rationals)."""
+    rng = np.random.default_rng(7)
+    for i in range(1000):
+        L = int(rng.integers(1, 48))
+        s = rng.normal(size=L) * rng.uniform(0.01, 5)
+        if i % 7 == 0:
+            s[:] = 0.5  # constant profile
+        if i % 11 == 0:
+            s = np.round(s, 1)  # repeated values: equal multipliers, equal remainders
+        r = float(rng.choice([1.0, 2.0, 3.0, float(rng.uniform(1.0, 8.0))]))
+        gamma = math.inf if i % 3 else float(rng.uniform(1.0, 3.0))
+        lo = int(rng.integers(0, 80))
+        hi = lo + int(rng.integers(0, 5000))
+        total = int(rng.integers(L * lo, L * hi + 1))
+        got = api.budget(s, r, gamma, total, lo, hi)
+        ref = oracle.layer_budgets(s, r, gamma, total, lo, hi)
+        assert list(got) == ref, (i, L, r, gamma, lo, hi, total)
+        assert got.sum() == total and got.min() >= lo and got.max() <= hi
+
+
+def test_budget_near_tie_pin():
+    """Two remainders 1e-10 apart (RippleKV Eq. 12 rounded under Eq. 5): the larger one
+    takes the extra slot. With sens = (0, 1) the multipliers are (1, r) (Eq. 9-10), so
+    x = 3 (1, r) / (1 + r); r = 1 + 4e-10/3 puts x near 1.5 - 5e-11 and 1.5 + 5e-11.
+    Rounding the remainders to 1e-9 before ordering them would tie them and hand the slot
+    to layer 0."""
+    r = 1.0 + 4e-10 / 3
+    w = [Fraction(1.0), Fraction(math.exp(math.log(r) * 1.0))]
+    x = [3 * wl / sum(w) for wl in w]
+    rem = [xi - math.floor(xi) for xi in x]
+    assert 0 < rem[1] - rem[0] < Fraction(1, 10 ** 9)
+    assert list(api.budget([0.0, 1.0], r, math.inf, 3, 0, 3)) == [1, 2]
+    assert oracle.layer_budgets([0.0, 1.0], r, math.inf, 3, 0, 3) == [1, 2]
+    # the same near-tie between the first and the last of four layers, with a clip active
+    sens = [0.0, 0.3, 0.3, 1.0]
+    for total in (10, 11, 13):
+        assert list(api.budget(sens, r, math.inf, total, 2, 6)) == oracle.layer_budgets(sens, r, math.inf, total, 2, 6)
+
+
+def test_pyramid_budget_integer_gamma_against_oracle():
+    """Integer exponents: the curve is rational and both sides take it exactly."""
+    rng = np.random.default_rng(99)
+    for _ in range(300):
+        L = int(rng.integers(1, 40))
+        lo = int(rng.integers(0, 100))
+        hi = lo + int(rng.integers(0, 3000))
+        gamma = float(rng.integers(0, 13))
+        f = [1.0] if L == 1 else [(1 - l / (L - 1)) ** gamma for l in range(L)]
+        T = int(rng.integers(L * lo, sum(hi if x > 0 else lo for x in f) + 1))
+        assert api.budget_pyramid(L, gamma, T, lo, hi).tolist() == oracle.pyramid_budgets(L, T, lo, hi, gamma)
 
 
 @pytest.mark.parametrize("case", [dict(ratio=0.5), dict(gamma=0.5), dict(lo=-1), dict(total=10 ** 9)])
