@@ -126,6 +126,18 @@ def traffic_from(fetch_dir: str, write_dir: str, out_path: str, workload: str, c
     return rec
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, data, budgets, target_s: float, max_units: int):
     """The oracle (as it stands) on a bounded sample of units: score + top-k + gather."""
     import numpy as np
@@ -157,7 +169,9 @@ def cpu_baseline(w, data, budgets, target_s: float, max_units: int):
         tokens_equiv += n / (w.num_layers * w.num_kv_heads)
         if spent >= target_s:
             break
-    return {"value": tokens_equiv / spent, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+    threads = oracle.num_threads()
+    return {"value": tokens_equiv / spent, "unit": "tokens/s", "cores": threads, "threads": threads,
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{done} of {U} (layer, sequence, KV head) units of {w.name}, fp64 oracle score + full-sort "
                       f"top-k + gather, {spent:.1f} s; tokens/s = the units' share of the prompt tokens / time"}
 

@@ -90,6 +90,7 @@ extern "C" {
 
 #define KVSCORE_MAX_SEQS 64   /* sequences per call */
 #define KVSCORE_MAX_ROWS 1024 /* G*W query rows per unit */
+#define KVSCORE_MAX_UNITS 65535 /* L*S*Hkv units per call (a launch grid dimension) */
 
 #define KVSCORE_WS_ATTN_FWD 0
 #define KVSCORE_WS_SCORE 1
@@ -100,7 +101,7 @@ typedef struct kvscore_problem {
   int32_t num_seqs;          /* S, 1..KVSCORE_MAX_SEQS */
   int32_t num_layers;        /* L >= 1 */
   int32_t num_q_heads;       /* Hq, a multiple of num_kv_heads */
-  int32_t num_kv_heads;      /* Hkv >= 1 */
+  int32_t num_kv_heads;      /* Hkv >= 1; num_layers * num_seqs * num_kv_heads <= KVSCORE_MAX_UNITS */
   int32_t head_dim;          /* d: 64 or 128 */
   int32_t window;            /* W >= 1; every sequence must be longer than W */
   const int64_t* cu_seqlens; /* HOST array [S+1]: 0 = cu[0] < cu[1] < ... ; n_s = cu[s+1]-cu[s] */

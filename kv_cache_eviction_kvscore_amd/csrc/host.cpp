@@ -82,6 +82,12 @@ int make_dev(const kvscore_problem* p, kvs::Dev& d) {
   if (p->k_strides[2] >= ((int64_t)1 << 22) || p->v_strides[2] >= ((int64_t)1 << 22))
     return fail(KVSCORE_EINVAL, "token stride must be below 2^22 elements");
 
+  // units index gridDim.y or gridDim.z of every launch, whose limit is 65535
+  const int64_t units = (int64_t)p->num_layers * p->num_seqs * p->num_kv_heads;
+  if (units > kvs::kMaxUnits)
+    return fail(KVSCORE_EINVAL, "num_layers*num_seqs*num_kv_heads = %lld units exceeds %d", (long long)units,
+                kvs::kMaxUnits);
+
   d = kvs::Dev{};
   d.S = p->num_seqs;
   d.L = p->num_layers;
@@ -192,7 +198,7 @@ int make_decdev(const kvscore_problem* p, const int64_t* off, kvs::DecDev& d) {
   if (p->head_dim != 64 && p->head_dim != 128) return fail(KVSCORE_EINVAL, "head_dim must be 64 or 128");
   if (!off) return fail(KVSCORE_EINVAL, "host segment offsets are NULL");
   const int64_t U = (int64_t)p->num_layers * p->num_seqs * p->num_kv_heads;
-  if (U > 65535) return fail(KVSCORE_EINVAL, "too many segments (%lld)", (long long)U);
+  if (U > kvs::kMaxUnits) return fail(KVSCORE_EINVAL, "too many segments (%lld > %d)", (long long)U, kvs::kMaxUnits);
   if (off[0] != 0) return fail(KVSCORE_EINVAL, "segment offsets must start at 0");
   int64_t max_len = 0;
   for (int64_t u = 0; u < U; ++u) {

@@ -56,6 +56,7 @@ __device__ inline int wave_halves_min(int x) {
 }
 
 constexpr int kMaxSeqs = 64;
+constexpr int kMaxUnits = 65535;  // (layer, sequence, KV head) units: a grid dimension of every launch
 constexpr int kRowsPerTileMax = 256;  // query rows one workgroup holds (8 waves x 32 rows)
 constexpr int kMergeChunk = 8192;     // tokens per merge workgroup
 constexpr int kCompactRows = 32;      // packed rows per compaction workgroup

@@ -1,11 +1,11 @@
 // Score pass: per-token output-perturbation score partials for one query tile.
 //
-// DropKV page, "Methodology in Plain English" (engineering paragraph): the scoring
-// kernel reuses the forward's log-sum-exp, recomputes the logits tile by tile,
-// derives the attention weight on the fly and expands the squared distance
-// ||a||^2 + ||v||^2 - 2<a, v> so each value tile is read once per pass; the score of
-// token j is sum_i p_ij/(1-p_ij) * ||a_i - v_j||_2 (Key Contribution 1), summed over
-// the window rows and the query heads of the KV group. Mode ATTN scores sum_i p_ij
+// DropKV page, Key Contribution 1 (the score of token j is sum_i p_ij/(1-p_ij) *
+// ||a_i - v_j||_2, summed here over the window rows and the query heads of the KV
+// group) and "Methodology in Plain English" (the fused scorer's design). Here: p_ij
+// comes from q_i.k_j and the forward's lse_i, the distance from the expansion of
+// ||a_i - v_j||^2 into norms and a dot product, and every K and V tile is streamed
+// once per pass; no (row, token) matrix is ever stored. Mode ATTN scores sum_i p_ij
 // instead (PyramidKV page, "Observation Window and Aggregated Attention Eviction").
 //
 // score_prep: a_hat = fp16(a) (the MFMA operand), ||a_hat||^2 from the rounded values

@@ -12,15 +12,23 @@
 // pool_kernel (pool > 1): grid (4096-token tile, unit); the tile and its halo are loaded
 // into LDS (-inf outside the prefix) and every token takes the maximum of its window.
 //
-// One 1024-thread workgroup per (layer, sequence, KV head) unit. Radix select of the
-// k-th largest key over order-preserving uint32 images of the fp32 scores (4 passes of
-// 8 bits, per-wave LDS histograms merged in wave order, digit found by a wave scan),
-// which gives the threshold T and how many elements equal to T are taken; once the keys
-// sharing the threshold's prefix fit in LDS, the remaining passes count over that list.
+// topk_kernel: one 1024-thread workgroup per (layer, sequence, KV head) unit. Radix
+// select of the k-th largest key over order-preserving uint32 images of the fp32 scores
+// in three passes of 14, 9 and 9 bits, each counted into one shared LDS histogram (a
+// wave whose counted lanes share a bin adds their number with one atomic); the digit is
+// found by a two-level scan (each thread sums its run of bins, a block scan over the
+// threads' totals finds the thread where the count from the top reaches k). This gives
+// the threshold T and how many elements equal to T are taken. When the threshold's
+// 14-bit bin holds few enough keys, the second pass also appends them to an LDS list
+// and the last pass counts over that list instead of reading the scores again.
 // Then an ordered stream compaction in rounds of 4096 positions: prefix counts of
 // "surely kept" (window, or key > T) and "tied" (key == T) positions, from ballots within
 // a wave and LDS sums across waves, give every kept position its slot; ties are taken by
 // ascending position.
+//
+// heads_*_kernel (head budgets chosen jointly over a layer's KV heads) run a select of
+// their own, spread over many workgroups: four passes of 8 bits, one 256-bin histogram
+// per (chunk, head) summed per layer in a fixed order (described at those kernels).
 #include "kvs_internal.hpp"
 
 namespace kvs {
@@ -103,8 +111,8 @@ struct HistSmem {
   int tsum[NWAVES];
 };
 
-// LDS list of the keys that share the threshold's top byte (or top two bytes), so the
-// last radix passes need not read global memory again
+// LDS list of the keys that share the threshold's top 14 bits (filled during the second
+// pass), so the last radix pass need not read global memory again
 constexpr int kCandCap = 12288;
 struct CandSmem {
   unsigned key[kCandCap];

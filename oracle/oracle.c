@@ -11,8 +11,8 @@
  *     p_j/(1-p_j) * (a - v_j) (the softmax renormalises over the survivors), and the
  *     per-token eviction score is p_j/(1-p_j) * ||a - v_j||_2, computed from the
  *     full (unevicted) cache.
- *   - Same section: the practical score is accumulated over an observation window
- *     of the last w queries. Its "squared" variant is offered as mode SQ:
+ *   - Same section: in practice the per-token terms of the final w query rows are
+ *     summed into one score per token. Its "squared" variant is offered as mode SQ:
  *     sum_i (p_ij/(1-p_ij))^2 * ||a_i - v_j||^2; mode L2 (the default) is
  *     sum_i p_ij/(1-p_ij) * ||a_i - v_j||_2.
  *   - Query heads that share a KV head (grouped-query attention) are summed into

@@ -55,6 +55,9 @@ BAD = [
     dict(v_strides=(2 * 100 * 128, 100 * 128 + 3, 128)),
     dict(num_q_heads=1024 * 2, num_kv_heads=1, window=2),
     dict(num_seqs=0, cu_seqlens=[0]),
+    # units (L*S*Hkv) index a launch grid dimension: at most 65535
+    dict(num_layers=32768, num_q_heads=8, num_kv_heads=2),
+    dict(num_layers=1366, num_seqs=3, cu_seqlens=[0, 100, 200, 300], num_q_heads=32, num_kv_heads=16),
 ]
 
 
@@ -361,3 +364,13 @@ def test_topk_heads_and_compact_heads_validation():
     assert lib.kvscore_compact_heads(p.ref, fake, fake, bp, None, fake, fake, fake, None) == api.EINVAL
     assert lib.kvscore_compact_heads(p.ref, fake, fake, bp, fake, fake, ctypes.c_void_p(0x1004), fake,
                                      None) == api.EINVAL  # k_out misaligned
+
+
+def test_unit_limit_boundary():
+    """65535 units are accepted, one more is rejected with a message naming the limit."""
+    ok = make_problem(num_layers=65535 // 5, num_q_heads=5, num_kv_heads=5,
+                      k_strides=(5 * 100 * 128, 100 * 128, 128), v_strides=(5 * 100 * 128, 100 * 128, 128))
+    assert ok.workspace_size(api.WS_SCORE) > 0
+    bad = make_problem(num_layers=65536 // 4, num_q_heads=4, num_kv_heads=4)
+    assert bad.workspace_size(api.WS_SCORE) == 0
+    assert "65535" in api.load().kvscore_last_error().decode()
