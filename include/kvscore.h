@@ -292,6 +292,24 @@ int kvscore_decode_attn(const kvscore_problem* p, const void* q, const void* k_c
                         const int64_t* seg_offsets_host, const int64_t* seg_offsets, float* out, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The same decode attention with no workspace argument, for callers that cannot
+ * allocate device memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation). The split records go to a fixed device array of
+ * KVSCORE_DECODE_SCRATCH_BYTES inside the library; each GPU holds its own copy from the
+ * first call on it until the process ends. Nothing here allocates: no hipMalloc, no
+ * hipFree, no allocating library call. Arguments, outputs and errors as
+ * kvscore_decode_attn, plus KVSCORE_EWORKSPACE when the segments need more scratch than
+ * the array holds (kvscore_decode_workspace_size() > KVSCORE_DECODE_SCRATCH_BYTES; then
+ * use kvscore_decode_attn). Every call on one GPU uses that GPU's one array: calls that
+ * may overlap on one GPU (several streams, or several threads) race and must be ordered
+ * by the caller. The array keeps the last call's records; no call relies on its contents.
+ */
+#define KVSCORE_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+int kvscore_decode_attn_noalloc(const kvscore_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                                const int64_t* seg_offsets_host, const int64_t* seg_offsets, float* out, float* lse,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

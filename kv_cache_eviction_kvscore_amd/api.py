@@ -57,8 +57,9 @@ EXPORTS = (
     "kvscore_attn_fwd", "kvscore_score", "kvscore_merge", "kvscore_budget", "kvscore_budget_pyramid",
     "kvscore_segment_offsets",
     "kvscore_topk", "kvscore_compact", "kvscore_topk_heads", "kvscore_compact_heads",
-    "kvscore_decode_workspace_size", "kvscore_decode_attn",
+    "kvscore_decode_workspace_size", "kvscore_decode_attn", "kvscore_decode_attn_noalloc",
 )
+DECODE_SCRATCH_BYTES = 32 << 20  # KVSCORE_DECODE_SCRATCH_BYTES
 
 _lib = None
 
@@ -90,6 +91,7 @@ def load():
         "kvscore_compact_heads": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
         "kvscore_decode_workspace_size": (sz, [P, vp]),
         "kvscore_decode_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "kvscore_decode_attn_noalloc": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -350,3 +352,22 @@ def decode_attn(p: Problem, q, k_cache, v_cache, seg_off_host, seg_off_dev, out,
     _need(ws, nbytes, torch.uint8, "workspace")
     _check(load().kvscore_decode_attn(p.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.c_void_p(off.ctypes.data),
                                       _ptr(seg_off_dev), _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream(stream)))
+
+
+def decode_attn_noalloc(p: Problem, q, k_cache, v_cache, seg_off_host, seg_off_dev, out, lse, stream=None):
+    """:func:`decode_attn` without a workspace: the split records go to the library's fixed
+    device array (``DECODE_SCRATCH_BYTES``). Calls that overlap on one GPU race."""
+    off = _host_offsets(seg_off_host, p.units)
+    rows = int(off[-1])
+    nq = p.num_layers * p.num_seqs * p.num_q_heads
+    _need(q, nq * p.head_dim, torch.bfloat16, "q")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [L][S][Hq][d]")
+    _need(k_cache, rows * p.head_dim, torch.bfloat16, "k_cache")
+    _need(v_cache, rows * p.head_dim, torch.bfloat16, "v_cache")
+    _need(seg_off_dev, p.units + 1, torch.int64, "seg_offsets")
+    _need(out, nq * p.head_dim, torch.float32, "out")
+    _need(lse, nq, torch.float32, "lse")
+    _check(load().kvscore_decode_attn_noalloc(p.ref, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                              ctypes.c_void_p(off.ctypes.data), _ptr(seg_off_dev), _ptr(out),
+                                              _ptr(lse), _stream(stream)))

@@ -18,12 +18,25 @@
 //   merge in the wave (shuffles) and the waves in LDS, in a fixed order. The split's
 //   (max, sum, sum p v) per head go to the workspace.
 // decode_combine: one wave per (unit, head) merges the splits in ascending order.
+//
+// Fixed scratch (kvscore_decode_attn_noalloc): the split records live in the file-scope
+// array `scratch` instead of a caller workspace. Each GPU the library runs on holds its
+// own copy of the array until the process ends. Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in for the device symbol): the device
+// address comes from hipGetSymbolAddress, once per device, with that device current.
+#include <mutex>
 #include <type_traits>
 
 #include "kvs_internal.hpp"
 
 namespace kvs {
 namespace {
+
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = 64 * NWAVES;
@@ -281,6 +294,21 @@ void launch_partial_g(const DecDev& p, const __bf16* q, const __bf16* k, const _
 }
 
 }  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecDev& p, const void* q, const void* k, const void* v, const int64_t* off, float* out,
                          float* lse, void* ws, hipStream_t st) {

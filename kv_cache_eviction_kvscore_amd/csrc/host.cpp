@@ -464,6 +464,28 @@ size_t kvscore_decode_workspace_size(const kvscore_problem* p, const int64_t* se
   return ws_decode(d);
 }
 
+int kvscore_decode_attn_noalloc(const kvscore_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                                const int64_t* seg_offsets_host, const int64_t* seg_offsets, float* out, float* lse,
+                                void* stream) {
+  static_assert(kvs::kDecodeScratchBytes == KVSCORE_DECODE_SCRATCH_BYTES, "header and library agree");
+  kvs::DecDev d;
+  if (int rc = make_decdev(p, seg_offsets_host, d)) return rc;
+  if (!q || !k_cache || !v_cache || !seg_offsets || !out || !lse) return fail(KVSCORE_EINVAL, "NULL tensor argument");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(KVSCORE_EINVAL, "q/k_cache/v_cache not 16-byte aligned");
+  if (!aligned(out, 4) || !aligned(lse, 4)) return fail(KVSCORE_EINVAL, "out/lse not 4-byte aligned");
+  const size_t need = ws_decode(d);
+  if (need > kvs::kDecodeScratchBytes)
+    return fail(KVSCORE_EWORKSPACE,
+                "decode needs %zu bytes of scratch for these segments; the fixed array holds %zu "
+                "(use kvscore_decode_attn with a workspace)",
+                need, kvs::kDecodeScratchBytes);
+  void* ws = nullptr;
+  if (hipError_t e = kvs::decode_scratch(&ws)) return fail(KVSCORE_EDEVICE, "decode scratch: %s", hipGetErrorString(e));
+  return launched(kvs::launch_decode(d, q, k_cache, v_cache, seg_offsets, out, lse, ws, (hipStream_t)stream),
+                  "kvscore_decode_attn_noalloc");
+}
+
 int kvscore_decode_attn(const kvscore_problem* p, const void* q, const void* k_cache, const void* v_cache,
                         const int64_t* seg_offsets_host, const int64_t* seg_offsets, float* out, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream) {

@@ -133,6 +133,10 @@ constexpr int kMaxPoolSize = 255;
 constexpr int kDecodeMaxGroup = 8;  // query heads per KV head the decode kernels take
 hipError_t launch_decode(const DecDev& p, const void* q, const void* k, const void* v, const int64_t* off, float* out,
                          float* lse, void* ws, hipStream_t st);
+// device address of the decode pass's fixed scratch array on the current device (looked up
+// once per device)
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_compact(const Dev& p, const void* k, const void* v, const int64_t* seg_off, const int32_t* kept,
                           void* k_out, void* v_out, int max_budget, hipStream_t st);
 

@@ -374,3 +374,22 @@ def test_unit_limit_boundary():
     bad = make_problem(num_layers=65536 // 4, num_q_heads=4, num_kv_heads=4)
     assert bad.workspace_size(api.WS_SCORE) == 0
     assert "65535" in api.load().kvscore_last_error().decode()
+
+
+def test_decode_noalloc_rejects_scratch_beyond_its_array():
+    """kvscore_decode_attn_noalloc: segments whose split records exceed the fixed array
+    (KVSCORE_DECODE_SCRATCH_BYTES) are rejected with EWORKSPACE before any HIP call, so the
+    placeholder pointers are never used."""
+    L, Hkv, Hq, d = 1100, 8, 64, 128  # 8800 one-row segments x 8 heads x 130 floats > 32 MiB
+    p = api.Problem(num_seqs=1, num_layers=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, window=1,
+                    cu_seqlens=[0, 2], k_strides=(Hkv * 2 * d, 2 * d, d), v_strides=(Hkv * 2 * d, 2 * d, d))
+    off = np.arange(0, L * Hkv + 1, dtype=np.int64)
+    assert api.decode_workspace_size(p, off) > api.DECODE_SCRATCH_BYTES
+    fake = ctypes.c_void_p(0x1000)
+    lib = api.load()
+    rc = lib.kvscore_decode_attn_noalloc(p.ref, fake, fake, fake, ctypes.c_void_p(off.ctypes.data), fake, fake, fake,
+                                         None)
+    assert rc == api.EWORKSPACE
+    assert "scratch" in lib.kvscore_last_error().decode()
+    assert lib.kvscore_decode_attn_noalloc(p.ref, None, fake, fake, ctypes.c_void_p(off.ctypes.data), fake, fake,
+                                           fake, None) == api.EINVAL
