@@ -43,26 +43,6 @@ constexpr int NTHREADS = 64 * NWAVES;
 constexpr int UNROLL = 4;        // key steps in flight per lane
 constexpr float kSlack = 8.f;    // log2 units a logit may exceed the running max before a rescale
 
-// x summed over the lanes of its group of LANES (16 or 8 consecutive lanes), every lane
-// of the group receiving the sum (DPP within rows of 16 lanes)
-template <int LANES>
-__device__ inline float group_sum(float x) {
-  auto dpp = [](float v, auto ctrl) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
-  };
-  if constexpr (LANES == 16) {
-    x += dpp(x, std::integral_constant<int, 0x128>{});  // row_ror:8
-    x += dpp(x, std::integral_constant<int, 0x124>{});  // row_ror:4
-    x += dpp(x, std::integral_constant<int, 0x122>{});  // row_ror:2
-    x += dpp(x, std::integral_constant<int, 0x121>{});  // row_ror:1
-  } else {
-    x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror: lane i <-> 7 - i
-    x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
-    x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
-  }
-  return x;
-}
-
 __device__ inline float bf16lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kvs {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -53,6 +55,27 @@ __device__ inline HalfPair wave_halves(float x) {
 __device__ inline int wave_halves_min(int x) {
   const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
   return min((int)r[0], (int)r[1]);
+}
+
+// x summed over the lanes of its group of LANES consecutive lanes (16, 8 or 4), every lane
+// of the group receiving the sum: DPP within rows of 16 lanes, no LDS round trip
+template <int LANES>
+__device__ inline float group_sum(float x) {
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  static_assert(LANES == 16 || LANES == 8 || LANES == 4, "group size");
+  if constexpr (LANES == 16) {
+    x += dpp(x, std::integral_constant<int, 0x128>{});  // row_ror:8
+    x += dpp(x, std::integral_constant<int, 0x124>{});  // row_ror:4
+    x += dpp(x, std::integral_constant<int, 0x122>{});  // row_ror:2
+    x += dpp(x, std::integral_constant<int, 0x121>{});  // row_ror:1
+  } else {
+    if constexpr (LANES == 8) x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror: lane i <-> 7 - i
+    x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+    x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  }
+  return x;
 }
 
 constexpr int kMaxSeqs = 64;

@@ -13,28 +13,39 @@
 //   fp16, not bf16: the distance's error from rounding a is 2 (a - a_hat).(a - v), and
 //   fp16's 11-bit significand makes it eight times smaller; with bf16 a pair whose term
 //   dominates a token's score could miss a 1e-3 relative bound.
-// score_kernel: grid (key chunk, query tile, unit); 8 waves of 32 rows, two per SIMD, so
-//   one wave's VALU work overlaps the other's MFMAs. Orientation S = Q.K^T on
-//   v_mfma_f32_32x32x16_bf16 and X = A_hat.V^T (rows x keys) on v_mfma_f32_32x32x16_f16,
-//   with the row operands held in AGPRs and the accumulators written to VGPRs. K/V tiles
-//   of 64 keys go from HBM straight into LDS (global_load_lds_dwordx4, no register
-//   staging) through a ring of four buffers, so two tiles are in flight while one is
-//   computed. A tile keeps whole key rows (each DMA instruction moves four or eight full
-//   rows); the 16-byte chunks of row r are XOR-swizzled with a function of r so that the
-//   32 keys x 16 slots an MFMA operand needs are read conflict-free with ds_read_b128. A
-//   lane owns one key column and 16 rows of the 32x32 block, so the sum over rows stays in
-//   the lane (plus one half-wave exchange); the waves' column sums are added in LDS in
-//   wave order.
+// score_kernel: grid (key chunk, query tile, unit); 8 waves of one 32-row block each, two
+//   per SIMD (the kernel also builds with 4 waves of two blocks, one per SIMD; measured
+//   slower). Orientation S = Q.K^T on v_mfma_f32_32x32x16_bf16 and X = A_hat.V^T (rows x
+//   keys) on v_mfma_f32_32x32x16_f16, with the row operands held in AGPRs and the
+//   accumulators written to VGPRs. K/V tiles of 64 keys go from HBM straight into LDS
+//   (global_load_lds_dwordx4, no register staging) through a ring of four buffers, so two
+//   tiles are in flight while one is computed. A tile keeps whole key rows (each DMA
+//   instruction moves four or eight full rows); the 16-byte chunks of row r are
+//   XOR-swizzled with a function of r so that the 32 keys x 16 slots an MFMA operand needs
+//   are read conflict-free with ds_read_b128. A lane owns one key column and 16 rows of the
+//   32x32 block, so the sum over rows stays in the lane (plus one half-wave exchange); the
+//   waves' column sums are added in LDS in wave order.
+//   Software pipeline: a tile is two half tiles of 32 keys; each half tile's MFMAs run
+//   with the pair work of the previous half tile spread over their k-steps (one MFMA, then
+//   a share of the VALU work, and so on; an empty volatile asm statement ends each share,
+//   which keeps the compiler from gathering the VALU work after the MFMAs), so a wave keeps
+//   the matrix pipe and the VALU busy at once. Two accumulator sets alternate with fixed
+//   roles (block 0 and block 1 of a tile), so no registers are copied.
 //   The expansion runs on the matrix cores: one extra bf16 k-step multiplies
 //   (1, 1, 1, -||a_hat_i||^2/2 in three parts) by (-||v_j||^2/2 in three parts, 1, 1, 1)
 //   into the same accumulator; every part is an exact bf16 split, so X is -D/2 with
-//   D = ||a_hat - v||^2. ||v_j||^2 is summed from the tile in LDS (v_dot2_f32_bf16) one
-//   tile ahead of its use, and the same pass converts the tile's V to fp16 in place (exact
-//   in fp16's normal range) for the A_hat.V^T product. The Q.K^T chain gets an augmented
-//   k-step too: (-lse_i/scale in three bf16 parts) times (1, 1, 1), so its accumulator is
-//   ln p / scale and needs no per-row register. Per pair: 1/p = exp2(-acc * scale *
-//   log2 e), and c*sqrt(D) = sqrt(2) * sqrt(D/2) / (1/p - 1): three transcendentals and
-//   three other VALU instructions; the sqrt(2) (2 in mode SQ) is applied once per token.
+//   D = ||a_hat - v||^2. ||v_j||^2 is summed from the tile in LDS (v_dot2_f32_bf16, the
+//   key's lanes added by DPP) one tile ahead of its use, and the same pass converts the
+//   tile's V to fp16 in place (exact in fp16's normal range) for the A_hat.V^T product. The
+//   Q.K^T chain gets an augmented k-step too: (-lse_i/scale in three bf16 parts) times
+//   (1, 1, 1), so its accumulator is ln p / scale and needs no per-row register.
+//   Per pair, two forms (one wave-wide vote per half tile picks one):
+//   - every p of the half tile below 2^-8: p = exp2(acc * scale * log2 e), c = p + p^2,
+//     whose relative error against p/(1-p) is p^2 < 2^-16; term c * sqrt(D/2): two
+//     transcendentals and three other VALU instructions;
+//   - otherwise 1/p = exp2(-acc * scale * log2 e) and c*sqrt(D) = sqrt(2) * sqrt(D/2) /
+//     (1/p - 1): three transcendentals and three other VALU instructions.
+//   The sqrt(2) (2 in mode SQ) is applied once per token.
 //   Pairs (i, j*_i) are skipped (their term comes exactly from the forward); so are keys
 //   after a row's position. Both masks only act on tiles flagged in LDS, others run
 //   unmasked.
@@ -48,11 +59,12 @@ namespace kvs {
 namespace {
 
 constexpr int KT = 64;   // keys per LDS tile
-constexpr int KB = 32;   // keys per MFMA block
+constexpr int KB = 32;   // keys per half tile (one MFMA column block)
 constexpr int NBUF = 4;  // tile ring: computed, next (its ||v||^2 summed), two in flight
-constexpr int NWAVES = 8;                // 32 rows each: one query tile of up to 256 rows
-constexpr int NTHREADS = 64 * NWAVES;
-static_assert(NWAVES * 32 == kRowsPerTileMax, "a workgroup covers one query tile");
+// A workgroup covers one query tile of up to 256 rows: 8 waves of one 32-row block each
+// (two waves per SIMD) or 4 waves of two blocks (one wave per SIMD); RB = blocks per wave.
+constexpr int kMaxWaves = 8;
+constexpr int kScoreRowBlocks = 1;
 constexpr int kMaxTilesPerChunk = 1024;  // score_chunk <= 65536
 
 template <int D>
@@ -60,7 +72,7 @@ struct ScoreSmem {
   // tile ring: [buffer][tensor K, V][key][D] with row r's 16-byte chunks XOR-swizzled
   alignas(16) __bf16 tile[NBUF][2][KT * D];
   alignas(16) __bf16 nvx[2][KT][8];  // (-||v||^2/2 as hi, mid, lo bf16 parts, 1, 1, 1, 0, 0)
-  float red[3][NWAVES][KT];
+  float red[3][kMaxWaves][KT];
   int tlim[kRowsPerTileMax];
   int jst[kRowsPerTileMax];
   unsigned char flag[kMaxTilesPerChunk];
@@ -75,8 +87,10 @@ __device__ inline int swz(int r) {
   else return (r & 7) ^ ((r >> 3) & 1);
 }
 
-struct BlockAcc {
-  f32x16 S, X;
+// accumulators of one half tile: S = ln p / scale and X = -D/2 for each row block
+template <int RB>
+struct Half {
+  f32x16 S[RB], X[RB];
 };
 
 // x as three bf16 parts (hi, mid, lo) whose sum is x to about 24 bits
@@ -117,15 +131,14 @@ __global__ __launch_bounds__(256) void score_prep_kernel(int64_t rows, const flo
   }
 }
 
-template <int D, int MODE>
-__global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __restrict__ q,
-                                                         const __bf16* __restrict__ k,
-                                                         const __bf16* __restrict__ v,
-                                                         const _Float16* __restrict__ ahat,
-                                                         const float* __restrict__ na,
-                                                         const float* __restrict__ lse2,
-                                                         const int32_t* __restrict__ jstar,
-                                                         float* __restrict__ partial) {
+template <int D, int MODE, int RB>
+__global__ __launch_bounds__(512 / RB) __attribute__((amdgpu_waves_per_eu(2 / RB, 2 / RB))) void score_kernel(
+    Dev p, const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const _Float16* __restrict__ ahat, const float* __restrict__ na, const float* __restrict__ lse2,
+    const int32_t* __restrict__ jstar, float* __restrict__ partial) {
+  constexpr int NWAVES = 8 / RB;
+  constexpr int NTHREADS = 64 * NWAVES;
+  static_assert(NWAVES * RB * 32 == kRowsPerTileMax && NWAVES <= kMaxWaves, "a workgroup covers one query tile");
   constexpr int NKK = D / 16;             // k-steps per row operand
   constexpr int RS = D * 2;               // bytes per key row
   constexpr int CPK = D / 8;              // 16-byte chunks per key row
@@ -133,11 +146,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   constexpr bool WITH_V = MODE != 2;      // the attention-sum mode reads no V, a or norms
   constexpr int IPT = KT * CPK / 64;      // DMA wave instructions per tensor tile
   constexpr int NLD = (WITH_V ? 2 : 1) * IPT / NWAVES;  // DMA instructions per wave per tile
-  constexpr int PPR = 4;                  // pairs per lockstep group of the VALU work
   constexpr int KPW = KT / NWAVES;        // keys per wave in the norm pass and the column sums
   constexpr int LPK = 64 / KPW;           // lanes per key in the norm pass
   constexpr int CPN = CPK / LPK;          // 16-byte chunks per lane in the norm pass
-  static_assert(IPT % NWAVES == 0 && NLD >= 1 && NLD <= 4 && (NLD & (NLD - 1)) == 0, "tile shape");
+  static_assert(IPT % NWAVES == 0 && NLD >= 1 && NLD <= 8 && (NLD & (NLD - 1)) == 0, "tile shape");
   static_assert(KT % NWAVES == 0 && 64 % KPW == 0 && CPK % LPK == 0 && CPN >= 1, "norm pass shape");
   __shared__ ScoreSmem<D> sm;
 
@@ -152,10 +164,10 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
-  const int wrow0 = wave * 32;  // first tile row of this wave
-  const bool computing = wrow0 < p.RT;
+  const int wrow0 = wave * 32 * RB;  // first tile row of this wave
   const int64_t rbase = (int64_t)u * p.R + (int64_t)qt * p.RT;  // first row of this tile (global row index)
   const int rows_here = min(p.RT, p.R - qt * p.RT);
+  const bool computing = wrow0 < rows_here;
 
   // fields the lambdas below use, as locals: a by-reference capture of the by-value
   // argument would be re-read from kernel-argument memory with vector loads
@@ -204,31 +216,34 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       lds_dma16(base, doff[i], smb + (unsigned)(((it % NBUF) * 2 + tensor) * TBYTES + (f % IPT) * 1024));
     }
   };
+  auto issue_any = [&](int it) __attribute__((always_inline)) {
+    if (c0 + (int64_t)(it + 1) * KT <= c1) issue_full(it);
+    else issue(it);
+  };
   // -||v||^2/2 of tile it (landed, visible), into nvx[it & 1]: wave w sums keys
   // KPW*w .. KPW*w+KPW-1, LPK lanes per key (lanes key%KPW + KPW*c), CPN chunks each.
   auto norms = [&](int it) __attribute__((always_inline)) {
     if constexpr (!WITH_V) return;
     char* vt = (char*)sm.tile[it % NBUF][1];
-    const int key = KPW * wave + (lane % KPW), cg = lane / KPW;
+    // a key's LPK lanes are consecutive, so its sum is a DPP reduction within the lanes' row
+    const int key = KPW * wave + lane / LPK, cg = lane % LPK;
     float ss = 0.f;
+    u32x4 w[CPN];
+#pragma unroll
+    for (int e = 0; e < CPN; ++e) w[e] = *(const u32x4*)(vt + key * RS + (((CPN * cg + e) ^ swz<D>(key)) << 4));
 #pragma unroll
     for (int e = 0; e < CPN; ++e) {
-      const int c = CPN * cg + e;
-      u32x4* cp = (u32x4*)(vt + key * RS + ((c ^ swz<D>(key)) << 4));
-      const u32x4 w = *cp;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         // copy the element out first: a bit_cast of a vector-element lvalue reads element 0
-        const unsigned wm = w[m];
+        const unsigned wm = w[e][m];
         const bf16x2 x = __builtin_bit_cast(bf16x2, wm);
         ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
       }
-      *cp = bf16x8_to_f16x8(w);  // the A_hat.V^T product reads the tile in fp16
+      // the A_hat.V^T product reads the tile in fp16
+      *(u32x4*)(vt + key * RS + (((CPN * cg + e) ^ swz<D>(key)) << 4)) = bf16x8_to_f16x8(w[e]);
     }
-    // a shuffle here, not a VALU exchange chain: this side work is off the MFMA path, and
-    // the dependent DPP / permlane steps measured slower than LDS shuffles in flight
-#pragma unroll
-    for (int off = KPW; off < 64; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    ss = group_sum<LPK>(ss);
     const Split3 sp = split3(-0.5f * ss);
     bf16x8 w8 = {};
     w8[0] = sp.hi;
@@ -237,12 +252,12 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
     w8[3] = (__bf16)1.f;
     w8[4] = (__bf16)1.f;
     w8[5] = (__bf16)1.f;
-    *(bf16x8*)&sm.nvx[it & 1][key][0] = w8;  // the key's lanes store the same entry
+    if (cg == 0) *(bf16x8*)&sm.nvx[it & 1][key][0] = w8;
   };
 
   // ---- per-row masks in LDS, tile flags for rows whose argmax falls in this chunk
   for (int t = tid; t < ntiles; t += NTHREADS) sm.flag[t] = 0;
-  for (int t = tid; t < 3 * NWAVES * KT; t += NTHREADS) (&sm.red[0][0][0])[t] = 0.f;  // waves that never compute add zeros
+  for (int t = tid; t < 3 * kMaxWaves * KT; t += NTHREADS) (&sm.red[0][0][0])[t] = 0.f;  // waves that never compute add zeros
   for (int t = tid; t < kRowsPerTileMax; t += NTHREADS) {
     const bool ok = t < rows_here;
     sm.tlim[t] = ok ? (int)(n - W + (qt * p.RT + t) % W) : -1;
@@ -255,20 +270,22 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
     if (js >= c0 && js < c1) sm.flag[(js - c0) / KT] = 1;
   }
 
-  // ---- row operands (A side): lane row l32 of the wave's 32, k-slots 8h..8h+7
-  bf16x8 qf[NKK], aug, augs;
-  f16x8 af[NKK];
-  {
-    const int rt = wrow0 + l32;
-    const bool ok = computing && rt < rows_here;
+  // ---- row operands (A side) of the wave's RB blocks of 32 rows: lane row l32 of block
+  // r, k-slots 8h..8h+7
+  bf16x8 qf[RB][NKK], aug[RB], augs[RB];
+  f16x8 af[RB][NKK];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int rt = wrow0 + 32 * r + l32;
+    const bool ok = rt < rows_here;
     const __bf16* qrow = q + (rbase + (ok ? rt : 0)) * D;
     const _Float16* arow = ahat + (rbase + (ok ? rt : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       bf16x8 z = {};
       f16x8 zh = {};
-      qf[kk] = ok ? *(const bf16x8*)(qrow + 16 * kk + 8 * h) : z;
-      af[kk] = (ok && WITH_V) ? *(const f16x8*)(arow + 16 * kk + 8 * h) : zh;
+      qf[r][kk] = ok ? *(const bf16x8*)(qrow + 16 * kk + 8 * h) : z;
+      af[r][kk] = (ok && WITH_V) ? *(const f16x8*)(arow + 16 * kk + 8 * h) : zh;
     }
     // augmented k-step of the A.V^T chain: (1, 1, 1, -||a_hat||^2/2 in three parts) in slots 0..5
     bf16x8 w8 = {};
@@ -290,8 +307,8 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
       s8[1] = sp.mid;
       s8[2] = sp.lo;
     }
-    aug = w8;
-    augs = s8;
+    aug[r] = w8;
+    augs[r] = s8;
   }
   // B side of the Q.K^T k-step: 1 in slots 0..2 for every key
   bf16x8 ones3 = {};
@@ -303,62 +320,88 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   // the row operands live in AGPRs (MFMA reads them there), which leaves the VGPRs to
   // the accumulators the VALU consumes
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    asm volatile("" : "+a"(qf[kk]));
-    if constexpr (WITH_V) asm volatile("" : "+a"(af[kk]));
+  for (int r = 0; r < RB; ++r) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      asm volatile("" : "+a"(qf[r][kk]));
+      if constexpr (WITH_V) asm volatile("" : "+a"(af[r][kk]));
+    }
+    if constexpr (WITH_V) asm volatile("" : "+a"(aug[r]));
+    asm volatile("" : "+a"(augs[r]));
   }
-  if constexpr (WITH_V) asm volatile("" : "+a"(aug));
-  asm volatile("" : "+a"(augs));
   // sqrt(2) turns sqrt(D/2) into sqrt(D); mode SQ's p^2 (D/2)/(1-p)^2 needs 2; p needs 1
   const float out_scale = (MODE == 0) ? 1.41421356237309515f : (MODE == 1 ? 2.f : 1.f);
   // byte offset, within a tensor tile, of this lane's operand chunk (key l32, slots
-  // 16kk + 8h .. +7) for k-step kk; block b adds 32 rows
+  // 16kk + 8h .. +7) for k-step kk; half tile b adds 32 rows
   const int kbase = l32 * RS, khs = h ^ swz<D>(l32);
   auto koff = [&](int kk) __attribute__((always_inline)) { return kbase + (((2 * kk) ^ khs) << 4); };
 
-  // adds the terms of pairs pi0 .. pi0+PPR-1 (pair = row of the output layout: element r
-  // is row 8(r/4) + 4h + (r%4)) to col, written stage by stage so the PPR independent
-  // chains interleave
-  auto pair_terms = [&](auto masked, const BlockAcc& acc, const int pi0, const int key, float& col)
+  // The pair terms of pairs [pi0, pi0 + NP) of a half tile's accumulators, added to col
+  // (pair pi = 16r + e: row 32r + 8(e/4) + 4h + (e%4) of the wave, the lane's key
+  // column). Stage by stage over the NP pairs, so their chains interleave.
+  // kind: 0 = small p (every p of the half tile below 2^-8: p/(1-p) = p + p^2 to 2^-16
+  // relative), 1 = the exact form, 2 = the exact form with the masks (causal limit, the
+  // row's isolated argmax)
+  auto pair_terms = [&](auto kind, auto np, Half<RB>& acc, const int pi0, const int key, float& col)
       __attribute__((always_inline)) {
-    float x[PPR], y[PPR];  // the pair's term is x * y
+    constexpr int NP = decltype(np)::value;
+    constexpr int KIND = decltype(kind)::value;
+    static_assert(16 % NP == 0, "a slice stays within one row block");
+    const int rb = pi0 >> 4;
+    float sv[NP], xv[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      sv[i] = acc.S[rb][(pi0 + i) & 15];
+      if constexpr (MODE != 2) xv[i] = acc.X[rb][(pi0 + i) & 15];
+    }
+    float x[NP], y[NP];  // the pair's term is x * y
     if constexpr (MODE == 2) {
 #pragma unroll
-      for (int i = 0; i < PPR; ++i) {
-        x[i] = __builtin_amdgcn_exp2f(acc.S[pi0 + i] * c1s);  // p itself
+      for (int i = 0; i < NP; ++i) {
+        x[i] = __builtin_amdgcn_exp2f(sv[i] * c1s);  // p itself
         y[i] = 1.f;
       }
-    } else {
-      // e = 1/p and r = 1/(e - 1) = p/(1-p): e >= 2 on every unmasked pair, so r is finite
-      // (0 when p underflows); a masked pair's value is never added
-      float e[PPR], r[PPR];
+    } else if constexpr (KIND == 0) {
+      // c = p/(1-p) = p (1 + p + p^2 + ...) = p + p^2 up to a relative p^2 < 2^-16
 #pragma unroll
-      for (int i = 0; i < PPR; ++i) e[i] = __builtin_amdgcn_exp2f(acc.S[pi0 + i] * nc1s);
-#pragma unroll
-      for (int i = 0; i < PPR; ++i) r[i] = __builtin_amdgcn_rcpf(e[i] - 1.f);
+      for (int i = 0; i < NP; ++i) {
+        const float pp = __builtin_amdgcn_exp2f(sv[i] * c1s);
+        x[i] = fmaf(pp, pp, pp);
+      }
       if constexpr (MODE == 0) {
-        // p/(1-p) sqrt(D/2): three transcendentals and three other VALU instructions. The
-        // matrix cores leave room for about four VALU instructions of any kind per MFMA,
-        // so this beats a form with one transcendental less and three more plain ones.
 #pragma unroll
-        for (int i = 0; i < PPR; ++i) {
-          x[i] = r[i];
-          y[i] = __builtin_amdgcn_sqrtf(fabsf(acc.X[pi0 + i]));
-        }
+        for (int i = 0; i < NP; ++i) y[i] = __builtin_amdgcn_sqrtf(fabsf(xv[i]));
       } else {
-        // p^2 (D/2) / (1-p)^2
 #pragma unroll
-        for (int i = 0; i < PPR; ++i) {
-          x[i] = r[i] * r[i];
-          y[i] = fabsf(acc.X[pi0 + i]);
+        for (int i = 0; i < NP; ++i) {
+          x[i] = x[i] * x[i];
+          y[i] = fabsf(xv[i]);
+        }
+      }
+    } else {
+      // e = 1/p and 1/(e - 1) = p/(1-p): e >= 2 on every unmasked pair, so it is finite
+      // (0 when p underflows); a masked pair's value is never added
+      float e[NP];
+#pragma unroll
+      for (int i = 0; i < NP; ++i) e[i] = __builtin_amdgcn_exp2f(sv[i] * nc1s);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) x[i] = __builtin_amdgcn_rcpf(e[i] - 1.f);
+      if constexpr (MODE == 0) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) y[i] = __builtin_amdgcn_sqrtf(fabsf(xv[i]));
+      } else {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          x[i] = x[i] * x[i];
+          y[i] = fabsf(xv[i]);
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < PPR; ++i) {
-      if constexpr (decltype(masked)::value) {
-        const int rr = pi0 + i;
-        const int rt = wrow0 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+    for (int i = 0; i < NP; ++i) {
+      if constexpr (KIND == 2) {
+        const int pi = pi0 + i, e = pi & 15;
+        const int rt = wrow0 + 32 * (pi >> 4) + 8 * (e >> 2) + 4 * h + (e & 3);
         col += (key > sm.tlim[rt] || key == sm.jst[rt]) ? 0.f : x[i] * y[i];
       } else if constexpr (MODE == 2) {
         col += x[i];
@@ -366,39 +409,113 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
         col = fmaf(x[i], y[i], col);
       }
     }
+    // an empty volatile asm statement that reads and redefines the sum: the slice is complete
+    // here (the compiler otherwise gathers every slice after the MFMAs)
+    asm volatile("" : "+v"(col));
   };
-  // the MFMAs of 32-key block b of ring tile it: S = ln p / scale, X = -D/2
-  auto mfma_block = [&](int it, int b) __attribute__((always_inline)) {
+  // One half tile (it, b): the MFMAs of keys 32b .. 32b+31 of ring tile it against the
+  // wave's RB row blocks (S = ln p / scale, X = -D/2; four independent accumulation chains,
+  // S and X of two row blocks, keep the matrix pipe issuing back to back), with the pair
+  // work of the previous half tile (pv, from tile pit, block pb) spread over its k-steps:
+  // each k-step's MFMAs are followed by a slice of that work and a scheduling fence, so the
+  // matrix pipe and the VALU run together within the wave. Returns the previous half
+  // tile's column sum over the wave's rows (both half-waves hold it).
+  constexpr int PPK = 16 * RB / NKK;  // pairs of the previous half tile per k-step
+  auto half_tile = [&](auto kind, auto first, int it, int b, Half<RB>& acc, Half<RB>& pv, int pit, int pb)
+      __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first)::value;
     const char* kt = (const char*)sm.tile[it % NBUF][0] + b * KB * RS;
-    BlockAcc acc;
+    const int pkey = (int)(c0 + (int64_t)pit * KT + pb * KB) + l32;
     bf16x8 nv = {};
     if constexpr (WITH_V) nv = *(const bf16x8*)&sm.nvx[it & 1][b * KB + l32][0];
+    float col = 0.f;
+    bf16x8 kx = *(const bf16x8*)(kt + koff(0));
+    f16x8 vx = {};
+    if constexpr (WITH_V) vx = *(const f16x8*)(kt + TB + koff(0));  // converted to fp16 by the norm pass
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const bf16x8 kx = *(const bf16x8*)(kt + koff(kk));
-      acc.S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[kk], kx, kk ? acc.S : f32x16{}, 0, 0, 0);
-      if constexpr (WITH_V) {
-        const f16x8 vx = *(const f16x8*)(kt + TB + koff(kk));  // converted to fp16 by the norm pass
-        acc.X = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk], vx, kk ? acc.X : f32x16{}, 0, 0, 0);
+      bf16x8 kxn = kx;
+      f16x8 vxn = vx;
+      if (kk + 1 < NKK) {  // the next k-step's operands are read while this one's MFMAs run
+        kxn = *(const bf16x8*)(kt + koff(kk + 1));
+        if constexpr (WITH_V) vxn = *(const f16x8*)(kt + TB + koff(kk + 1));
+      }
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        acc.S[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[r][kk], kx, kk ? acc.S[r] : f32x16{}, 0, 0, 0);
+        if constexpr (WITH_V) acc.X[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[r][kk], vx, kk ? acc.X[r] : f32x16{}, 0, 0, 0);
       }
       if (kk == NKK / 2) {  // the augmented k-steps sit mid-chain, off the chains' tails
-        acc.S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(augs, ones3, acc.S, 0, 0, 0);
-        if constexpr (WITH_V) acc.X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aug, nv, acc.X, 0, 0, 0);
-      }
-    }
-    return acc;
-  };
-  // a column's sum over the wave rows of red, in wave order (every flush adds the same way)
-  auto col_sum = [&](const float(*rd)[KT], int col) __attribute__((always_inline)) {
-    float acc = rd[0][col];
 #pragma unroll
-    for (int w = 1; w < NWAVES; ++w) acc += rd[w][col];
-    return acc * out_scale;
+        for (int r = 0; r < RB; ++r) {
+          acc.S[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(augs[r], ones3, acc.S[r], 0, 0, 0);
+          if constexpr (WITH_V) acc.X[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aug[r], nv, acc.X[r], 0, 0, 0);
+        }
+      }
+      if constexpr (!FIRST) {
+        pair_terms(kind, std::integral_constant<int, PPK>{}, pv, kk * PPK, pkey, col);
+        // within the k-step: one MFMA, then a share of the slice's VALU work, and so on; a
+        // wave issues in order, so MFMAs issued back to back would hold the VALU work behind
+        // them
+        constexpr int MPK = (WITH_V ? 2 : 1) * RB;  // MFMAs per k-step (twice that at the augmented one)
+        constexpr int VS = PPK * (MODE == 2 ? 3 : 6);  // VALU instructions of the slice
+        if (kk == NKK / 2) {
+#pragma unroll
+          for (int m = 0; m < 2 * MPK; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, (VS + 2 * MPK - 1) / (2 * MPK), 0);
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < MPK; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, (VS + MPK - 1) / MPK, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      kx = kxn;
+      vx = vxn;
+    }
+    if constexpr (FIRST) return 0.f;
+    const HalfPair c2 = wave_halves(col);
+    return c2.lo + c2.hi;
   };
-  auto flush_share = [&](int it) __attribute__((always_inline)) {  // tile it's columns KPW*w ..
-    const int fcol = KPW * wave + (lane % KPW);
-    const int64_t j = c0 + (int64_t)it * KT + fcol;
-    if (j < c1) pout[j] = col_sum(sm.red[it % 3], fcol);  // the lanes of a column store the same value
+  // the pair work of the last half tile, alone
+  auto tail_pairs = [&](auto kind, Half<RB>& pv, int pit, int pb) __attribute__((always_inline)) {
+    const int pkey = (int)(c0 + (int64_t)pit * KT + pb * KB) + l32;
+    float col = 0.f;
+#pragma unroll
+    for (int pi = 0; pi < 16 * RB; pi += PPK) pair_terms(kind, std::integral_constant<int, PPK>{}, pv, pi, pkey, col);
+    const HalfPair c2 = wave_halves(col);
+    return c2.lo + c2.hi;
+  };
+  // the column sums of tile it, columns KPW*w .. KPW*w+KPW-1: flush_load reads the waves'
+  // row sums from LDS, flush_store adds them in wave order and writes the scores; between
+  // the two the LDS reads are in flight
+  auto flush_load = [&](int it, float (&fv)[NWAVES]) __attribute__((always_inline)) {
+    // the lane index taken afresh (an opaque v_mbcnt): kept from the prologue, the column
+    // offset would stay live across the whole loop only for this use
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int fcol = KPW * wave + (ln % KPW);
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) fv[w] = sm.red[it % 3][w][fcol];
+  };
+  auto flush_store = [&](int it, const float (&fv)[NWAVES]) __attribute__((always_inline)) {
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    if (ln >= KPW) return;
+    const int64_t j = c0 + (int64_t)it * KT + KPW * wave + ln;
+    float acc = fv[0];
+#pragma unroll
+    for (int w = 1; w < NWAVES; ++w) acc += fv[w];
+    if (j < c1) pout[j] = acc * out_scale;
+  };
+  auto flush_share = [&](int it) __attribute__((always_inline)) {
+    float fv[NWAVES];
+    flush_load(it, fv);
+    flush_store(it, fv);
   };
   // tile flags as bits: lane L holds tiles 32L .. 32L+31 (a chunk has at most 1024 tiles)
   static_assert(kMaxTilesPerChunk <= 32 * 64, "flag bits");
@@ -410,15 +527,42 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  using K2 = std::integral_constant<int, 2>;
+  // whether every pair of a half tile has p below 2^-8: S = ln p / scale, so p < 2^-8 is
+  // S < -8 / (scale log2 e); one wave-wide vote
+  const float small_lim = -8.f / c1s;
+  auto all_small = [&](const Half<RB>& acc) __attribute__((always_inline)) {
+    if constexpr (MODE == 2) return false;
+    float m = acc.S[0][0];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, acc.S[r][e]);
+    return __ballot(m >= small_lim) == 0;
+  };
+  // the pair work of pv (tile pit, block pb) with the right kind, run with the MFMAs of (it, b)
+  auto step = [&](bool special_prev, auto first, int it, int b, Half<RB>& acc, Half<RB>& pv, int pit, int pb)
+      __attribute__((always_inline)) {
+    if (special_prev) return half_tile(K2{}, first, it, b, acc, pv, pit, pb);
+    if (all_small(pv)) return half_tile(K0{}, first, it, b, acc, pv, pit, pb);
+    return half_tile(K1{}, first, it, b, acc, pv, pit, pb);
+  };
+  auto tail = [&](bool special_prev, Half<RB>& pv, int pit, int pb) __attribute__((always_inline)) {
+    if (special_prev) return tail_pairs(K2{}, pv, pit, pb);
+    if (all_small(pv)) return tail_pairs(K0{}, pv, pit, pb);
+    return tail_pairs(K1{}, pv, pit, pb);
+  };
   // Ring schedule (one barrier per tile). At the top of iteration t, tiles t+1 and t+2
   // are in flight; waiting until at most NLD of this wave's DMA instructions are
-  // outstanding means tile t+1 has landed. After the barrier: the column sums of tile t-1
+  // outstanding means tile t+1 has landed. After the barrier: the column sums of tile t-2
   // are complete and are written; buffer (t+3)%4, last read by tile t-1's MFMAs, takes
-  // tile t+3; tile t+1's norms are summed; tile t is computed from buffer t%4 with the
-  // norms summed one iteration earlier. The two waves on a SIMD (w and w + NWAVES/2) do
-  // the side work at different points of the iteration, so the SIMD's MFMA pipe keeps a
-  // wave to feed it.
+  // tile t+3; tile t+1's norms are summed and its V converted. Then the two half tiles of
+  // tile t: each one's MFMAs run with the previous half tile's pair work interleaved (the
+  // last half tile of tile t-1, then the first of tile t). The pair work of a half tile
+  // therefore ends one half tile later, and a tile's column sums are complete after the
+  // barrier two iterations on.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 landed
   __syncthreads();
   for (int i = 0; i < 32; ++i) {
@@ -426,51 +570,56 @@ __global__ __launch_bounds__(NTHREADS) void score_kernel(Dev p, const __bf16* __
     if (t < ntiles && sm.flag[t]) flagbits |= 1u << i;
   }
   norms(0);
-  if (ntiles > 1) issue(1);
-  if (ntiles > 2) issue(2);
+  if (ntiles > 1) issue_any(1);
+  if (ntiles > 2) issue_any(2);
+  // two accumulator sets with fixed roles: A holds block 0 of a tile, B block 1 (no copies
+  // between half tiles)
+  Half<RB> A, B;
+  bool sp_prev = false;  // tile t-1 needs the masked pair work
   for (int t = 0; t < ntiles; ++t) {
     if (t + 2 < ntiles) {
-      if constexpr (NLD == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      if constexpr (NLD == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if constexpr (NLD == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       else if constexpr (NLD == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     lds_barrier();  // the column stores of earlier tiles stay in flight
+    // the side work (flush, DMA, norms) is mostly waiting on LDS round trips; the two waves
+    // of a SIMD (w and w + NWAVES/2 with two waves per SIMD) do it at different points of
+    // the iteration, so one wave's MFMAs and VALU work run while the other waits
     auto side = [&]() __attribute__((always_inline)) {
-      if (t >= 1) flush_share(t - 1);
-      if (t + 3 < ntiles) {
-        if (c0 + (int64_t)(t + 4) * KT <= c1) issue_full(t + 3);
-        else issue(t + 3);
-      }
+      float fv[NWAVES];
+      if (t >= 2) flush_load(t - 2, fv);
+      if (t + 3 < ntiles) issue_any(t + 3);
       if (t + 1 < ntiles) norms(t + 1);
+      if (t >= 2) flush_store(t - 2, fv);
     };
-    const bool early = !computing || wave < NWAVES / 2;
+    const bool early = !computing || RB == 2 || wave < NWAVES / 2;
     if (early) side();
     if (computing) {
       const bool sp = special(t);
-#pragma unroll
-      for (int b = 0; b < KT / KB; ++b) {
-        if (b == 1 && !early) side();
-        const BlockAcc acc = mfma_block(t, b);
-        float col = 0.f;
-        const int key = (int)(c0 + (int64_t)t * KT + b * KB) + l32;
-        if (sp) {
-#pragma unroll
-          for (int pi = 0; pi < 16; pi += PPR) pair_terms(T_{}, acc, pi, key, col);
-        } else {
-#pragma unroll
-          for (int pi = 0; pi < 16; pi += PPR) pair_terms(F_{}, acc, pi, key, col);
-        }
-        {
-          const HalfPair c2 = wave_halves(col);  // both half-waves hold the sum and write it
-          col = c2.lo + c2.hi;
-        }
-        sm.red[t % 3][wave][b * KB + l32] = col;
+      // block 0 of tile t into A, with the pair work of block 1 of tile t-1 (B)
+      if (t == 0) {
+        half_tile(K1{}, T_{}, t, 0, A, B, 0, 0);
+      } else {
+        const float cs = step(sp_prev, F_{}, t, 0, A, B, t - 1, 1);
+        sm.red[(t - 1) % 3][wave][KB + l32] = cs;
       }
+      if (!early) side();
+      // block 1 of tile t into B, with the pair work of block 0 of tile t (A)
+      const float cs = step(sp, F_{}, t, 1, B, A, t, 0);
+      sm.red[t % 3][wave][l32] = cs;
+      sp_prev = sp;
     }
   }
+  if (computing) {  // the pair work of the last half tile
+    const float cs = tail(sp_prev, B, ntiles - 1, 1);
+    sm.red[(ntiles - 1) % 3][wave][KB + l32] = cs;
+  }
   __syncthreads();
+  if (ntiles >= 2) flush_share(ntiles - 2);
   flush_share(ntiles - 1);
 }
 
@@ -483,20 +632,21 @@ hipError_t launch_score(const Dev& p, const void* q, const void* k, const void* 
   float* na = (float*)((char*)ws + (size_t)rows * p.d * 2);
   float* l2 = na + rows;
   const dim3 gp((unsigned)((rows + 3) / 4)), gs(p.score_chunks, p.Tq, p.U);
+  constexpr int RBL = kScoreRowBlocks;
   auto run = [&](auto kern) {
-    hipLaunchKernelGGL(kern, gs, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+    hipLaunchKernelGGL(kern, gs, dim3(512 / RBL), 0, st, p, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                        (const _Float16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
   };
   if (p.d == 128) {
     hipLaunchKernelGGL(score_prep_kernel<128>, gp, dim3(256), 0, st, rows, a, lse, ahat, na, l2);
-    if (p.mode == 0) run(score_kernel<128, 0>);
-    else if (p.mode == 1) run(score_kernel<128, 1>);
-    else run(score_kernel<128, 2>);
+    if (p.mode == 0) run(score_kernel<128, 0, RBL>);
+    else if (p.mode == 1) run(score_kernel<128, 1, RBL>);
+    else run(score_kernel<128, 2, RBL>);
   } else {
     hipLaunchKernelGGL(score_prep_kernel<64>, gp, dim3(256), 0, st, rows, a, lse, ahat, na, l2);
-    if (p.mode == 0) run(score_kernel<64, 0>);
-    else if (p.mode == 1) run(score_kernel<64, 1>);
-    else run(score_kernel<64, 2>);
+    if (p.mode == 0) run(score_kernel<64, 0, RBL>);
+    else if (p.mode == 1) run(score_kernel<64, 1, RBL>);
+    else run(score_kernel<64, 2, RBL>);
   }
   return hipGetLastError();
 }
