@@ -32,9 +32,10 @@ def say(msg: str) -> None:
 
 
 def run_gpu(w: Workload, mode: int = api.MODE_L2, data=None, k_layout: str = "head_major", pool: int = 1,
-            n_sink: int = 0, heads: bool = False):
+            n_sink: int = 0, heads: bool = False, budgets=None):
     """Generate (or take) inputs on the GPU and run the whole pipeline once (pool > 1: rank by
-    the max-pooled score; n_sink: pinned first tokens, budgets then start at W + sinks)."""
+    the max-pooled score; n_sink: pinned first tokens, budgets then start at W + sinks;
+    budgets: int [S][L] to use instead of the workload's own map)."""
     if data is None:
         data = synth.generate(w, "cuda")
     q, k, v = data["q"], data["k"], data["v"]
@@ -42,7 +43,8 @@ def run_gpu(w: Workload, mode: int = api.MODE_L2, data=None, k_layout: str = "he
         k = k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
         v = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
     prob = pipeline.problem_for(w, k, v, mode)
-    budgets = pipeline.workload_budgets(w, n_sink)
+    if budgets is None:
+        budgets = pipeline.workload_budgets(w, n_sink)
     pipe = pipeline.Pipeline(prob, budgets, pool=pool, n_sink=n_sink, heads=heads)
     pipe.run(q, k, v)
     torch.cuda.synchronize()
@@ -164,3 +166,46 @@ def sample_units(w: Workload, count: int) -> List[int]:
     while len(picks) < count:
         picks.add(int(rng.integers(0, U)))
     return sorted(picks)[:max(count, len(picks))]
+
+
+def cover_units(w: Workload) -> List[int]:
+    """Units that cover every layer index, every KV-head index and every sequence at least
+    once: layer l takes head l mod Hkv and sequence (l div Hkv) mod S, plus the first and
+    the last unit (Hkv and S are at most L in every workload checked this way)."""
+    U = w.num_layers * w.num_seqs * w.num_kv_heads
+    picks = {0, U - 1}
+    for l in range(w.num_layers):
+        g = l % w.num_kv_heads
+        s = (l // w.num_kv_heads) % w.num_seqs
+        picks.add((l * w.num_seqs + s) * w.num_kv_heads + g)
+    units = sorted(picks)
+    covered = {unit_coords(w, u) for u in units}
+    assert {c[0] for c in covered} == set(range(w.num_layers))
+    assert {c[2] for c in covered} == set(range(w.num_kv_heads))
+    assert {c[1] for c in covered} == set(range(w.num_seqs))
+    return units
+
+
+def check_selection_every_unit(w: Workload, run) -> int:
+    """Selection and compaction of every unit, on the GPU's own fp32 scores (integer and byte
+    work, so exact): kept positions equal to the oracle's full sort of those scores, and the
+    packed K/V rows equal to the oracle's naive gather of the input rows at those positions.
+    Returns the number of units checked."""
+    out, cu = run["out"], w.cu_seqlens()
+    seg = out["seg_off"]
+    pool, n_sink = run["pipe"].pool, run["pipe"].n_sink
+    U = w.num_layers * w.num_seqs * w.num_kv_heads
+    for u in range(U):
+        l, s, g = unit_coords(w, u)
+        n = w.seqlens[s]
+        b = int(seg[u + 1] - seg[u])
+        sc = out["score"][l, g, cu[s]:cu[s + 1]].cpu().numpy().astype(np.float64)
+        kept = out["kept"][seg[u]:seg[u + 1]].cpu().numpy().astype(np.int64)
+        own = oracle.kept_positions(sc, n, w.window, b, pool, n_sink)
+        np.testing.assert_array_equal(kept, own, err_msg=f"unit {u}")
+        kb = synth.bf16_bits(run["k"][l, g, cu[s]:cu[s + 1]])
+        vb = synth.bf16_bits(run["v"][l, g, cu[s]:cu[s + 1]])
+        gk, gv = oracle.gather(kb, vb, kept)
+        np.testing.assert_array_equal(synth.bf16_bits(out["k_out"][seg[u]:seg[u + 1]]), gk, err_msg=f"unit {u}")
+        np.testing.assert_array_equal(synth.bf16_bits(out["v_out"][seg[u]:seg[u + 1]]), gv, err_msg=f"unit {u}")
+    return U

@@ -1,7 +1,8 @@
 """GPU parity: the HIP pipeline (through the C ABI) against the fp64 oracle.
 
-Workloads 1 and 2 are checked on every unit; 3, 4 and 5 at full size on sampled units
-(first, last, one per sequence, a few random), every output of each sampled unit.
+Workloads 1 and 2 are checked on every unit; 3, 4 and 5 at full size on one unit per
+layer (every layer, KV-head and sequence index covered), every output of each, plus the
+selection and compaction of every unit on the GPU's own scores.
 Edge cases cover one candidate, empty and full selections, G = 1 / W = 1, d = 64,
 ragged sequences, more than 256 rows per unit (several query tiles), token-major
 strides, ties, and run-to-run determinism.
@@ -10,10 +11,12 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+
 from kv_cache_eviction_kvscore_amd import api, pipeline, synth
 from kv_cache_eviction_kvscore_amd.configs import WORKLOADS, Workload, small_variant
 
-from parity import check_unit, run_gpu, sample_units, say
+from parity import check_selection_every_unit, check_unit, cover_units, run_gpu, sample_units, say
 
 pytestmark = pytest.mark.gpu
 
@@ -42,19 +45,14 @@ def test_workload2_all_units():
     _check_all(w, list(range(w.num_kv_heads)))
 
 
-def test_workload3_sampled_units():
-    w = WORKLOADS[3]
-    _check_all(w, sample_units(w, 4))
-
-
-def test_workload4_sampled_units():
-    w = WORKLOADS[4]
-    _check_all(w, sample_units(w, 3))
-
-
-def test_workload5_sampled_units():
-    w = WORKLOADS[5]
-    _check_all(w, sample_units(w, 6))
+@pytest.mark.parametrize("wid", [3, 4, 5])
+def test_full_workloads_every_layer_and_head(wid):
+    """Workloads 3-5 at full size: every output of one unit per layer (covering every
+    KV-head index and, for the ragged batch, every sequence) against the fp64 oracle, and
+    the selection and compaction of every unit on the GPU's own scores."""
+    w = WORKLOADS[wid]
+    run = _check_all(w, cover_units(w))
+    say(f"[parity] {w.name}: selection and compaction of all {check_selection_every_unit(w, run)} units exact")
 
 
 EDGE = [
@@ -146,6 +144,43 @@ def test_ties_constant_values():
     floor = _expansion_floor(w, run, 0)
     say(f"[parity] ties: expansion floor {floor:.3e}")
     check_unit(w, run, 0, atol=floor)
+
+
+@pytest.mark.parametrize("ratio", [3, 10, 30])
+def test_values_with_a_common_offset(ratio):
+    """Value rows sharing a large offset: v_j = mu + e_j with e_j ~ N(0, 1) and
+    ||mu|| = ratio * sqrt(d), so every a_i lies near mu and ||a_i - v_j|| is small next to
+    ||a_i|| and ||v_j||. The expanded distance ||a||^2 - 2 a.v + ||v||^2 then cancels, and
+    the fp16 rounding of a weighs ratio times more against the distance; the scores are
+    held to the same 1e-3 relative bar with the default absolute floor (DropKV page,
+    "Methodology in Plain English": the expanded squared distance)."""
+    w = Workload(f"offset{ratio}", 19, 1, 8, 2, 128, (4096,), 32, (20,), "uniform", 0.1)
+    data = synth.generate(w, "cuda")
+    g = torch.Generator().manual_seed(1000 + ratio)
+    mu = torch.randn(w.head_dim, generator=g, dtype=torch.float64)
+    mu = mu / mu.norm() * ratio * np.sqrt(w.head_dim)
+    data["v"] = (data["v"].double() + mu.to("cuda")).to(torch.bfloat16)
+    say(f"[parity] common value offset, ||mu|| / sqrt(d) = {ratio}")
+    _check_all(w, list(range(w.num_layers * w.num_seqs * w.num_kv_heads)), data=data)
+
+
+def test_pyramid_budgets_end_to_end():
+    """Layer budgets from kvscore_budget_pyramid (PyramidKV page, "Layer-Adaptive Dynamic
+    Budget Allocation": the uniform total reallocated, most to the lowest layer) drive the
+    selection and compaction: the library's integers equal the oracle's, and every unit's
+    outputs match the oracle with those budgets."""
+    w = small_variant(WORKLOADS[3], name="pyramid8", num_layers=8, seqlens=(8192,), heavy_count=(16,))
+    L, n, W = w.num_layers, w.seqlens[0], w.window
+    total = int(0.1 * n) * L
+    b = api.budget_pyramid(L, 1.0, total, W, n)
+    assert b.tolist() == oracle.pyramid_budgets(L, total, W, n, 1.0)
+    assert b.sum() == total and b[0] > b[L // 2] > b[-1] == W
+    say(f"[parity] pyramid budgets {b.tolist()}")
+    run = run_gpu(w, budgets=b[None, :].astype(np.int32))
+    rep = {}
+    for u in range(L * w.num_kv_heads):
+        check_unit(w, run, u, api.MODE_L2, rep)
+    say(f"[parity] pyramid: max rel score err {max(rep['max_rel']):.2e}")
 
 
 def _bits(t: torch.Tensor) -> torch.Tensor:
