@@ -126,6 +126,42 @@ def traffic_from(fetch_dir: str, write_dir: str, out_path: str, workload: str, c
     return rec
 
 
+def counters_from(dirs, kernels=("score_kernel", "fwd_partial_kernel")) -> dict:
+    """Per-dispatch means of rocprofv3 --pmc counters (csv output folders of runs of this script),
+    for each kernel whose name contains one of ``kernels``, plus derived figures. SQ time counters
+    are in quad-cycles summed over the SIMDs' waves; GRBM_GUI_ACTIVE is summed over the 8 XCDs;
+    SQ_VALU_MFMA_BUSY_CYCLES and SQ_VALU_MFMA_COEXEC_CYCLES are cycles summed over the 1024 SIMDs."""
+    import csv
+    import glob
+    acc = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                key = next((k for k in kernels if k in row["Kernel_Name"]), None)
+                if key is None:
+                    continue
+                ent = acc.setdefault(key, {}).setdefault(row["Counter_Name"], {})
+                did = (d, row["Dispatch_Id"])  # a counter collected in several runs is averaged over them
+                ent[did] = ent.get(did, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for key, cs in acc.items():
+        mean = {c: sum(v.values()) / len(v) for c, v in cs.items()}
+        simds, xcds = 1024, 8
+        der = {}
+        cyc = mean.get("GRBM_GUI_ACTIVE", 0) / xcds  # kernel duration in cycles
+        if cyc:
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                der["mfma_busy_frac"] = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / cyc
+            if "SQ_ACTIVE_INST_VALU" in mean:
+                der["valu_active_frac"] = 4 * mean["SQ_ACTIVE_INST_VALU"] / simds / cyc
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in mean:
+                der["coexec_frac"] = mean["SQ_VALU_MFMA_COEXEC_CYCLES"] / simds / cyc
+        if "SQ_INSTS_VALU" in mean and "SQ_INSTS_MFMA" in mean:
+            der["valu_non_mfma_insts"] = mean["SQ_INSTS_VALU"] - mean["SQ_INSTS_MFMA"]
+        out[key] = {"counters": mean, "derived": der, "dispatches": max(len(v) for v in cs.values())}
+    return out
+
+
 def cpu_model() -> str:
     """The host CPU's model name (first entry of /proc/cpuinfo)."""
     try:
@@ -240,7 +276,14 @@ def main():
                     help="no run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of this script "
                          "into HBM bytes per launch, written to --traffic-out")
     ap.add_argument("--traffic-out", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    ap.add_argument("--counters-from", nargs="+", metavar="DIR",
+                    help="no run: per-dispatch means and derived figures of rocprofv3 --pmc output folders "
+                         "(csv) of this script, for the score, forward, top-k and compaction kernels")
     args = ap.parse_args()
+    if args.counters_from:
+        print(json.dumps(counters_from(args.counters_from, ("score_kernel", "fwd_partial_kernel", "topk_kernel",
+                                                            "compact_kernel")), indent=1))
+        return
     if args.traffic_from:
         from kv_cache_eviction_kvscore_amd.configs import WORKLOADS
         rec = traffic_from(args.traffic_from[0], args.traffic_from[1], args.traffic_out, WORKLOADS[args.workload].name,
