@@ -19,12 +19,15 @@
 // found by a two-level scan (each thread sums its run of bins, a block scan over the
 // threads' totals finds the thread where the count from the top reaches k). This gives
 // the threshold T and how many elements equal to T are taken. When the threshold's
-// 14-bit bin holds few enough keys, the second pass also appends them to an LDS list
-// and the last pass counts over that list instead of reading the scores again.
-// Then an ordered stream compaction in rounds of 4096 positions: prefix counts of
-// "surely kept" (window, or key > T) and "tied" (key == T) positions, from ballots within
-// a wave and LDS sums across waves, give every kept position its slot; ties are taken by
-// ascending position.
+// 14-bit bin holds few enough keys, the second pass also lists them (key and competitor
+// index) in LDS and sets a bit in an LDS bitmask for every competitor above that bin; the
+// last pass counts over the list, the listed keys are then marked against T (a "surely
+// kept" bit above it, a "tied" bit equal to it), and the kept positions are written from
+// the bitmasks: the scores are read twice. Each thread takes a 32-bit word of each
+// bitmask per round, block scans of the words' counts give its slots, ties are taken by
+// ascending position. Otherwise (a bin too full for the list, or more competitors than
+// the bitmasks hold) an ordered stream compaction over the scores in rounds of 4096
+// positions does the same from ballots within a wave and LDS sums across waves.
 //
 // heads_*_kernel (head budgets chosen jointly over a layer's KV heads) run a select of
 // their own, spread over many workgroups: four passes of 8 bits, one 256-bin histogram
@@ -62,6 +65,18 @@ __device__ inline void hist_add(unsigned* h, bool in, unsigned bin) {
   if (__ballot(in && bin == b0) == m) {
     if ((int)(threadIdx.x & 63) == first) atomicAdd(&h[b0], (unsigned)__popcll(m));
   } else if (in) {
+    atomicAdd(&h[bin], 1u);
+  }
+}
+
+// The same for a pass that counts every lane: a per-lane atomic unless the wave's lanes all
+// fall in one bin (then one atomic with their number).
+__device__ inline void hist_add_all(unsigned* h, unsigned bin) {
+  const unsigned b0 = (unsigned)__builtin_amdgcn_readfirstlane((int)bin);
+  if (__ballot(bin != b0) == 0) {
+    const unsigned long long ex = __ballot(true);
+    if ((int)(threadIdx.x & 63) == __ffsll((long long)ex) - 1) atomicAdd(&h[b0], (unsigned)__popcll(ex));
+  } else {
     atomicAdd(&h[bin], 1u);
   }
 }
@@ -111,13 +126,21 @@ struct HistSmem {
   int tsum[NWAVES];
 };
 
-// LDS list of the keys that share the threshold's top 14 bits (filled during the second
-// pass), so the last radix pass need not read global memory again
-constexpr int kCandCap = 12288;
+// LDS list of the keys that share the threshold's top 14 bits and their competitor indices
+// (filled during the second pass), so that neither the last radix pass nor the emission
+// reads global memory again
+constexpr int kCandCap = 11264;
 struct CandSmem {
   unsigned key[kCandCap];
+  unsigned pos[kCandCap];
   unsigned n;
 };
+// After the first pass only the first 2^9 words of the histogram are counted into; the rest
+// holds two bitmasks over the competitors (bit c: competitor c), "surely kept" and "tied",
+// so the emission reads no score. Units with more competitors read the scores a third time.
+constexpr int kBitBase = 1 << kBits12;
+constexpr int kBitWords = ((1 << kBits0) - kBitBase) / 2;  // words per bitmask
+constexpr int64_t kBitCap = (int64_t)kBitWords * 32;       // competitors the bitmasks cover
 
 // Radix select of the kr-th largest key among the keys `visit` enumerates (each thread
 // calls f(key) on its share, all lanes of a wave together): T = that key, need_eq = how
@@ -126,36 +149,49 @@ struct CandSmem {
 // descending order. With cs, the second pass also appends the keys that share the
 // threshold's top 14 bits to cs when they fit, and the last pass reads that list instead
 // (the counts, so T and need_eq, do not depend on the list's order).
+// visit(f) calls f(key, c) for every competitor c. With sure, the second pass also sets bit c
+// of sure for every key above the threshold's top 14 bits, and listed tells whether the
+// list was filled (the caller then marks the listed keys against T itself).
 template <class Visit>
 __device__ void radix_select(SelectSmem& sm, HistSmem& hs, Visit visit, int64_t kr, unsigned& T, int64_t& need_eq,
-                             CandSmem* cs = nullptr) {
+                             CandSmem* cs, unsigned* sure, bool& listed) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   unsigned prefix = 0, pmask = 0;
-  bool listed = false;  // uniform: the last pass reads cs
+  listed = false;  // uniform: the last pass reads cs
   for (int pass = 0; pass < 3; ++pass) {
     const int bits = pass == 0 ? kBits0 : kBits12;
     const int shift = pass == 0 ? 32 - kBits0 : (pass == 1 ? kBits12 : 0);
     const int nb = 1 << bits;
     const unsigned dmask = (unsigned)nb - 1u;
-    for (int i = tid; i < nb; i += NT) hs.hist[i] = 0;
     // keys with the current prefix: the last pass's count of its digit
     const bool collect = cs && pass == 1 && sm.s_count <= (unsigned)kCandCap;
+    const bool mark = collect && sure;
+    for (int i = tid; i < nb; i += NT) hs.hist[i] = 0;
+    if (mark)  // both bitmasks
+      for (int i = tid; i < 2 * kBitWords; i += NT) hs.hist[kBitBase + i] = 0;
     if (collect && tid == 0) cs->n = 0;
     __syncthreads();
-    auto count = [&](unsigned key) { hist_add(hs.hist, (key & pmask) == prefix, (key >> shift) & dmask); };
-    if (listed) {
-      for (int i = tid; i < (int)cs->n; i += NT) count(cs->key[i]);
+    auto count = [&](unsigned key, int64_t) { hist_add(hs.hist, (key & pmask) == prefix, (key >> shift) & dmask); };
+    if (pass == 0) {
+      visit([&](unsigned key, int64_t) { hist_add_all(hs.hist, key >> shift); });
+    } else if (listed) {
+      for (int i = tid; i < (int)cs->n; i += NT) count(cs->key[i], 0);
     } else if (collect) {
-      visit([&](unsigned key) {
+      visit([&](unsigned key, int64_t c) {
         const bool in = (key & pmask) == prefix;
         hist_add(hs.hist, in, (key >> shift) & dmask);
+        if (mark && (key & pmask) > prefix) atomicOr(&sure[c >> 5], 1u << (c & 31));
         // one slot reservation per wave, then each lane writes at its rank among the wave's
         const unsigned long long m = __ballot(in);
         if (m) {
           unsigned base = 0;
           if (lane == __ffsll((long long)m) - 1) base = atomicAdd(&cs->n, (unsigned)__popcll(m));
           base = __shfl(base, __ffsll((long long)m) - 1, 64);
-          if (in) cs->key[base + __popcll(m & ((1ull << lane) - 1))] = key;
+          if (in) {
+            const unsigned slot = base + __popcll(m & ((1ull << lane) - 1));
+            cs->key[slot] = key;
+            cs->pos[slot] = (unsigned)c;
+          }
         }
       });
     } else {
@@ -200,64 +236,19 @@ __device__ void radix_select(SelectSmem& sm, HistSmem& hs, Visit visit, int64_t 
   need_eq = kr;
 }
 
-// Ordered stream compaction of one segment (b rows at out): positions j in [0, n), kept
-// when j < ns or j >= cand (sinks, window), or by the selection: sel 0 none, 1 all,
-// 2 key > T and the first need_eq keys equal to T (ascending position). Rounds of 4096
-// positions; ballots and a sum over the waves give every kept position its slot.
-__device__ void emit_segment(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int sel, unsigned T,
-                             int64_t need_eq, const float* __restrict__ sc, int64_t n, int64_t cand, int64_t ns) {
+// Ordered stream compaction of one segment (b rows at out) over positions j in [0, n), in
+// rounds of 4 NT positions, 4 per thread: flags(base, sure, tie) gives each of this
+// thread's positions base + 4 tid + e its flags (surely kept, or tied with the threshold);
+// the first need_eq tied positions are taken. Ballots and a sum over the waves give every
+// kept position its slot.
+template <class Flags>
+__device__ void emit_ordered(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int64_t need_eq, int64_t n,
+                             Flags flags) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  // the keys of a round are loaded three rounds ahead, 16 bytes per lane when aligned (the
-  // row holds n keys, so a load never leaves it)
-  const bool vec = (((size_t)sc) & 15) == 0;
-  auto load = [&](int64_t base, float* x) __attribute__((always_inline)) {
-    const int64_t j = base + 4 * tid;
-    if (sel != 2 || j >= n) return;
-    if (vec && j + 4 <= n) {
-      const float4 v = *(const float4*)(sc + j);
-      x[0] = v.x;
-      x[1] = v.y;
-      x[2] = v.z;
-      x[3] = v.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (j + e < n) x[e] = sc[j + e];
-    }
-  };
-  // three rounds in flight: the emit is bound by the latency of its reads
-  float nx[3][4] = {};
-  load(0, nx[0]);
-  load(4 * NT, nx[1]);
-  load(8 * NT, nx[2]);
   int64_t sure_base = 0, eq_base = 0;
   for (int64_t base = 0; base < n; base += 4 * NT) {
-    float x[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = nx[0][e];
-      nx[0][e] = nx[1][e];
-      nx[1][e] = nx[2][e];
-    }
-    load(base + 12 * NT, nx[2]);
     bool sure[4], tie[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t j = base + 4 * tid + e;
-      sure[e] = false;
-      tie[e] = false;
-      if (j < n) {
-        if (j >= cand || j < ns) {
-          sure[e] = true;
-        } else if (sel == 1) {
-          sure[e] = true;
-        } else if (sel == 2) {
-          const unsigned key = f2key(x[e]);
-          sure[e] = key > T;
-          tie[e] = key == T;
-        }
-      }
-    }
+    flags(base, sure, tie);
     // this lane's exclusive prefix over the wave and the wave's totals, from one ballot per
     // element slot (the flags are bits: no shuffle chain through LDS)
     int ps = 0, pe = 0, tws = 0, twe = 0;
@@ -302,6 +293,125 @@ __device__ void emit_segment(SelectSmem& sm, int32_t* __restrict__ out, int64_t 
   }
 }
 
+// The same from the scores: positions j < ns or j >= cand (sinks, window) are kept; the
+// selection sel 0 keeps no competitor, 1 all, 2 key > T and the first need_eq keys equal to
+// T (ascending position).
+__device__ void emit_segment(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int sel, unsigned T,
+                             int64_t need_eq, const float* __restrict__ sc, int64_t n, int64_t cand, int64_t ns) {
+  const int tid = threadIdx.x;
+  // the keys of a round are loaded three rounds ahead, 16 bytes per lane when aligned (the
+  // row holds n keys, so a load never leaves it)
+  const bool vec = (((size_t)sc) & 15) == 0;
+  auto load = [&](int64_t base, float* x) __attribute__((always_inline)) {
+    const int64_t j = base + 4 * tid;
+    if (sel != 2 || j >= n) return;
+    if (vec && j + 4 <= n) {
+      const float4 v = *(const float4*)(sc + j);
+      x[0] = v.x;
+      x[1] = v.y;
+      x[2] = v.z;
+      x[3] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j + e < n) x[e] = sc[j + e];
+    }
+  };
+  // three rounds in flight: the emit is bound by the latency of its reads
+  float nx[3][4] = {};
+  load(0, nx[0]);
+  load(4 * NT, nx[1]);
+  load(8 * NT, nx[2]);
+  emit_ordered(sm, out, b, need_eq, n, [&](int64_t base, bool* sure, bool* tie) __attribute__((always_inline)) {
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = nx[0][e];
+      nx[0][e] = nx[1][e];
+      nx[1][e] = nx[2][e];
+    }
+    load(base + 12 * NT, nx[2]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t j = base + 4 * tid + e;
+      sure[e] = false;
+      tie[e] = false;
+      if (j < n) {
+        if (j >= cand || j < ns) {
+          sure[e] = true;
+        } else if (sel == 1) {
+          sure[e] = true;
+        } else if (sel == 2) {
+          const unsigned key = f2key(x[e]);
+          sure[e] = key > T;
+          tie[e] = key == T;
+        }
+      }
+    }
+  });
+}
+
+// The same from LDS bitmasks over the competitors (bit c of sure / tie: competitor c, at
+// position ns + c), for a selection that filled them: the sinks, then the selected
+// competitors, then the window. Thread t takes the 32 competitors of word t of each round
+// of NT words; block scans of the words' counts give its slots.
+__device__ void emit_words(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int64_t need_eq,
+                           const unsigned* sure_bits, const unsigned* tie_bits, int64_t n, int64_t cand, int64_t ns) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t m = cand - ns;
+  for (int64_t j = tid; j < ns; j += NT) out[j] = (int32_t)j;
+  const int64_t nw = (m + 31) >> 5;
+  int64_t sure_base = 0, eq_base = 0;
+  for (int64_t w0 = 0; w0 < nw; w0 += NT) {
+    const int64_t w = w0 + tid;
+    unsigned sw = 0, tw = 0;
+    if (w < nw) {
+      sw = sure_bits[w];
+      tw = tie_bits[w];
+    }
+    const int cs_ = __popc(sw), ce = __popc(tw);
+    const int is = wave_incl_scan(cs_, lane), ie = wave_incl_scan(ce, lane);
+    if (lane == 63) {
+      sm.wsum[0][wave] = is;
+      sm.wsum[1][wave] = ie;
+    }
+    __syncthreads();
+    int ps = is - cs_, pe = ie - ce, ts = 0, te = 0;
+    for (int v = 0; v < NWAVES; ++v) {
+      if (v < wave) {
+        ps += sm.wsum[0][v];
+        pe += sm.wsum[1][v];
+      }
+      ts += sm.wsum[0][v];
+      te += sm.wsum[1][v];
+    }
+    int64_t rs = sure_base + ps, re = eq_base + pe;
+    unsigned bits = sw | tw;
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      bits &= bits - 1;
+      const int32_t j = (int32_t)(ns + (w << 5) + bit);
+      if ((sw >> bit) & 1u) {
+        const int64_t pos = ns + rs + (re < need_eq ? re : need_eq);
+        if (pos < b) out[pos] = j;
+        ++rs;
+      } else {
+        if (re < need_eq && ns + rs + re < b) out[ns + rs + re] = j;
+        ++re;
+      }
+    }
+    sure_base += ts;
+    eq_base += te;
+    __syncthreads();  // wsum is rewritten next round
+  }
+  // the window after the selected competitors
+  const int64_t kept_c = sure_base + (eq_base < need_eq ? eq_base : need_eq);
+  for (int64_t i = tid; i < n - cand; i += NT) {
+    const int64_t pos = ns + kept_c + i;
+    if (pos < b) out[pos] = (int32_t)(cand + i);
+  }
+}
+
 __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict__ score, int n_sink,
                                                  const int64_t* __restrict__ seg_off, int32_t* __restrict__ kept) {
   __shared__ SelectSmem sm;
@@ -328,26 +438,62 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
     __shared__ HistSmem hs;
     const float* c0 = sc + ns;
     const int64_t m = cand - ns;
+    unsigned* sure = &hs.hist[kBitBase];
+    unsigned* tie = sure + kBitWords;
+    bool listed = false;
     radix_select(sm, hs, [&](auto f) {
-      int64_t j0 = 0;
-      if ((((size_t)c0) & 15) == 0) {  // 16-byte loads, two in flight per thread
-        const int64_t m8 = m / (8 * NT) * (8 * NT);
-        for (int64_t j = 4 * tid; j < m8; j += 8 * NT) {
-          const float4 x = *(const float4*)(c0 + j);
-          const float4 y = *(const float4*)(c0 + j + 4 * NT);
-          f(f2key(x.x));
-          f(f2key(x.y));
-          f(f2key(x.z));
-          f(f2key(x.w));
-          f(f2key(y.x));
-          f(f2key(y.y));
-          f(f2key(y.z));
-          f(f2key(y.w));
+      int64_t m4 = 0;  // competitors read as float4s
+      if ((((size_t)c0) & 15) == 0) {
+        // 16-byte loads: thread tid takes float4s tid + NT r, four rounds r per step, the
+        // next step's issued before this one is counted (eight in flight per thread, 128 KB
+        // per workgroup); two buffers with fixed roles and two steps per trip (a register
+        // rotation would make the compiler wait for the next step's loads at the copy)
+        constexpr int V = 4;
+        m4 = m >> 2;
+        const int64_t nr = (m4 + NT - 1) / NT;  // rounds
+        float4 A[V], B[V];
+        auto ld = [&](float4* buf, int64_t r0) __attribute__((always_inline)) {
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            const int64_t fi = tid + NT * (r0 + i);
+            if (fi < m4) buf[i] = *(const float4*)(c0 + 4 * fi);
+          }
+        };
+        auto run = [&](const float4* buf, int64_t r0) __attribute__((always_inline)) {
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            const int64_t fi = tid + NT * (r0 + i);
+            if (fi < m4) {
+              const int64_t j = 4 * fi;
+              f(f2key(buf[i].x), j);
+              f(f2key(buf[i].y), j + 1);
+              f(f2key(buf[i].z), j + 2);
+              f(f2key(buf[i].w), j + 3);
+            }
+          }
+        };
+        ld(A, 0);
+        for (int64_t r = 0; r < nr; r += 2 * V) {
+          ld(B, r + V);
+          run(A, r);
+          ld(A, r + 2 * V);
+          run(B, r + V);
         }
-        j0 = m8;
       }
-      for (int64_t j = j0 + tid; j < m; j += NT) f(f2key(c0[j]));
-    }, k, T, need_eq, &cs);
+      for (int64_t j = 4 * m4 + tid; j < m; j += NT) f(f2key(c0[j]), j);
+    }, k, T, need_eq, &cs, m <= kBitCap ? sure : nullptr, listed);
+    if (listed && m <= kBitCap) {
+      // the listed keys (those sharing T's top 14 bits) against T; the ones above those bits
+      // were marked during the second pass
+      for (int i = tid; i < (int)cs.n; i += NT) {
+        const unsigned key = cs.key[i], c = cs.pos[i];
+        if (key > T) atomicOr(&sure[c >> 5], 1u << (c & 31));
+        else if (key == T) atomicOr(&tie[c >> 5], 1u << (c & 31));
+      }
+      __syncthreads();
+      emit_words(sm, kept + off0, b, need_eq, sure, tie, n, cand, ns);
+      return;
+    }
   }
   emit_segment(sm, kept + off0, b, sel, T, need_eq, sc, n, cand, ns);
 }

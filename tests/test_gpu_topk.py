@@ -4,13 +4,17 @@ DropKV page, "Methodology in Plain English": keep the largest scores, the recent
 always. The selection is integer work decided on the same fp32 values on both sides, so
 every segment must equal the oracle's (a full sort on (-score, position)) exactly.
 
-The score distributions steer the radix select down both of its routes: when at most
-12288 keys share the threshold's top 14 bits, its last pass reads an LDS list of them;
-otherwise it reads the scores again. Covered: a log-uniform spread, one top byte for every
-key (uniform in [2, 8)), sixteen distinct values (ties decided by position), ties inside a
-listed bin (all of these take the list), a narrow range whose keys all share their top 14
-bits but differ below (no list, distinct keys), all keys equal (no list, all ties), and
-budgets keeping every competitor or none.
+The score distributions steer the radix select down its routes: when at most 11264 keys
+share the threshold's top 14 bits, the second pass lists them (key and position) in LDS and
+marks every competitor above those bits in an LDS bitmask; the last pass and the ordered
+emission then read no score. Otherwise the last pass and the emission read the scores
+again, and so does the emission of a unit with more competitors than the bitmasks hold
+(253952). Covered: a log-uniform spread, one top byte for every key (uniform in [2, 8)),
+sixteen distinct values (ties decided by position), ties inside a listed bin (all of these
+take the list), a narrow range whose keys all share their top 14 bits but differ below (no
+list, distinct keys), all keys equal (no list, all ties), budgets keeping every competitor
+or none, sinks (which shift the bitmasks' positions off word boundaries), and a unit too
+long for the bitmasks.
 """
 import numpy as np
 import pytest
@@ -44,22 +48,24 @@ def _scores(kind, n, rng):
 KINDS = ["log_uniform", "one_top_byte", "sixteen_values", "all_equal", "ties_in_list", "narrow"]
 
 
-@pytest.mark.parametrize("budget_extra", [5000, 0, 70000])
-def test_topk_threshold_bins_both_routes(budget_extra):
+@pytest.mark.parametrize("budget_extra,n_sink,n", [(5000, 0, 60011), (0, 0, 60011), (70000, 0, 60011),
+                                                    (5000, 5, 60011), (5000, 37, 60011), (20000, 3, 300007)])
+def test_topk_threshold_bins_both_routes(budget_extra, n_sink, n):
+    # n = 60011 is ragged against the 4-key loads; 300007 - W competitors exceed the bitmasks
     L, S, Hkv, Hq, d, W = 1, 1, len(KINDS), len(KINDS), 128, 16
-    n = 60011  # ragged against the 4-key loads
-    rng = np.random.default_rng(budget_extra + 5)
+    rng = np.random.default_rng(budget_extra + 5 + n_sink)
     p = api.Problem(num_seqs=S, num_layers=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, window=W,
                     cu_seqlens=[0, n], k_strides=(Hkv * n * d, n * d, d), v_strides=(Hkv * n * d, n * d, d))
     sc = np.stack([_scores(kind, n, rng) for kind in KINDS])  # [Hkv][n]
-    b = min(W + budget_extra, n)
+    b = min(W + n_sink + budget_extra, n)
     budgets = np.full((S, L), b, dtype=np.int32)
     off = api.segment_offsets(p, budgets)
     kept = torch.full((int(off[-1]),), -7, dtype=torch.int32, device="cuda")
-    say(f"top-k on hand-made scores: n={n}, budget {b}, kinds {KINDS}")
-    api.topk(p, torch.from_numpy(sc.reshape(-1)).cuda(), budgets, torch.from_numpy(off).cuda(), kept)
+    say(f"top-k on hand-made scores: n={n}, budget {b}, sinks {n_sink}, kinds {KINDS}")
+    api.topk(p, torch.from_numpy(sc.reshape(-1)).cuda(), budgets, torch.from_numpy(off).cuda(), kept,
+             n_sink=n_sink)
     torch.cuda.synchronize()
     got = kept.cpu().numpy()
     for g, kind in enumerate(KINDS):
-        ref = oracle.kept_positions(sc[g].astype(np.float64), n, W, b)
+        ref = oracle.kept_positions(sc[g].astype(np.float64), n, W, b, n_sink=n_sink)
         np.testing.assert_array_equal(got[off[g]:off[g + 1]], ref, err_msg=kind)
