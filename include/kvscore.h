@@ -142,7 +142,9 @@ size_t kvscore_workspace_size(const kvscore_problem* p, int32_t which);
  * mode ATTN, dom_i = p* (that pair's attention weight).
  * Inputs q_win, k, v (device, bf16). Outputs a, lse, jstar, dom (device).
  * workspace: device, >= kvscore_workspace_size(p, KVSCORE_WS_ATTN_FWD) bytes,
- * 256-byte aligned; contents are scratch.
+ * 256-byte aligned; contents are scratch. That size is 0 (workspace may be NULL) when
+ * every sequence fits in one key chunk of the pass; otherwise it holds one record per
+ * (unit, query tile, chunk).
  */
 int kvscore_attn_fwd(const kvscore_problem* p, const void* q_win, const void* k, const void* v, float* a,
                      float* lse, int32_t* jstar, float* dom, void* workspace, size_t workspace_bytes,

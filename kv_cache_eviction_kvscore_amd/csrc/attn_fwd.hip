@@ -85,7 +85,10 @@ __device__ inline float row_max(float x) {
 template <int D>
 __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf16* __restrict__ q,
                                                                const __bf16* __restrict__ k,
-                                                               const __bf16* __restrict__ v, float* __restrict__ ws) {
+                                                               const __bf16* __restrict__ v, float* __restrict__ ws,
+                                                               float* __restrict__ a_out, float* __restrict__ lse_out,
+                                                               int32_t* __restrict__ jstar_out,
+                                                               float* __restrict__ dom_out) {
   constexpr int NKK = D / 16;              // k-steps of the QK^T contraction
   constexpr int NDB = D / 32;              // 32-wide d blocks of O^T
   constexpr int CPK = D / 8;               // 16-byte chunks per row
@@ -461,6 +464,60 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
   }
 
   if (!computing) return;
+  const HalfPair lp = wave_halves(lrest);  // the row's two half sums
+  lrest = lp.lo + lp.hi;
+  if (n <= p.fwd_chunk) {
+    // the sequence is one chunk: this workgroup saw every key of its rows, so it writes the
+    // outputs itself (the one-chunk case of fwd_combine, whose record it would otherwise
+    // write and which then skips these rows)
+    if (!row_ok) return;
+    const size_t ro = (size_t)u * p.R + row;
+    float* arow = a_out + ro * D;
+    if (jst < 0) {  // no visible key recorded (cannot happen for valid shapes: key 0 is always visible)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) *(float4*)&arow[32 * db + 8 * qq + 4 * h] = float4{0.f, 0.f, 0.f, 0.f};
+      if (h == 0) {
+        dom_out[ro] = 0.f;
+        lse_out[ro] = -INFINITY;
+        jstar_out[ro] = -1;
+      }
+      return;
+    }
+    const float M = m * c1s, M2 = m2 * c1s, lr = lrest * kPUnscale;  // log2 units
+    const float w2 = (M2 == -INFINITY) ? 0.f : 1.f;
+    const float lrs = w2 * lr;
+    const float rel = (M2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M2 - M);
+    const float lt = rel * lrs;
+    const float pstar = 1.f / (1.f + lt);
+    float d2 = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        float4 w4;
+        float* wv = (float*)&w4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float acc = w2 * (o[db][4 * qq + e] * kPUnscale), vv = (float)vs[db][qq][e];
+          wv[e] = (rel * acc + vv) * pstar;
+          const float df = (lrs > 0.f ? acc / lrs : vv) - vv;
+          d2 += df * df;
+        }
+        *(float4*)&arow[32 * db + 8 * qq + 4 * h] = w4;
+      }
+    const HalfPair dp = wave_halves(d2);
+    if (h == 0) {
+      const float shift = pstar * sqrtf(dp.lo + dp.hi);
+      // the isolated pair's term in the call's score: its shift (L2), squared (SQ), or its
+      // attention weight p* (attention sum)
+      dom_out[ro] = (p.mode == 1) ? shift * shift : (p.mode == 2 ? pstar : shift);
+      lse_out[ro] = (M + __log2f(1.f + lt)) * 0.69314718055994531f;
+      jstar_out[ro] = jst;
+    }
+    return;
+  }
   float* blk = ws + ((size_t)(u * p.Tq + qt) * p.fwd_chunks + ch) * fwd_block_floats(p.RT, D);
   float* Ob = blk;
   _Float16* Vb = (_Float16*)(blk + (size_t)p.RT * D);
@@ -477,10 +534,6 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       *(float4*)&Ob[(size_t)row_t * D + 32 * db + 8 * qq + 4 * h] = w4;
       *(f16x4*)&Vb[(size_t)row_t * D + 32 * db + 8 * qq + 4 * h] = vs[db][qq];
     }
-  {
-    const HalfPair lp = wave_halves(lrest);  // the row's two half sums
-    lrest = lp.lo + lp.hi;
-  }
   if (h == 0) {
     Mb[row_t] = m * c1s;  // log2 units from here on
     M2b[row_t] = m2 * c1s;
@@ -509,51 +562,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
 
   // stat(c, 0) = m (max), 1 = m2 (max of the rest), 2 = l_rest (relative to m2), 3 = j*
   const size_t ro = (size_t)u * p.R + row;
-  if (nch == 1) {
-    // one chunk (uniform): every load of the row at once, then the arithmetic of the
-    // general path below with win = 0, M2 = m2, w2 = 1 and no other chunk
-    const float M = *stat(0, 0), M2 = *stat(0, 1), lr = *stat(0, 2);
-    const int j0 = *(const int*)stat(0, 3);
-    const float* Oc = block(0) + (size_t)row_t * D;
-    const _Float16* Vc = (const _Float16*)(block(0) + (size_t)p.RT * D) + (size_t)row_t * D;
-    float o[PER], vs[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      o[i] = Oc[lane + 64 * i];
-      vs[i] = (float)Vc[lane + 64 * i];
-    }
-    if (j0 < 0) {  // no visible key recorded (cannot happen for valid shapes: key 0 is always visible)
-      for (int e = lane; e < D; e += 64) a[ro * D + e] = 0.f;
-      if (lane == 0) {
-        dom[ro] = 0.f;
-        lse[ro] = -INFINITY;
-        jstar[ro] = -1;
-      }
-      return;
-    }
-    const float w2 = (M2 == -INFINITY) ? 0.f : 1.f;
-    const float lrs = w2 * lr;
-    const float rel = (M2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M2 - M);
-    const float lt = rel * lrs;
-    const float pstar = 1.f / (1.f + lt);
-    float d2 = 0.f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const float acc = w2 * o[i];
-      a[ro * D + lane + 64 * i] = (rel * acc + vs[i]) * pstar;
-      const float df = (lrs > 0.f ? acc / lrs : vs[i]) - vs[i];
-      d2 += df * df;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) d2 += __shfl_xor(d2, off, 64);
-    if (lane == 0) {
-      const float shift = pstar * sqrtf(d2);
-      dom[ro] = (p.mode == 1) ? shift * shift : (p.mode == 2 ? pstar : shift);
-      lse[ro] = (M + __log2f(1.f + lt)) * 0.69314718055994531f;
-      jstar[ro] = j0;
-    }
-    return;
-  }
+  if (nch == 1) return;  // uniform: fwd_partial wrote this row's outputs
   float M = -INFINITY;
   int win = -1;
   for (int c = 0; c < nch; ++c) {
@@ -631,12 +640,14 @@ hipError_t launch_attn_fwd(const Dev& p, const void* q, const void* k, const voi
   const dim3 g1(p.fwd_chunks, p.Tq, p.U), g2((p.R + 3) / 4, p.U);
   if (p.d == 128) {
     hipLaunchKernelGGL(fwd_partial_kernel<128>, g1, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, (float*)ws);
-    hipLaunchKernelGGL(fwd_combine_kernel<128>, g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
+                       (const __bf16*)v, (float*)ws, a, lse, jstar, dom);
+    if (p.fwd_chunks > 1)
+      hipLaunchKernelGGL(fwd_combine_kernel<128>, g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
   } else {
     hipLaunchKernelGGL(fwd_partial_kernel<64>, g1, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, (float*)ws);
-    hipLaunchKernelGGL(fwd_combine_kernel<64>, g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
+                       (const __bf16*)v, (float*)ws, a, lse, jstar, dom);
+    if (p.fwd_chunks > 1)
+      hipLaunchKernelGGL(fwd_combine_kernel<64>, g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
   }
   return hipGetLastError();
 }

@@ -150,7 +150,10 @@ int make_dev(const kvscore_problem* p, kvs::Dev& d) {
   return ok();
 }
 
+// the forward's per-chunk records; none when every sequence is one key chunk (the partial
+// kernel then writes the outputs itself)
 size_t ws_attn(const kvs::Dev& d) {
+  if (d.fwd_chunks == 1) return 0;
   return (size_t)d.U * d.Tq * d.fwd_chunks * kvs::fwd_block_floats(d.RT, d.d) * sizeof(float);
 }
 size_t ws_score(const kvs::Dev& d) { return kvs::prep_bytes((int64_t)d.U * d.R, d.d); }

@@ -78,12 +78,20 @@ def test_null_tensors_and_small_workspace_rejected():
     with pytest.raises(api.KvscoreError) as e:
         api._check(lib.kvscore_score(p.ref, None, None, None, None, None, None, None, None, 0, None))
     assert e.value.code == 1
-    need = p.workspace_size(api.WS_ATTN_FWD)
+    # every sequence in one key chunk: the forward needs no workspace
+    assert p.workspace_size(api.WS_ATTN_FWD) == 0
+    # one layer of 8 heads over 32K tokens is split into key chunks: then it needs records
+    n, Hkv = 32768, 8
+    pc = make_problem(num_layers=1, num_q_heads=4 * Hkv, num_kv_heads=Hkv, window=64, cu_seqlens=[0, n],
+                      k_strides=(Hkv * n * 128, n * 128, 128), v_strides=(Hkv * n * 128, n * 128, 128))
+    need = pc.workspace_size(api.WS_ATTN_FWD)
     assert need > 0
     fake = 1 << 20  # a non-null, aligned address that is never dereferenced
-    rc = lib.kvscore_attn_fwd(p.ref, fake, fake, fake, fake, fake, fake, fake, fake, need - 1, None)
+    rc = lib.kvscore_attn_fwd(pc.ref, fake, fake, fake, fake, fake, fake, fake, fake, need - 1, None)
     assert rc == 2 and b"need" in lib.kvscore_last_error()
-    rc = lib.kvscore_attn_fwd(p.ref, fake + 8, fake, fake, fake, fake, fake, fake, fake, need, None)
+    rc = lib.kvscore_attn_fwd(pc.ref, fake, fake, fake, fake, fake, fake, fake, None, need, None)
+    assert rc == 2 and b"NULL" in lib.kvscore_last_error()
+    rc = lib.kvscore_attn_fwd(pc.ref, fake + 8, fake, fake, fake, fake, fake, fake, fake, need, None)
     assert rc == 1  # q not 16-byte aligned
 
 
@@ -121,7 +129,8 @@ def test_forward_chunks_follow_the_makespan_estimate():
         U = L * len(seqlens) * Hkv
         ws = p.workspace_size(api.WS_ATTN_FWD)
         assert ws % (U * block) == 0
-        return ws // (U * block), n
+        # no records at all when every sequence is one chunk (the pass writes its outputs)
+        return (ws // (U * block) if ws else 1), n
 
     # 32 layers x 8 KV heads of 128K tokens: 256 units for 256 CUs, one chunk each
     assert fwd_chunks(32, 8, [131072]) == (1, 131072)
