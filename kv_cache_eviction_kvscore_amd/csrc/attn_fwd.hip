@@ -98,7 +98,8 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
   static_assert(IPT % NWAVES == 0 && (NLD == 2 || NLD == 4), "tile shape");
   __shared__ FwdSmem<D> sm;
 
-  const int u = blockIdx.z, qt = blockIdx.y, ch = blockIdx.x;
+  int ch, qt, u;
+  xcd_item3(p, ch, qt, u);
   int l, s, g;
   unit_coords(p, u, l, s, g);
   const int64_t n = p.cu[s + 1] - p.cu[s];

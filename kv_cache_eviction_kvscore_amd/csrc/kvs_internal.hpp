@@ -120,6 +120,30 @@ __host__ __device__ inline void unit_coords(const Dev& p, int u, int& l, int& s,
   l = u / (p.Hkv * p.S);
 }
 
+// XCD-aware work order for a grid of (x = key chunk, y = query tile, z = unit) items, or a
+// grid of units alone. The hardware deals workgroups round-robin by linear id to the chip's
+// 8 XCDs and, within an XCD, to its 4 shader engines (8 CUs each): workgroup id w goes to
+// queue w % 32 (measured). The identity order therefore hands each queue fixed (chunk,
+// tile) pairs, and on a ragged batch the queues that draw first chunks get most of the
+// work while the others idle (a 2x slower pass, measured). Here queue q takes the q-th
+// 32nd of the logical items, whose order runs chunk fastest, then tile, then unit with the
+// sequence fastest, so every queue holds nearly the same mix of sequence lengths. Returns
+// the item's chunk, tile and unit (u = (l*S + s)*Hkv + g).
+constexpr int kDispatchQueues = 32;
+__device__ inline void xcd_item(const Dev& p, int nx, int ny, int nz, int lw, int& x, int& y, int& u) {
+  const int G = nx * ny * nz, base = G / kDispatchQueues, rem = G % kDispatchQueues;
+  const int q = lw % kDispatchQueues, k = lw / kDispatchQueues;
+  const int lin = q * base + (q < rem ? q : rem) + k;  // a bijection of [0, G)
+  x = lin % nx;
+  y = (lin / nx) % ny;
+  const int up = lin / (nx * ny);
+  const int s = up % p.S, rest = up / p.S;
+  u = ((rest / p.Hkv) * p.S + s) * p.Hkv + rest % p.Hkv;
+}
+__device__ inline void xcd_item3(const Dev& p, int& x, int& y, int& u) {
+  xcd_item(p, gridDim.x, gridDim.y, gridDim.z, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), x, y, u);
+}
+
 // Forward split record block: [RT][d] fp32 O_rest | [RT][d] fp16 v* | [RT] m | [RT] m2 | [RT] l_rest | [RT] j*
 __host__ __device__ inline size_t fwd_block_floats(int RT, int d) { return (size_t)RT * d + (size_t)RT * d / 2 + 4 * (size_t)RT; }
 

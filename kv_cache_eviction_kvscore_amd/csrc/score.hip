@@ -153,7 +153,8 @@ __global__ __launch_bounds__(512 / RB) __attribute__((amdgpu_waves_per_eu(2 / RB
   static_assert(KT % NWAVES == 0 && 64 % KPW == 0 && CPK % LPK == 0 && CPN >= 1, "norm pass shape");
   __shared__ ScoreSmem<D> sm;
 
-  const int u = blockIdx.z, qt = blockIdx.y, ch = blockIdx.x;
+  int ch, qt, u;
+  xcd_item3(p, ch, qt, u);
   int l, s, g;
   unit_coords(p, u, l, s, g);
   const int64_t n = p.cu[s + 1] - p.cu[s];

@@ -415,7 +415,8 @@ __device__ void emit_words(SelectSmem& sm, int32_t* __restrict__ out, int64_t b,
 __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict__ score, int n_sink,
                                                  const int64_t* __restrict__ seg_off, int32_t* __restrict__ kept) {
   __shared__ SelectSmem sm;
-  const int u = blockIdx.x;
+  int x_, y_, u;
+  xcd_item(p, 1, 1, gridDim.x, blockIdx.x, x_, y_, u);
   int l, s, g;
   unit_coords(p, u, l, s, g);
   const int64_t n = p.cu[s + 1] - p.cu[s];
