@@ -130,18 +130,19 @@ __host__ __device__ inline void unit_coords(const Dev& p, int u, int& l, int& s,
 // sequence fastest, so every queue holds nearly the same mix of sequence lengths. Returns
 // the item's chunk, tile and unit (u = (l*S + s)*Hkv + g).
 constexpr int kDispatchQueues = 32;
-__device__ inline void xcd_item(const Dev& p, int nx, int ny, int nz, int lw, int& x, int& y, int& u) {
+__device__ inline void xcd_item(int S, int Hkv, int nx, int ny, int nz, int lw, int& x, int& y, int& u) {
   const int G = nx * ny * nz, base = G / kDispatchQueues, rem = G % kDispatchQueues;
   const int q = lw % kDispatchQueues, k = lw / kDispatchQueues;
   const int lin = q * base + (q < rem ? q : rem) + k;  // a bijection of [0, G)
   x = lin % nx;
   y = (lin / nx) % ny;
   const int up = lin / (nx * ny);
-  const int s = up % p.S, rest = up / p.S;
-  u = ((rest / p.Hkv) * p.S + s) * p.Hkv + rest % p.Hkv;
+  const int s = up % S, rest = up / S;
+  u = ((rest / Hkv) * S + s) * Hkv + rest % Hkv;
 }
 __device__ inline void xcd_item3(const Dev& p, int& x, int& y, int& u) {
-  xcd_item(p, gridDim.x, gridDim.y, gridDim.z, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), x, y, u);
+  xcd_item(p.S, p.Hkv, gridDim.x, gridDim.y, gridDim.z, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), x,
+           y, u);
 }
 
 // Forward split record block: [RT][d] fp32 O_rest | [RT][d] fp16 v* | [RT] m | [RT] m2 | [RT] l_rest | [RT] j*

@@ -416,7 +416,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
                                                  const int64_t* __restrict__ seg_off, int32_t* __restrict__ kept) {
   __shared__ SelectSmem sm;
   int x_, y_, u;
-  xcd_item(p, 1, 1, gridDim.x, blockIdx.x, x_, y_, u);
+  xcd_item(p.S, p.Hkv, 1, 1, gridDim.x, blockIdx.x, x_, y_, u);
   int l, s, g;
   unit_coords(p, u, l, s, g);
   const int64_t n = p.cu[s + 1] - p.cu[s];
