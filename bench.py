@@ -130,10 +130,12 @@ def counters_from(dirs, kernels=("score_kernel", "fwd_partial_kernel")) -> dict:
     """Per-dispatch means of rocprofv3 --pmc counters (csv output folders of runs of this script),
     for each kernel whose name contains one of ``kernels``, plus derived figures. SQ time counters
     are in quad-cycles summed over the SIMDs' waves; GRBM_GUI_ACTIVE is summed over the 8 XCDs;
-    SQ_VALU_MFMA_BUSY_CYCLES and SQ_VALU_MFMA_COEXEC_CYCLES are cycles summed over the 1024 SIMDs."""
+    SQ_VALU_MFMA_BUSY_CYCLES and SQ_VALU_MFMA_COEXEC_CYCLES are cycles summed over the 1024 SIMDs.
+    The dispatches' start and end timestamps give their mean duration, and with GRBM_GUI_ACTIVE
+    the mean shader clock over the kernel (cycles / duration)."""
     import csv
     import glob
-    acc = {}
+    acc, dur = {}, {}
     for d in dirs:
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for row in csv.DictReader(open(f)):
@@ -143,6 +145,7 @@ def counters_from(dirs, kernels=("score_kernel", "fwd_partial_kernel")) -> dict:
                 ent = acc.setdefault(key, {}).setdefault(row["Counter_Name"], {})
                 did = (d, row["Dispatch_Id"])  # a counter collected in several runs is averaged over them
                 ent[did] = ent.get(did, 0.0) + float(row["Counter_Value"])
+                dur.setdefault(key, {})[did] = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9
     out = {}
     for key, cs in acc.items():
         mean = {c: sum(v.values()) / len(v) for c, v in cs.items()}
@@ -156,6 +159,11 @@ def counters_from(dirs, kernels=("score_kernel", "fwd_partial_kernel")) -> dict:
                 der["valu_active_frac"] = 4 * mean["SQ_ACTIVE_INST_VALU"] / simds / cyc
             if "SQ_VALU_MFMA_COEXEC_CYCLES" in mean:
                 der["coexec_frac"] = mean["SQ_VALU_MFMA_COEXEC_CYCLES"] / simds / cyc
+            clk = [cs["GRBM_GUI_ACTIVE"][k] / xcds / t for k, t in dur[key].items()
+                   if k in cs["GRBM_GUI_ACTIVE"] and t > 0]
+            if clk:
+                der["clock_ghz"] = sum(clk) / len(clk) * 1e-9
+                der["duration_ms"] = sum(dur[key].values()) / len(dur[key]) * 1e3
         if "SQ_INSTS_VALU" in mean and "SQ_INSTS_MFMA" in mean:
             der["valu_non_mfma_insts"] = mean["SQ_INSTS_VALU"] - mean["SQ_INSTS_MFMA"]
         out[key] = {"counters": mean, "derived": der, "dispatches": max(len(v) for v in cs.values())}
