@@ -8,7 +8,13 @@ scores within 1e-3 relative, the GPU's selection the full sort of its own scores
 to the oracle's outside the 1e-3 band, the packed cache bit-exact. The head-budget cases
 check each (sequence, layer) group's joint selection. Cases like these found a row whose
 argmax outweighs the rest by ~45 nats, and a mode-SQ case that needed the fp16 A_hat.
+
+KVSCORE_SWEEP_CASES (default 16) and KVSCORE_SWEEP_SEED (default 9000) set how many cases are
+drawn and from which seed on, for longer runs over other seeds; the head-budget cases take a
+third as many from the seed plus 500.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -43,20 +49,24 @@ def _draw(seed, heads=False):
     return w, mode, pool, n_sink
 
 
-@pytest.mark.parametrize("seed", range(16))
+NCASES = int(os.environ.get("KVSCORE_SWEEP_CASES", "16"))
+SEED0 = int(os.environ.get("KVSCORE_SWEEP_SEED", "9000"))
+
+
+@pytest.mark.parametrize("seed", range(NCASES))
 def test_random_pipeline(seed):
-    w, mode, pool, n_sink = _draw(9000 + seed)
+    w, mode, pool, n_sink = _draw(SEED0 + seed)
     say(f"[sweep] {w} mode={mode} pool={pool} sinks={n_sink}")
     run = run_gpu(w, mode=mode, pool=pool, n_sink=n_sink)
     worst = max(check_unit(w, run, u, mode) for u in sample_units(w, 4))
     say(f"[sweep] {w.name}: max rel score err {worst:.2e}")
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(max(1, (NCASES + 2) // 3)))
 def test_random_head_budgets(seed):
     from test_gpu_heads import _check_group
 
-    w, mode, pool, n_sink = _draw(9500 + seed, heads=True)
+    w, mode, pool, n_sink = _draw(SEED0 + 500 + seed, heads=True)
     say(f"[sweep] {w} heads pool={pool} sinks={n_sink}")
     run = run_gpu(w, mode=mode, pool=pool, n_sink=n_sink, heads=True)
     for l in range(w.num_layers):
