@@ -4,8 +4,8 @@ Workloads 1 and 2 are checked on every unit; 3, 4 and 5 at full size on one unit
 layer (every layer, KV-head and sequence index covered), every output of each, plus the
 selection and compaction of every unit on the GPU's own scores.
 Edge cases cover one candidate, empty and full selections, G = 1 / W = 1, d = 64,
-ragged sequences, more than 256 rows per unit (several query tiles), token-major
-strides, ties, and run-to-run determinism.
+ragged sequences, more than 256 rows per unit (several query tiles), one sequence of a
+million tokens, token-major strides, ties, and run-to-run determinism.
 """
 import numpy as np
 import pytest
@@ -77,6 +77,15 @@ EDGE = [
 def test_edge_cases(w):
     U = w.num_layers * w.num_seqs * w.num_kv_heads
     _check_all(w, list(range(U)))
+
+
+def test_one_sequence_of_a_million_tokens():
+    """One unit with 2^20 + 37 cached tokens: the forward and the score pass split its keys into
+    many chunks (the forward's combine runs), the selection has ~1M competitors (more than its
+    LDS bitmasks hold, so the ordered-compaction path runs), every output against the fp64
+    oracle."""
+    w = Workload("long_1m", 31, 1, 4, 1, 128, (1048613,), 64, (2000,), "uniform", 0.05)
+    _check_all(w, [0])
 
 
 def test_dominant_sink_one_row():
