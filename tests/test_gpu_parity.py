@@ -5,7 +5,8 @@ layer (every layer, KV-head and sequence index covered), every output of each, p
 selection and compaction of every unit on the GPU's own scores.
 Edge cases cover one candidate, empty and full selections, G = 1 / W = 1, d = 64,
 ragged sequences, more than 256 rows per unit (several query tiles), one sequence of a
-million tokens, token-major strides, ties, and run-to-run determinism.
+million tokens, 65,280 units (near the launch grids' 65,535 limit), token-major strides,
+ties, and run-to-run determinism.
 """
 import numpy as np
 import pytest
@@ -22,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _check_all(w, units, mode=api.MODE_L2, **kw):  # kw: data, k_layout, pool, n_sink
-    say(f"[parity] {w.name} mode={mode} units={units} {kw}")
+    say(f"[parity] {w.name} mode={mode} units={units} {({k: x for k, x in kw.items() if k != 'data'})}")
     run = run_gpu(w, mode, **kw)
     rep = {}
     for u in units:
@@ -86,6 +87,19 @@ def test_one_sequence_of_a_million_tokens():
     oracle."""
     w = Workload("long_1m", 31, 1, 4, 1, 128, (1048613,), 64, (2000,), "uniform", 0.05)
     _check_all(w, [0])
+
+
+def test_units_near_the_grid_limit():
+    """65,280 units (255 layers, 4 short sequences, 64 KV heads; the launch grids carry the
+    unit count in a dimension capped at 65,535): a spread of units against the oracle, plus
+    the selection and compaction of every unit on the GPU's own scores."""
+    w = Workload("units_65280", 32, 255, 64, 64, 64, (70, 97, 66, 128), 64, None, "fixed", 66)
+    L, S, H, d, W, N = w.num_layers, w.num_seqs, w.num_q_heads, w.head_dim, w.window, w.total_tokens
+    gen = torch.Generator(device="cuda").manual_seed(w.seed)  # plain Gaussians: 65,280 per-unit draws would be slow
+    data = {"q": torch.randn((L, S, H, W, d), generator=gen, device="cuda").to(torch.bfloat16),
+            "k": torch.randn((L, H, N, d), generator=gen, device="cuda").to(torch.bfloat16),
+            "v": torch.randn((L, H, N, d), generator=gen, device="cuda").to(torch.bfloat16)}
+    _check_all(w, sample_units(w, 12), data=data)
 
 
 def test_dominant_sink_one_row():
