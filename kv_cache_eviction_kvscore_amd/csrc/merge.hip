@@ -50,11 +50,31 @@ __global__ __launch_bounds__(256) void merge_sum_kernel(Dev p, const float* __re
     for (int i = 0; i < NV; ++i) *(f32x4v*)(out + j0 + 4 * (tid + 256 * i)) = acc[i];
     return;
   }
+  // otherwise (rows not 16-byte aligned, as with an odd total token count, or the
+  // sequence's last chunk) 4-byte pieces, NB of them per thread with every tile's loads in
+  // flight before the sums; the same order of additions as above
+  constexpr int NB = 8;
   const int64_t jend = (n < j0 + kMergeChunk) ? n : j0 + kMergeChunk;
-  for (int64_t j = j0 + tid; j < jend; j += 256) {
-    float a1 = 0.f;
-    for (int t = 0; t < p.Tq; ++t) a1 += pb[(int64_t)t * p.N + j];
-    out[j] = a1;
+  for (int64_t jb = j0 + tid; jb < jend; jb += 256 * NB) {
+    float acc[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) acc[i] = 0.f;
+    for (int t = 0; t < p.Tq; ++t) {
+      const float* row = pb + (int64_t)t * p.N;
+      float x[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int64_t j = jb + 256 * i;
+        x[i] = j < jend ? __builtin_nontemporal_load(row + j) : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) acc[i] += x[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t j = jb + 256 * i;
+      if (j < jend) out[j] = acc[i];
+    }
   }
 }
 
