@@ -217,10 +217,15 @@ int make_decdev(const kvscore_problem* p, const int64_t* off, kvs::DecDev& d) {
   d.U = (int)U;
   const float scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
   d.c1 = (float)((double)scale * 1.4426950408889634);
-  // about 2048 workgroups in all (8 per CU), at least 256 keys per split
-  int64_t ns = std::max<int64_t>(1, (2048 + U - 1) / U);
-  ns = std::min<int64_t>(ns, std::max<int64_t>(1, max_len / 256));
-  const int64_t chunk = ((max_len + ns - 1) / ns + 63) / 64 * 64;
+  // Splits of one length for every segment: about 2048 of them in all (8 workgroups per
+  // CU), at least 256 keys each, so the longest segments of a ragged batch do not hold the
+  // launch while the short ones idle; at most kDecodeMaxSplits splits of the longest segment
+  // (the workspace holds that many records per segment). Workgroups past a segment's last
+  // split return at once.
+  constexpr int64_t kDecodeMaxSplits = 64;
+  int64_t chunk = std::max<int64_t>(256, (off[U] + 2047) / 2048);
+  chunk = std::max<int64_t>(chunk, (max_len + kDecodeMaxSplits - 1) / kDecodeMaxSplits);
+  chunk = (chunk + 63) / 64 * 64;
   if (chunk > (int64_t)1 << 30) return fail(KVSCORE_EINVAL, "segment too long");
   d.chunk = (int)chunk;
   d.nsplit = (int)((max_len + chunk - 1) / chunk);
