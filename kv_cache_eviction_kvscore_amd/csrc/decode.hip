@@ -88,47 +88,61 @@ __global__ __launch_bounds__(NTHREADS) void decode_partial_kernel(DecDev p, cons
   const __bf16* kb = kc + (a0 + k0) * D + 8 * dc;
   const __bf16* vb = vc + (a0 + k0) * D + 8 * dc;
 
-  // stream `stream` takes keys stream, stream + NSTREAM, ... of the split
-  auto step = [&](const u32x4& kx, const u32x4& vx) __attribute__((always_inline)) {
-    float x[G];
+  // stream `stream` takes keys stream, stream + NSTREAM, ... of the split. A block of R of
+  // its keys at a time: the R * G logits first (independent chains), one wave-wide test for
+  // a reference move over all of them (with the block's maximum per head), then the
+  // weights and the value sums in key order.
+  auto block = [&](auto rc, const u32x4* kx, const u32x4* vx) __attribute__((always_inline)) {
+    constexpr int R = decltype(rc)::value;
+    float x[R][G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float dsum = 0.f;
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const unsigned kw = kx[i];
-        dsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][i]), __builtin_bit_cast(bf16x2, kw),
-                                               dsum, false);
+      for (int h = 0; h < G; ++h) {
+        float dsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const unsigned kw = kx[r][i];
+          dsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][i]), __builtin_bit_cast(bf16x2, kw),
+                                                 dsum, false);
+        }
+        x[r][h] = group_sum<LPK>(dsum) * c1;  // log2 units
       }
-      x[h] = group_sum<LPK>(dsum) * c1;  // log2 units
-    }
     bool need = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h) need |= x[h] > m[h] + kSlack;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int h = 0; h < G; ++h) need |= x[r][h] > m[h] + kSlack;
     if (__any(need)) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const bool mv = x[h] > m[h] + kSlack;
-        const float alpha = mv ? __builtin_amdgcn_exp2f(m[h] - x[h]) : 1.f;  // exp2(-inf) = 0 at the start
-        m[h] = mv ? x[h] : m[h];
+        float xm = x[0][h];
+#pragma unroll
+        for (int r = 1; r < R; ++r) xm = fmaxf(xm, x[r][h]);
+        const bool mv = xm > m[h] + kSlack;
+        const float alpha = mv ? __builtin_amdgcn_exp2f(m[h] - xm) : 1.f;  // exp2(-inf) = 0 at the start
+        m[h] = mv ? xm : m[h];
         lsum[h] *= alpha;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[h][i] *= alpha;
       }
     }
-    float vf[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const unsigned vw = vx[i];
-      vf[2 * i] = bf16lo(vw);
-      vf[2 * i + 1] = bf16hi(vw);
-    }
+    for (int r = 0; r < R; ++r) {
+      float vf[8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float pr = __builtin_amdgcn_exp2f(x[h] - m[h]);  // <= 2^kSlack
-      lsum[h] += pr;
+      for (int i = 0; i < 4; ++i) {
+        const unsigned vw = vx[r][i];
+        vf[2 * i] = bf16lo(vw);
+        vf[2 * i + 1] = bf16hi(vw);
+      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(pr, vf[i], acc[h][i]);
+      for (int h = 0; h < G; ++h) {
+        const float pr = __builtin_amdgcn_exp2f(x[r][h] - m[h]);  // <= 2^kSlack
+        lsum[h] += pr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(pr, vf[i], acc[h][i]);
+      }
     }
   };
 
@@ -142,14 +156,13 @@ __global__ __launch_bounds__(NTHREADS) void decode_partial_kernel(DecDev p, cons
       kx[r] = __builtin_nontemporal_load((const u32x4*)(kb + (int64_t)(j + r * NSTREAM) * D));
       vx[r] = __builtin_nontemporal_load((const u32x4*)(vb + (int64_t)(j + r * NSTREAM) * D));
     }
-#pragma unroll
-    for (int r = 0; r < UNROLL; ++r) step(kx[r], vx[r]);
+    block(std::integral_constant<int, UNROLL>{}, kx, vx);
     j += UNROLL * NSTREAM;
   }
   for (; it < nsteps; ++it, j += NSTREAM) {
     const u32x4 kx = __builtin_nontemporal_load((const u32x4*)(kb + (int64_t)j * D));
     const u32x4 vx = __builtin_nontemporal_load((const u32x4*)(vb + (int64_t)j * D));
-    step(kx, vx);
+    block(std::integral_constant<int, 1>{}, &kx, &vx);
   }
 
   // merge the streams: first the KPS groups of the wave (lanes dc + LPK*ks), ascending
