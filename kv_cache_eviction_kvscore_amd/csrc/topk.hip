@@ -45,12 +45,17 @@ __device__ inline unsigned f2key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ inline int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+// Inclusive sum over the lanes of a wave, in registers (DPP, no LDS): Hillis-Steele steps of
+// 1, 2, 4 and 8 lanes within each row of 16 (a lane whose source lies outside its row adds
+// 0), then the last lane of row 0 is broadcast into row 1 and that of row 2 into row 3, then
+// the last lane of row 1 into rows 2 and 3.
+__device__ inline int wave_incl_scan(int x, int) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
   return x;
 }
 
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(256) void pool_kernel(Dev p, const float* __restric
 }
 
 struct SelectSmem {
-  unsigned s_digit, s_above, s_count;
+  unsigned s_digit[2], s_above[2], s_count[2];
   int wsum[2][NWAVES];
   long long red[2][NWAVES];
 };
@@ -142,6 +147,69 @@ constexpr int kBitBase = 1 << kBits12;
 constexpr int kBitWords = ((1 << kBits0) - kBitBase) / 2;  // words per bitmask
 constexpr int64_t kBitCap = (int64_t)kBitWords * 32;       // competitors the bitmasks cover
 
+// For each r < NR: the bin of h[0, nb) (in LDS) where the count from the top first reaches
+// kr[r] (1 <= kr[r] <= the total), into sm.s_digit[r], with the count above it
+// (s_above[r]) and its own (s_count[r]); every thread returns with them visible. With
+// PER > 1, nb = PER * NT and thread t owns bins nb-1-PER*t .. nb-PER*(t+1) (descending);
+// with PER = 1, thread t < nb owns bin nb-1-t. A scan over the threads' totals finds the
+// owning thread, and that thread the bin.
+template <int PER, int NR>
+__device__ __attribute__((always_inline)) void scan_digit(SelectSmem& sm, HistSmem& hs, const unsigned* h, int nb,
+                                                          const int64_t (&kr)[NR]) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool owns = tid * PER < nb;
+  unsigned tot = 0;
+  // the run's bins in an order rotated by lane / 2, so a half-wave's reads fall in distinct
+  // LDS banks
+  if (owns)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) tot += h[nb - 1 - (PER * tid + ((e + (lane >> 1)) & (PER - 1)))];
+  const int incl_w = wave_incl_scan((int)tot, lane);
+  if (lane == 63) hs.tsum[wave] = incl_w;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVES; ++w) {
+    const int t = hs.tsum[w];
+    before += w < wave ? t : 0;
+  }
+  // counts fit 32 bits (a unit has fewer than 2^31 competitors)
+  const unsigned incl = (unsigned)(before + incl_w), excl = incl - tot;
+  bool mine[NR], any = false;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    mine[r] = owns && excl < (unsigned)kr[r] && (unsigned)kr[r] <= incl;
+    any = any || mine[r];
+  }
+  if (any) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      if (!mine[r]) continue;
+      unsigned above = excl;
+      int e = 0;
+      if constexpr (PER >= 4) {  // runs of four bins first (one 16-byte read each)
+        for (; e + 4 < PER; e += 4) {
+          const uint4 v = *(const uint4*)(h + nb - 4 - PER * tid - e);
+          const unsigned s4 = v.x + v.y + v.z + v.w;
+          if (above + s4 >= (unsigned)kr[r]) break;
+          above += s4;
+        }
+      }
+      unsigned c = h[nb - 1 - (PER * tid + e)];
+      while (above + c < (unsigned)kr[r]) {  // ends at e < PER
+        above += c;
+        c = h[nb - 1 - (PER * tid + ++e)];
+      }
+      sm.s_digit[r] = (unsigned)(nb - 1 - (PER * tid + e));
+      sm.s_above[r] = above;
+      sm.s_count[r] = c;
+    }
+  }
+  __syncthreads();
+}
+constexpr int kPer0 = (1 << kBits0) / NT;  // bins per thread in a 14-bit scan
+static_assert(kPer0 * NT == (1 << kBits0) && (1 << kBits12) <= NT, "scan shapes");
+
 // Radix select of the kr-th largest key among the keys `visit` enumerates (each thread
 // calls f(key) on its share, all lanes of a wave together): T = that key, need_eq = how
 // many keys equal to T are among the kr largest. Three passes (14, 9 and 9 bits) count
@@ -153,9 +221,9 @@ constexpr int64_t kBitCap = (int64_t)kBitWords * 32;       // competitors the bi
 // of sure for every key above the threshold's top 14 bits, and listed tells whether the
 // list was filled (the caller then marks the listed keys against T itself).
 template <class Visit>
-__device__ void radix_select(SelectSmem& sm, HistSmem& hs, Visit visit, int64_t kr, unsigned& T, int64_t& need_eq,
+__device__ __attribute__((always_inline)) void radix_select(SelectSmem& sm, HistSmem& hs, Visit visit, int64_t kr, unsigned& T, int64_t& need_eq,
                              CandSmem* cs, unsigned* sure, bool& listed) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   unsigned prefix = 0, pmask = 0;
   listed = false;  // uniform: the last pass reads cs
   for (int pass = 0; pass < 3; ++pass) {
@@ -164,20 +232,20 @@ __device__ void radix_select(SelectSmem& sm, HistSmem& hs, Visit visit, int64_t 
     const int nb = 1 << bits;
     const unsigned dmask = (unsigned)nb - 1u;
     // keys with the current prefix: the last pass's count of its digit
-    const bool collect = cs && pass == 1 && sm.s_count <= (unsigned)kCandCap;
+    const bool collect = cs && pass == 1 && sm.s_count[0] <= (unsigned)kCandCap;
     const bool mark = collect && sure;
     for (int i = tid; i < nb; i += NT) hs.hist[i] = 0;
     if (mark)  // both bitmasks
       for (int i = tid; i < 2 * kBitWords; i += NT) hs.hist[kBitBase + i] = 0;
     if (collect && tid == 0) cs->n = 0;
     __syncthreads();
-    auto count = [&](unsigned key, int64_t) { hist_add(hs.hist, (key & pmask) == prefix, (key >> shift) & dmask); };
+    auto count = [&](unsigned key, int) { hist_add(hs.hist, (key & pmask) == prefix, (key >> shift) & dmask); };
     if (pass == 0) {
-      visit([&](unsigned key, int64_t) { hist_add_all(hs.hist, key >> shift); });
+      visit([&](unsigned key, int) { hist_add_all(hs.hist, key >> shift); });
     } else if (listed) {
       for (int i = tid; i < (int)cs->n; i += NT) count(cs->key[i], 0);
     } else if (collect) {
-      visit([&](unsigned key, int64_t c) {
+      visit([&](unsigned key, int c) {
         const bool in = (key & pmask) == prefix;
         hist_add(hs.hist, in, (key >> shift) & dmask);
         if (mark && (key & pmask) > prefix) atomicOr(&sure[c >> 5], 1u << (c & 31));
@@ -199,41 +267,199 @@ __device__ void radix_select(SelectSmem& sm, HistSmem& hs, Visit visit, int64_t 
     }
     __syncthreads();
     listed = listed || collect;
-    // thread t owns bins nb-1-per*t .. nb-per*(t+1) (descending); a scan over the threads'
-    // totals finds the thread, and that thread the bin, where the running count from the
-    // top first reaches kr
-    const int per = nb >= NT ? nb / NT : 1;
-    const bool owns = tid * per < nb;
-    unsigned tot = 0;
-    if (owns)
-      for (int e = 0; e < per; ++e) tot += hs.hist[nb - 1 - (per * tid + e)];
-    const int incl_w = wave_incl_scan((int)tot, lane);
-    if (lane == 63) hs.tsum[wave] = incl_w;
-    __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += hs.tsum[w];
-    const int64_t incl = (int64_t)before + incl_w, excl = incl - (int64_t)tot;
-    if (owns && excl < kr && kr <= incl) {
-      unsigned above = (unsigned)excl;
-      for (int e = 0; e < per; ++e) {
-        const int bin = nb - 1 - (per * tid + e);
-        const unsigned c = hs.hist[bin];
-        if ((int64_t)(above + c) >= kr) {
-          sm.s_digit = (unsigned)bin;
-          sm.s_above = above;
-          sm.s_count = c;
-          break;
-        }
-        above += c;
-      }
-    }
-    __syncthreads();
-    prefix |= sm.s_digit << shift;
+    const int64_t k1[1] = {kr};
+    if (pass == 0) scan_digit<kPer0, 1>(sm, hs, hs.hist, nb, k1);
+    else scan_digit<1, 1>(sm, hs, hs.hist, nb, k1);
+    prefix |= sm.s_digit[0] << shift;
     pmask |= dmask << shift;
-    kr -= sm.s_above;
+    kr -= sm.s_above[0];
   }
   T = prefix;
   need_eq = kr;
+}
+
+// Exact select over the cnt keys of a list in LDS: T = the kr-th largest (1 <= kr <= cnt),
+// need_eq = how many keys equal to T are among the kr largest, given that every key shares
+// the bits of prefix above bit hb. Passes of 9 bits from bit hb down count into
+// hs.hist[0, 512), below kBitBase, so the bitmasks are kept.
+__device__ __attribute__((always_inline)) void list_select(SelectSmem& sm, HistSmem& hs, const unsigned* key, int cnt,
+                                                           int64_t kr, unsigned prefix, int hb, unsigned& T,
+                                                           int64_t& need_eq) {
+  const int tid = threadIdx.x;
+  unsigned pmask = hb >= 32 ? 0u : ~0u << hb;
+  while (hb > 0) {
+    const int bits = hb < kBits12 ? hb : kBits12;
+    const int shift = hb - bits, nb = 1 << bits;
+    const unsigned dmask = (unsigned)nb - 1u;
+    for (int i = tid; i < nb; i += NT) hs.hist[i] = 0;
+    __syncthreads();
+    for (int i0 = 0; i0 < cnt; i0 += NT) {  // whole waves through hist_add
+      const int i = i0 + tid;
+      const unsigned x = i < cnt ? key[i] : 0u;
+      hist_add(hs.hist, i < cnt && (x & pmask) == prefix, (x >> shift) & dmask);
+    }
+    __syncthreads();
+    const int64_t k1[1] = {kr};
+    scan_digit<1, 1>(sm, hs, hs.hist, nb, k1);
+    prefix |= sm.s_digit[0] << shift;
+    kr -= sm.s_above[0];
+    pmask |= dmask << shift;
+    hb = shift;
+  }
+  T = prefix;
+  need_eq = kr;
+}
+
+// Sample-guided select of the kr-th largest competitor key in one read of the scores, into
+// the list and bitmasks the emission takes. A strided sample (one 4-key run per thread)
+// gives a band [lo, hi] of keys that should hold the threshold: the sample's order
+// statistics a few standard deviations of a binomial count either side of the threshold's
+// expected rank, widened to whole bins of the top 23 key bits. One read then marks every
+// key above hi as surely kept and lists the band's keys (key and competitor index), each
+// wave in a region of its own (no atomics). The band held the threshold if A < kr <= A + L
+// (A keys above it, L listed, no region overflowed); the regions are then packed into one
+// list and the threshold is the (kr - A)-th largest listed key, found in LDS. Returns false
+// otherwise (uniform), and the caller selects from scratch: the sample steers only how much
+// work is done, never the result. Units with at most kCandCap competitors list them all
+// without a sample.
+constexpr int kWaveCap = kCandCap / NWAVES;  // listed keys per wave region
+constexpr int kPackPer = kCandCap / NT;      // list entries per thread when packing
+static_assert(kWaveCap * NWAVES == kCandCap && kPackPer * NT == kCandCap, "regions tile the list");
+
+template <class Visit, class Prime>
+__device__ __attribute__((always_inline)) bool band_select(SelectSmem& sm, HistSmem& hs, CandSmem& cs, Visit visit,
+                                                           Prime prime, const float* __restrict__ c0, int64_t m,
+                                                           int64_t kr,
+                                                           unsigned* sure, unsigned* tie, unsigned& T,
+                                                           int64_t& need_eq) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  unsigned lo = 0u, hi = ~0u;
+  if (m > kCandCap) {
+    constexpr int MS = 4 * NT;  // sampled keys
+    const int64_t j = (int64_t)tid * (m >> 2) / NT * 4;  // <= m - 4
+    unsigned x[4];
+    if ((((size_t)c0) & 15) == 0) {
+      const float4 v = *(const float4*)(c0 + j);
+      x[0] = f2key(v.x);
+      x[1] = f2key(v.y);
+      x[2] = f2key(v.z);
+      x[3] = f2key(v.w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = f2key(c0[j + e]);
+    }
+    prime();  // the read's first loads in flight during the sample's selection
+    // expected rank of the threshold in the sample, and the band's half-width in sample ranks
+    const float rho = (float)kr * (float)MS / (float)m;
+    const float half = 4.f * sqrtf(rho * (1.f - rho / (float)MS)) + 16.f;
+    const int64_t rh = (int64_t)floorf(rho - half), rl = (int64_t)ceilf(rho + half);
+    const int64_t r0 = rh < 1 ? 1 : (rh > MS ? MS : rh), r1 = rl < 1 ? 1 : (rl > MS ? MS : rl);
+    // the sample's top 14 bits (one histogram for both ranks), then the next 9 for each
+    constexpr int sh0 = 32 - kBits0, sh1 = sh0 - kBits12;
+    for (int i = tid; i < (1 << kBits0); i += NT) hs.hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hist_add_all(hs.hist, x[e] >> sh0);
+    __syncthreads();
+    const int64_t rr[2] = {r0, r1};
+    scan_digit<kPer0, 2>(sm, hs, hs.hist, 1 << kBits0, rr);
+    const unsigned d0 = sm.s_digit[0], d1 = sm.s_digit[1];  // d0 >= d1
+    // the next 9 bits of the keys in bins d0 and d1, in one histogram of two halves: d0's
+    // keys in the upper half, above all of d1's (when the bins differ)
+    const int64_t qq[2] = {r0 - sm.s_above[0], r1 - sm.s_above[1] + (d0 != d1 ? sm.s_count[0] : 0u)};
+    for (int i = tid; i < 2 << kBits12; i += NT) hs.hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned top = x[e] >> sh0;
+      const unsigned dg = ((x[e] >> sh1) & ((1u << kBits12) - 1u)) | (top == d0 ? 1u << kBits12 : 0u);
+      hist_add(hs.hist, top == d0 || top == d1, dg);
+    }
+    __syncthreads();
+    scan_digit<1, 2>(sm, hs, hs.hist, 2 << kBits12, qq);
+    const unsigned e0 = sm.s_digit[0] & ((1u << kBits12) - 1u), e1 = sm.s_digit[1] & ((1u << kBits12) - 1u);
+    if (rh >= 1) hi = (d0 << sh0) | (e0 << sh1) | ((1u << sh1) - 1u);
+    if (rl <= MS) lo = (d1 << sh0) | (e1 << sh1);
+  }
+  for (int i = tid; i < 2 * kBitWords; i += NT) sure[i] = 0;  // both bitmasks
+  __syncthreads();
+  const bool all = m <= kCandCap;  // uniform
+  unsigned wn = 0;                  // keys this wave listed (uniform)
+  if (all) {  // every competitor, at its own index
+    visit([&](unsigned key, int c) {
+      cs.key[c] = key;
+      cs.pos[c] = (unsigned)c;
+    });
+  } else {
+    unsigned* wkey = cs.key + wave * kWaveCap;
+    unsigned* wpos = cs.pos + wave * kWaveCap;
+    visit([&](unsigned key, int c) {
+      if (key > hi) atomicOr(&sure[c >> 5], 1u << (c & 31));
+      const bool in = key >= lo && key <= hi;
+      const unsigned long long msk = __ballot(in);
+      const unsigned slot =
+          wn + __builtin_amdgcn_mbcnt_hi((unsigned)(msk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)msk, 0u));
+      if (in && slot < (unsigned)kWaveCap) {
+        wkey[slot] = key;
+        wpos[slot] = (unsigned)c;
+      }
+      wn += (unsigned)__popcll(msk);
+    });
+  }
+  if (lane == 0) sm.wsum[1][wave] = (int)wn;
+  if (all && tid == 0) cs.n = (unsigned)m;
+  __syncthreads();
+  if (all) {
+    list_select(sm, hs, cs.key, (int)m, kr, 0u, 32, T, need_eq);
+    return true;
+  }
+  // A = the keys above the band, from the bitmask
+  unsigned a = 0;
+  for (int i = tid; i < kBitWords; i += NT) a += __popc(sure[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
+  if (lane == 0) sm.wsum[0][wave] = (int)a;
+  __syncthreads();
+  int64_t A = 0;
+  int L = 0, before = 0;
+  bool over = false;
+  for (int w = 0; w < NWAVES; ++w) {
+    const int c = sm.wsum[1][w];
+    A += (unsigned)sm.wsum[0][w];
+    over = over || c > kWaveCap;
+    if (w == tid) before = L;
+    L += c;
+  }
+  if (tid < NWAVES) sm.red[0][tid] = before;  // where region tid goes in the packed list
+  __syncthreads();
+  if (over || A >= kr || kr > A + L) return false;
+  // pack the regions into one list: all entries into registers, then to their places
+  unsigned pk[kPackPer], pp[kPackPer];
+  int pd[kPackPer];
+#pragma unroll
+  for (int t = 0; t < kPackPer; ++t) {
+    const int i = tid + NT * t, w = i / kWaveCap, r = i - w * kWaveCap;
+    pd[t] = -1;
+    if (r < sm.wsum[1][w]) {
+      pk[t] = cs.key[i];
+      pp[t] = cs.pos[i];
+      pd[t] = (int)sm.red[0][w] + r;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < kPackPer; ++t)
+    if (pd[t] >= 0) {
+      cs.key[pd[t]] = pk[t];
+      cs.pos[pd[t]] = pp[t];
+    }
+  if (tid == 0) cs.n = (unsigned)L;
+  __syncthreads();
+  // keys in [lo, hi] share the bits above the highest bit where lo and hi differ
+  const unsigned dif = lo ^ hi;
+  const int hb = dif ? 32 - __clz((int)dif) : 0;
+  list_select(sm, hs, cs.key, L, kr - A, hb >= 32 ? 0u : lo & (~0u << hb), hb, T, need_eq);
+  return true;
 }
 
 // Ordered stream compaction of one segment (b rows at out) over positions j in [0, n), in
@@ -242,7 +468,7 @@ __device__ void radix_select(SelectSmem& sm, HistSmem& hs, Visit visit, int64_t 
 // the first need_eq tied positions are taken. Ballots and a sum over the waves give every
 // kept position its slot.
 template <class Flags>
-__device__ void emit_ordered(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int64_t need_eq, int64_t n,
+__device__ __attribute__((always_inline)) void emit_ordered(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int64_t need_eq, int64_t n,
                              Flags flags) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int64_t sure_base = 0, eq_base = 0;
@@ -296,7 +522,7 @@ __device__ void emit_ordered(SelectSmem& sm, int32_t* __restrict__ out, int64_t 
 // The same from the scores: positions j < ns or j >= cand (sinks, window) are kept; the
 // selection sel 0 keeps no competitor, 1 all, 2 key > T and the first need_eq keys equal to
 // T (ascending position).
-__device__ void emit_segment(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int sel, unsigned T,
+__device__ __attribute__((always_inline)) void emit_segment(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int sel, unsigned T,
                              int64_t need_eq, const float* __restrict__ sc, int64_t n, int64_t cand, int64_t ns) {
   const int tid = threadIdx.x;
   // the keys of a round are loaded three rounds ahead, 16 bytes per lane when aligned (the
@@ -355,7 +581,7 @@ __device__ void emit_segment(SelectSmem& sm, int32_t* __restrict__ out, int64_t 
 // position ns + c), for a selection that filled them: the sinks, then the selected
 // competitors, then the window. Thread t takes the 32 competitors of word t of each round
 // of NT words; block scans of the words' counts give its slots.
-__device__ void emit_words(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int64_t need_eq,
+__device__ __attribute__((always_inline)) void emit_words(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int64_t need_eq,
                            const unsigned* sure_bits, const unsigned* tie_bits, int64_t n, int64_t cand, int64_t ns) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t m = cand - ns;
@@ -442,47 +668,67 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
     unsigned* sure = &hs.hist[kBitBase];
     unsigned* tie = sure + kBitWords;
     bool listed = false;
-    radix_select(sm, hs, [&](auto f) {
-      int64_t m4 = 0;  // competitors read as float4s
-      if ((((size_t)c0) & 15) == 0) {
-        // 16-byte loads: thread tid takes float4s tid + NT r, four rounds r per step, the
-        // next step's issued before this one is counted (eight in flight per thread, 128 KB
-        // per workgroup); two buffers with fixed roles and two steps per trip (a register
-        // rotation would make the compiler wait for the next step's loads at the copy)
-        constexpr int V = 4;
-        m4 = m >> 2;
-        const int64_t nr = (m4 + NT - 1) / NT;  // rounds
-        float4 A[V], B[V];
-        auto ld = [&](float4* buf, int64_t r0) __attribute__((always_inline)) {
+    // A read of the competitors, visit(f) calling f(key, c) for each. With 16-byte loads,
+    // thread tid takes float4s tid + NT r, four rounds r per step, the next step's issued
+    // before this one is counted (eight in flight per thread, 128 KB per workgroup); two
+    // buffers with fixed roles and two steps per trip (a register rotation would make the
+    // compiler wait for the next step's loads at the copy). prime() issues the first step's
+    // loads ahead of the next read.
+    // competitor indices fit 32 bits (kept positions are int32)
+    constexpr int V = 4;
+    const int mc = (int)m;
+    const int m4 = ((((size_t)c0) & 15) == 0 && mc >= 4) ? mc >> 2 : 0;  // competitors read as float4s
+    float4 A[V], B[V];
+    bool primed = false;
+    // loads past the row repeat its last float4 (no branch around a load, so the next step's
+    // loads need not wait for this one's)
+    auto ld = [&](float4* buf, int r0) __attribute__((always_inline)) {
 #pragma unroll
-          for (int i = 0; i < V; ++i) {
-            const int64_t fi = tid + NT * (r0 + i);
-            if (fi < m4) buf[i] = *(const float4*)(c0 + 4 * fi);
-          }
-        };
-        auto run = [&](const float4* buf, int64_t r0) __attribute__((always_inline)) {
-#pragma unroll
-          for (int i = 0; i < V; ++i) {
-            const int64_t fi = tid + NT * (r0 + i);
-            if (fi < m4) {
-              const int64_t j = 4 * fi;
-              f(f2key(buf[i].x), j);
-              f(f2key(buf[i].y), j + 1);
-              f(f2key(buf[i].z), j + 2);
-              f(f2key(buf[i].w), j + 3);
-            }
-          }
-        };
+      for (int i = 0; i < V; ++i) {
+        const int fi = tid + NT * (r0 + i);
+        buf[i] = *(const float4*)(c0 + 4 * (fi < m4 ? fi : m4 - 1));
+      }
+    };
+    auto prime = [&]() __attribute__((always_inline)) {
+      if (m4 > 0) {
         ld(A, 0);
-        for (int64_t r = 0; r < nr; r += 2 * V) {
+        primed = true;
+      }
+    };
+    auto visit = [&](auto f) {
+      auto run = [&](const float4* buf, int r0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const int fi = tid + NT * (r0 + i);
+          if (fi < m4) {
+            const int j = 4 * fi;
+            f(f2key(buf[i].x), j);
+            f(f2key(buf[i].y), j + 1);
+            f(f2key(buf[i].z), j + 2);
+            f(f2key(buf[i].w), j + 3);
+          }
+        }
+      };
+      if (m4 > 0) {
+        const int nr = (m4 + NT - 1) / NT;  // rounds
+        if (!primed) ld(A, 0);
+        primed = false;
+        for (int r = 0; r < nr; r += 2 * V) {
           ld(B, r + V);
           run(A, r);
           ld(A, r + 2 * V);
           run(B, r + V);
         }
       }
-      for (int64_t j = 4 * m4 + tid; j < m; j += NT) f(f2key(c0[j]), j);
-    }, k, T, need_eq, &cs, m <= kBitCap ? sure : nullptr, listed);
+      for (int j = 4 * m4 + tid; j < mc; j += NT) f(f2key(c0[j]), j);
+    };
+    // the band's expected width in keys, from the sample half-width at the threshold's rank
+    const float q = (float)k / (float)m;
+    const float band = 2.f * (4.f * sqrtf(4.f * NT * q * (1.f - q)) + 16.f) * (float)m / (4.f * NT);
+    if (m <= kBitCap && (m <= kCandCap || band <= 0.85f * kCandCap)) {
+      if (band_select(sm, hs, cs, visit, prime, c0, m, k, sure, tie, T, need_eq)) listed = true;
+    }
+    if (!listed) radix_select(sm, hs, visit, k, T, need_eq, &cs, m <= kBitCap ? sure : nullptr, listed);
     if (listed && m <= kBitCap) {
       // the listed keys (those sharing T's top 14 bits) against T; the ones above those bits
       // were marked during the second pass

@@ -4,6 +4,14 @@ DropKV page, "Methodology in Plain English": keep the largest scores, the recent
 always. The selection is integer work decided on the same fp32 values on both sides, so
 every segment must equal the oracle's (a full sort on (-score, position)) exactly.
 
+Most units are selected in one read of the scores: a strided sample (one 4-key run per
+thread of the workgroup, 4096 keys) gives a band of keys around the threshold's expected
+rank; one read marks the keys above the band and lists the band's keys in LDS, and the
+threshold is found in that list. A unit with at most 11264 competitors lists them all. When
+the band missed the threshold or overflowed the list (all keys equal; a periodic pattern
+whose high half the sample never sees; a band wider than the list), the unit is selected
+from scratch by the radix select below, so the sample never changes the result.
+
 The score distributions steer the radix select down its routes: when at most 11264 keys
 share the threshold's top 14 bits, the second pass lists them (key and position) in LDS and
 marks every competitor above those bits in an LDS bitmask; the last pass and the ordered
@@ -42,16 +50,23 @@ def _scores(kind, n, rng):
         x = np.exp2(rng.uniform(-60.0, 0.0, n)).astype(np.float32)
         x[rng.choice(n, 8000, replace=False)] = (2.0 + 0.25 * rng.integers(0, 16, 8000)).astype(np.float32)
         return x
+    if kind == "periodic":  # high scores in the second half of every 128 positions, low in the first
+        j = np.arange(n)
+        return np.where(j % 128 >= 64, rng.uniform(4.0, 8.0, n), rng.uniform(0.0, 1.0, n)).astype(np.float32)
     raise ValueError(kind)
 
 
-KINDS = ["log_uniform", "one_top_byte", "sixteen_values", "all_equal", "ties_in_list", "narrow"]
+KINDS = ["log_uniform", "one_top_byte", "sixteen_values", "all_equal", "ties_in_list", "narrow", "periodic"]
 
 
 @pytest.mark.parametrize("budget_extra,n_sink,n", [(5000, 0, 60011), (0, 0, 60011), (70000, 0, 60011),
-                                                    (5000, 5, 60011), (5000, 37, 60011), (20000, 3, 300007)])
+                                                    (5000, 5, 60011), (5000, 37, 60011), (20000, 3, 300007),
+                                                    (5000, 0, 131088), (70000, 0, 131088), (500, 0, 9000),
+                                                    (6000, 2, 9000), (3000, 0, 11280), (3000, 0, 11281)])
 def test_topk_threshold_bins_both_routes(budget_extra, n_sink, n):
-    # n = 60011 is ragged against the 4-key loads; 300007 - W competitors exceed the bitmasks
+    # n = 60011 is ragged against the 4-key loads; 300007 - W competitors exceed the bitmasks;
+    # 131088 - W = 2^17 competitors put every sampled run in the low half of the periodic
+    # scores; 11280 - W competitors fit the LDS list whole, 11281 - W do not
     L, S, Hkv, Hq, d, W = 1, 1, len(KINDS), len(KINDS), 128, 16
     rng = np.random.default_rng(budget_extra + 5 + n_sink)
     p = api.Problem(num_seqs=S, num_layers=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, window=W,
