@@ -116,8 +116,10 @@ __global__ __launch_bounds__(256) void pool_kernel(Dev p, const float* __restric
   }
 }
 
+constexpr int kFew = 64;  // a list select finishes in one wave once this few keys are left
 struct SelectSmem {
   unsigned s_digit[2], s_above[2], s_count[2];
+  unsigned few_n, few_key[kFew];
   int wsum[2][NWAVES];
   long long red[2][NWAVES];
 };
@@ -281,13 +283,16 @@ __device__ __attribute__((always_inline)) void radix_select(SelectSmem& sm, Hist
 // Exact select over the cnt keys of a list in LDS: T = the kr-th largest (1 <= kr <= cnt),
 // need_eq = how many keys equal to T are among the kr largest, given that every key shares
 // the bits of prefix above bit hb. Passes of 9 bits from bit hb down count into
-// hs.hist[0, 512), below kBitBase, so the bitmasks are kept.
+// hs.hist[0, 512), below kBitBase, so the bitmasks are kept. Once at most kFew keys share
+// the prefix found so far, they are gathered and one wave ranks them directly: the key
+// with fewer than kr keys above it and at least kr at or above it.
 __device__ __attribute__((always_inline)) void list_select(SelectSmem& sm, HistSmem& hs, const unsigned* key, int cnt,
                                                            int64_t kr, unsigned prefix, int hb, unsigned& T,
                                                            int64_t& need_eq) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   unsigned pmask = hb >= 32 ? 0u : ~0u << hb;
-  while (hb > 0) {
+  unsigned left = (unsigned)cnt;  // keys sharing the prefix
+  while (hb > 0 && left > (unsigned)kFew) {
     const int bits = hb < kBits12 ? hb : kBits12;
     const int shift = hb - bits, nb = 1 << bits;
     const unsigned dmask = (unsigned)nb - 1u;
@@ -303,8 +308,46 @@ __device__ __attribute__((always_inline)) void list_select(SelectSmem& sm, HistS
     scan_digit<1, 1>(sm, hs, hs.hist, nb, k1);
     prefix |= sm.s_digit[0] << shift;
     kr -= sm.s_above[0];
+    left = sm.s_count[0];
     pmask |= dmask << shift;
     hb = shift;
+  }
+  if (hb > 0) {
+    if (tid == 0) sm.few_n = 0;
+    __syncthreads();
+    for (int i0 = 0; i0 < cnt; i0 += NT) {
+      const int i = i0 + tid;
+      const unsigned x = i < cnt ? key[i] : 0u;
+      const bool in = i < cnt && (x & pmask) == prefix;
+      const unsigned long long msk = __ballot(in);
+      if (msk) {  // one slot reservation per wave
+        const int first = __ffsll((long long)msk) - 1;
+        unsigned base = 0;
+        if (lane == first) base = atomicAdd(&sm.few_n, (unsigned)__popcll(msk));
+        base = (unsigned)__builtin_amdgcn_readlane((int)base, first);
+        if (in)
+          sm.few_key[base + __builtin_amdgcn_mbcnt_hi((unsigned)(msk >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((unsigned)msk, 0u))] = x;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int nf = (int)left;  // == few_n
+      const unsigned x = lane < nf ? sm.few_key[lane] : 0u;
+      int gt = 0, eq = 0;
+      for (int t = 0; t < nf; ++t) {
+        const unsigned y = sm.few_key[t];
+        gt += y > x ? 1 : 0;
+        eq += y == x ? 1 : 0;
+      }
+      if (lane < nf && gt < kr && kr <= gt + eq) {  // every lane holding the key writes the same
+        sm.s_digit[1] = x;
+        sm.s_above[1] = (unsigned)gt;
+      }
+    }
+    __syncthreads();
+    prefix = sm.s_digit[1];
+    kr -= sm.s_above[1];
   }
   T = prefix;
   need_eq = kr;
@@ -326,10 +369,9 @@ constexpr int kWaveCap = kCandCap / NWAVES;  // listed keys per wave region
 constexpr int kPackPer = kCandCap / NT;      // list entries per thread when packing
 static_assert(kWaveCap * NWAVES == kCandCap && kPackPer * NT == kCandCap, "regions tile the list");
 
-template <class Visit, class Prime>
+template <class Visit>
 __device__ __attribute__((always_inline)) bool band_select(SelectSmem& sm, HistSmem& hs, CandSmem& cs, Visit visit,
-                                                           Prime prime, const float* __restrict__ c0, int64_t m,
-                                                           int64_t kr,
+                                                           const float* __restrict__ c0, int64_t m, int64_t kr,
                                                            unsigned* sure, unsigned* tie, unsigned& T,
                                                            int64_t& need_eq) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -348,7 +390,6 @@ __device__ __attribute__((always_inline)) bool band_select(SelectSmem& sm, HistS
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = f2key(c0[j + e]);
     }
-    prime();  // the read's first loads in flight during the sample's selection
     // expected rank of the threshold in the sample, and the band's half-width in sample ranks
     const float rho = (float)kr * (float)MS / (float)m;
     const float half = 4.f * sqrtf(rho * (1.f - rho / (float)MS)) + 16.f;
@@ -579,72 +620,110 @@ __device__ __attribute__((always_inline)) void emit_segment(SelectSmem& sm, int3
 
 // The same from LDS bitmasks over the competitors (bit c of sure / tie: competitor c, at
 // position ns + c), for a selection that filled them: the sinks, then the selected
-// competitors, then the window. Thread t takes the 32 competitors of word t of each round
-// of NT words; block scans of the words' counts give its slots.
-__device__ __attribute__((always_inline)) void emit_words(SelectSmem& sm, int32_t* __restrict__ out, int64_t b, int64_t need_eq,
-                           const unsigned* sure_bits, const unsigned* tie_bits, int64_t n, int64_t cand, int64_t ns) {
+// competitors, then the window. Thread t takes a run of consecutive words (at most
+// kWordsPer); one block scan of the runs' counts gives every thread its first slot.
+constexpr int kWordsPer = (kBitWords + NT - 1) / NT;
+__device__ __attribute__((always_inline)) void emit_words(SelectSmem& sm, int32_t* __restrict__ out, int64_t b64,
+                                                          int64_t need_eq64, const unsigned* sure_bits,
+                                                          const unsigned* tie_bits, int64_t n64, int64_t cand64,
+                                                          int64_t ns64) {
+  // positions fit 32 bits (kept positions are int32)
+  const int b = (int)b64, neq = (int)need_eq64, n = (int)n64, cand = (int)cand64, ns = (int)ns64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t m = cand - ns;
-  for (int64_t j = tid; j < ns; j += NT) out[j] = (int32_t)j;
-  const int64_t nw = (m + 31) >> 5;
-  int64_t sure_base = 0, eq_base = 0;
-  for (int64_t w0 = 0; w0 < nw; w0 += NT) {
-    const int64_t w = w0 + tid;
-    unsigned sw = 0, tw = 0;
-    if (w < nw) {
-      sw = sure_bits[w];
-      tw = tie_bits[w];
+  const int m = cand - ns;
+  for (int j = tid; j < ns; j += NT) out[j] = j;
+  const int nw = (m + 31) >> 5;
+  const int per = (nw + NT - 1) / NT;  // words per thread, at most kWordsPer
+  const int wb = tid * per;
+  unsigned sw[kWordsPer], tw[kWordsPer];
+  int cs_ = 0, ce = 0;
+#pragma unroll
+  for (int e = 0; e < kWordsPer; ++e) {
+    sw[e] = 0;
+    tw[e] = 0;
+    if (e < per && wb + e < nw) {
+      sw[e] = sure_bits[wb + e];
+      tw[e] = tie_bits[wb + e];
     }
-    const int cs_ = __popc(sw), ce = __popc(tw);
-    const int is = wave_incl_scan(cs_, lane), ie = wave_incl_scan(ce, lane);
-    if (lane == 63) {
-      sm.wsum[0][wave] = is;
-      sm.wsum[1][wave] = ie;
-    }
-    __syncthreads();
-    int ps = is - cs_, pe = ie - ce, ts = 0, te = 0;
-    for (int v = 0; v < NWAVES; ++v) {
-      if (v < wave) {
-        ps += sm.wsum[0][v];
-        pe += sm.wsum[1][v];
+    cs_ += __popc(sw[e]);
+    ce += __popc(tw[e]);
+  }
+  const int is = wave_incl_scan(cs_, lane), ie = wave_incl_scan(ce, lane);
+  if (lane == 63) {
+    sm.wsum[0][wave] = is;
+    sm.wsum[1][wave] = ie;
+  }
+  __syncthreads();
+  int ps = is - cs_, pe = ie - ce, ts = 0, te = 0;
+#pragma unroll
+  for (int v = 0; v < NWAVES; ++v) {
+    const int a = sm.wsum[0][v], e = sm.wsum[1][v];
+    ps += v < wave ? a : 0;
+    pe += v < wave ? e : 0;
+    ts += a;
+    te += e;
+  }
+  int rs = ns + ps, re = pe;  // slots before this thread's run
+  if (__ballot(ce != 0) == 0) {
+    // no tie in the wave's words: this thread's kept competitors take consecutive slots
+    int o = rs + (re < neq ? re : neq);
+#pragma unroll
+    for (int e = 0; e < kWordsPer; ++e) {
+      const int j0 = ns + ((wb + e) << 5);
+      unsigned bits = sw[e];
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1;
+        if (o < b) out[o] = j0 + bit;
+        ++o;
       }
-      ts += sm.wsum[0][v];
-      te += sm.wsum[1][v];
     }
-    int64_t rs = sure_base + ps, re = eq_base + pe;
-    unsigned bits = sw | tw;
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      bits &= bits - 1;
-      const int32_t j = (int32_t)(ns + (w << 5) + bit);
-      if ((sw >> bit) & 1u) {
-        const int64_t pos = ns + rs + (re < need_eq ? re : need_eq);
-        if (pos < b) out[pos] = j;
-        ++rs;
-      } else {
-        if (re < need_eq && ns + rs + re < b) out[ns + rs + re] = j;
-        ++re;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kWordsPer; ++e) {
+      const int j0 = ns + ((wb + e) << 5);
+      unsigned bits = sw[e] | tw[e];
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1;
+        const bool sb = (sw[e] >> bit) & 1u;
+        const int o = rs + (sb ? (re < neq ? re : neq) : re);
+        if ((sb || re < neq) && o < b) out[o] = j0 + bit;
+        rs += sb ? 1 : 0;
+        re += sb ? 0 : 1;
       }
     }
-    sure_base += ts;
-    eq_base += te;
-    __syncthreads();  // wsum is rewritten next round
   }
   // the window after the selected competitors
-  const int64_t kept_c = sure_base + (eq_base < need_eq ? eq_base : need_eq);
-  for (int64_t i = tid; i < n - cand; i += NT) {
-    const int64_t pos = ns + kept_c + i;
-    if (pos < b) out[pos] = (int32_t)(cand + i);
+  const int kept_c = ts + (te < neq ? te : neq);
+  for (int i = tid; i < n - cand; i += NT) {
+    const int pos = ns + kept_c + i;
+    if (pos < b) out[pos] = cand + i;
   }
 }
 
 __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict__ score, int n_sink,
                                                  const int64_t* __restrict__ seg_off, int32_t* __restrict__ kept) {
   __shared__ SelectSmem sm;
-  int x_, y_, u;
-  xcd_item(p.S, p.Hkv, 1, 1, gridDim.x, blockIdx.x, x_, y_, u);
-  int l, s, g;
-  unit_coords(p, u, l, s, g);
+  // longest units first: workgroup w takes the w-th unit in order of decreasing sequence
+  // length (ties by sequence), then layer and head. Workgroups are dealt round-robin to the
+  // dispatch queues, so every queue gets its share of each length, longest first, and the
+  // short units fill in behind the long ones.
+  const int per_seq = p.L * p.Hkv, rank = blockIdx.x / per_seq, within = blockIdx.x % per_seq;
+  if (threadIdx.x < p.S) {
+    const int me = threadIdx.x;
+    const int64_t nme = p.cu[me + 1] - p.cu[me];
+    int r = 0;
+    for (int o = 0; o < p.S; ++o) {
+      const int64_t no = p.cu[o + 1] - p.cu[o];
+      r += (no > nme || (no == nme && o < me)) ? 1 : 0;
+    }
+    if (r == rank) sm.s_digit[0] = (unsigned)me;
+  }
+  __syncthreads();
+  const int s = (int)sm.s_digit[0], l = within / p.Hkv, g = within % p.Hkv;
+  const int u = (l * p.S + s) * p.Hkv + g;
+  __syncthreads();  // s_digit is rewritten by the select
   const int64_t n = p.cu[s + 1] - p.cu[s];
   const int64_t cand = n - p.W;
   const int64_t ns = n_sink < cand ? n_sink : cand;  // pinned sinks [0, ns); competitors [ns, cand)
@@ -672,14 +751,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
     // thread tid takes float4s tid + NT r, four rounds r per step, the next step's issued
     // before this one is counted (eight in flight per thread, 128 KB per workgroup); two
     // buffers with fixed roles and two steps per trip (a register rotation would make the
-    // compiler wait for the next step's loads at the copy). prime() issues the first step's
-    // loads ahead of the next read.
+    // compiler wait for the next step's loads at the copy).
     // competitor indices fit 32 bits (kept positions are int32)
     constexpr int V = 4;
     const int mc = (int)m;
     const int m4 = ((((size_t)c0) & 15) == 0 && mc >= 4) ? mc >> 2 : 0;  // competitors read as float4s
-    float4 A[V], B[V];
-    bool primed = false;
     // loads past the row repeat its last float4 (no branch around a load, so the next step's
     // loads need not wait for this one's)
     auto ld = [&](float4* buf, int r0) __attribute__((always_inline)) {
@@ -687,12 +763,6 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
       for (int i = 0; i < V; ++i) {
         const int fi = tid + NT * (r0 + i);
         buf[i] = *(const float4*)(c0 + 4 * (fi < m4 ? fi : m4 - 1));
-      }
-    };
-    auto prime = [&]() __attribute__((always_inline)) {
-      if (m4 > 0) {
-        ld(A, 0);
-        primed = true;
       }
     };
     auto visit = [&](auto f) {
@@ -711,8 +781,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
       };
       if (m4 > 0) {
         const int nr = (m4 + NT - 1) / NT;  // rounds
-        if (!primed) ld(A, 0);
-        primed = false;
+        float4 A[V], B[V];
+        ld(A, 0);
         for (int r = 0; r < nr; r += 2 * V) {
           ld(B, r + V);
           run(A, r);
@@ -726,7 +796,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(Dev p, const float* __restrict
     const float q = (float)k / (float)m;
     const float band = 2.f * (4.f * sqrtf(4.f * NT * q * (1.f - q)) + 16.f) * (float)m / (4.f * NT);
     if (m <= kBitCap && (m <= kCandCap || band <= 0.85f * kCandCap)) {
-      if (band_select(sm, hs, cs, visit, prime, c0, m, k, sure, tie, T, need_eq)) listed = true;
+      if (band_select(sm, hs, cs, visit, c0, m, k, sure, tie, T, need_eq)) listed = true;
     }
     if (!listed) radix_select(sm, hs, visit, k, T, need_eq, &cs, m <= kBitCap ? sure : nullptr, listed);
     if (listed && m <= kBitCap) {
