@@ -9,8 +9,9 @@ thread of the workgroup, 4096 keys) gives a band of keys around the threshold's 
 rank; one read marks the keys above the band and lists the band's keys in LDS, and the
 threshold is found in that list. A unit with at most 11264 competitors lists them all. When
 the band missed the threshold or overflowed the list (all keys equal; a periodic pattern
-whose high half the sample never sees; a band wider than the list), the unit is selected
-from scratch by the radix select below, so the sample never changes the result.
+whose high half the sample never sees; the band's keys all in one wave's share of the read,
+overflowing that wave's list region), the unit is selected from scratch by the radix select
+below, so the sample never changes the result.
 
 The score distributions steer the radix select down its routes: when at most 11264 keys
 share the threshold's top 14 bits, the second pass lists them (key and position) in LDS and
@@ -53,10 +54,20 @@ def _scores(kind, n, rng):
     if kind == "periodic":  # high scores in the second half of every 128 positions, low in the first
         j = np.arange(n)
         return np.where(j % 128 >= 64, rng.uniform(4.0, 8.0, n), rng.uniform(0.0, 1.0, n)).astype(np.float32)
+    if kind == "one_wave_band":
+        # the scores near the threshold all sit where one wave of the read takes its float4s
+        # (float4 index mod 1024 below 64); 4000 high scores elsewhere, the rest low
+        j = np.arange(n)
+        mine = ((j // 4) % 1024) < 64
+        x = rng.uniform(0.0, 1.0, n)
+        x[rng.choice(np.flatnonzero(~mine), 4000, replace=False)] = rng.uniform(8.0, 9.0, 4000)
+        x[mine] = rng.uniform(2.0, 2.001, int(mine.sum()))
+        return x.astype(np.float32)
     raise ValueError(kind)
 
 
-KINDS = ["log_uniform", "one_top_byte", "sixteen_values", "all_equal", "ties_in_list", "narrow", "periodic"]
+KINDS = ["log_uniform", "one_top_byte", "sixteen_values", "all_equal", "ties_in_list", "narrow", "periodic",
+         "one_wave_band"]
 
 
 @pytest.mark.parametrize("budget_extra,n_sink,n", [(5000, 0, 60011), (0, 0, 60011), (70000, 0, 60011),
