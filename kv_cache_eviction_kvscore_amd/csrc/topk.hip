@@ -12,22 +12,26 @@
 // pool_kernel (pool > 1): grid (4096-token tile, unit); the tile and its halo are loaded
 // into LDS (-inf outside the prefix) and every token takes the maximum of its window.
 //
-// topk_kernel: one 1024-thread workgroup per (layer, sequence, KV head) unit. Radix
-// select of the k-th largest key over order-preserving uint32 images of the fp32 scores
-// in three passes of 14, 9 and 9 bits, each counted into one shared LDS histogram (a
-// wave whose counted lanes share a bin adds their number with one atomic); the digit is
-// found by a two-level scan (each thread sums its run of bins, a block scan over the
-// threads' totals finds the thread where the count from the top reaches k). This gives
-// the threshold T and how many elements equal to T are taken. When the threshold's
-// 14-bit bin holds few enough keys, the second pass also lists them (key and competitor
-// index) in LDS and sets a bit in an LDS bitmask for every competitor above that bin; the
-// last pass counts over the list, the listed keys are then marked against T (a "surely
-// kept" bit above it, a "tied" bit equal to it), and the kept positions are written from
-// the bitmasks: the scores are read twice. Each thread takes a 32-bit word of each
-// bitmask per round, block scans of the words' counts give its slots, ties are taken by
-// ascending position. Otherwise (a bin too full for the list, or more competitors than
-// the bitmasks hold) an ordered stream compaction over the scores in rounds of 4096
-// positions does the same from ballots within a wave and LDS sums across waves.
+// topk_kernel: one 1024-thread workgroup per (layer, sequence, KV head) unit, longest
+// sequences first. Keys are order-preserving uint32 images of the fp32 scores. The common
+// case reads the scores once: a strided sample (a 4-key run per thread) locates a band
+// [lo, hi] of keys around the threshold's expected rank; one read sets a bit in an LDS
+// bitmask for every competitor above the band ("surely kept") and lists the band's keys
+// (key and competitor index) in per-wave LDS regions; if the band held the k-th largest
+// key and the regions did not overflow, that key (the threshold T) and the number of keys
+// equal to it that are taken follow from an exact select over the list in LDS. Otherwise
+// (and for units with more competitors than the bitmasks hold) a radix select in three
+// passes of 14, 9 and 9 bits finds them, each pass counted into one shared LDS histogram
+// (a wave whose counted lanes share a bin adds their number with one atomic); the digit
+// is found by a two-level scan (each thread sums its run of bins, a block scan over the
+// threads' totals finds the thread where the count from the top reaches k). When the
+// threshold's 14-bit bin holds few enough keys, that route's second pass also lists them
+// and marks every competitor above the bin, and its last pass counts over the list. The
+// listed keys are then marked against T (a "surely kept" bit above it, a "tied" bit equal
+// to it) and the kept positions written from the bitmasks: each thread takes a run of
+// words, a block scan of their counts gives its slots, ties are taken by ascending
+// position. Without the bitmasks an ordered stream compaction over the scores in rounds of
+// 4096 positions does the same from ballots within a wave and LDS sums across waves.
 //
 // heads_*_kernel (head budgets chosen jointly over a layer's KV heads) run a select of
 // their own, spread over many workgroups: four passes of 8 bits, one 256-bin histogram
