@@ -73,11 +73,13 @@ KINDS = ["log_uniform", "one_top_byte", "sixteen_values", "all_equal", "ties_in_
 @pytest.mark.parametrize("budget_extra,n_sink,n", [(5000, 0, 60011), (0, 0, 60011), (70000, 0, 60011),
                                                     (5000, 5, 60011), (5000, 37, 60011), (20000, 3, 300007),
                                                     (5000, 0, 131088), (70000, 0, 131088), (500, 0, 9000),
-                                                    (6000, 2, 9000), (3000, 0, 11280), (3000, 0, 11281)])
+                                                    (6000, 2, 9000), (3000, 0, 11280), (3000, 0, 11281),
+                                                    (5000, 0, 253968)])
 def test_topk_threshold_bins_both_routes(budget_extra, n_sink, n):
     # n = 60011 is ragged against the 4-key loads; 300007 - W competitors exceed the bitmasks;
     # 131088 - W = 2^17 competitors put every sampled run in the low half of the periodic
-    # scores; 11280 - W competitors fit the LDS list whole, 11281 - W do not
+    # scores; 11280 - W competitors fit the LDS list whole, 11281 - W do not; 253968 - W fill
+    # the bitmasks exactly (eight words per thread in the emission)
     L, S, Hkv, Hq, d, W = 1, 1, len(KINDS), len(KINDS), 128, 16
     rng = np.random.default_rng(budget_extra + 5 + n_sink)
     p = api.Problem(num_seqs=S, num_layers=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, window=W,
