@@ -137,18 +137,20 @@ struct HistSmem {
   int tsum[NWAVES];
 };
 
-// LDS list of the keys that share the threshold's top 14 bits and their competitor indices
-// (filled during the second pass), so that neither the last radix pass nor the emission
-// reads global memory again
+// LDS list of candidate keys and their competitor indices: the sampled band's keys (the
+// one-read select), or the keys that share the threshold's top 14 bits (filled by the radix
+// select's second pass), so that neither the final select nor the emission reads global
+// memory again
 constexpr int kCandCap = 11264;
 struct CandSmem {
   unsigned key[kCandCap];
   unsigned pos[kCandCap];
   unsigned n;
 };
-// After the first pass only the first 2^9 words of the histogram are counted into; the rest
-// holds two bitmasks over the competitors (bit c: competitor c), "surely kept" and "tied",
-// so the emission reads no score. Units with more competitors read the scores a third time.
+// Once the 14-bit counts are no longer needed only the first 2^9 words of the histogram are
+// counted into; the rest holds two bitmasks over the competitors (bit c: competitor c),
+// "surely kept" and "tied", so the emission reads no score. Units with more competitors
+// take the radix select and an emission that reads the scores again.
 constexpr int kBitBase = 1 << kBits12;
 constexpr int kBitWords = ((1 << kBits0) - kBitBase) / 2;  // words per bitmask
 constexpr int64_t kBitCap = (int64_t)kBitWords * 32;       // competitors the bitmasks cover
