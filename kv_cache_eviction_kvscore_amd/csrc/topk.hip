@@ -834,8 +834,11 @@ struct HeadsState {  // per group
   long long kr;       // rank still to place inside the current prefix
   long long need_eq;  // keys equal to T taken (after the last pass)
   unsigned prefix;    // T after the last pass
-  int sel;            // 0: no competitor kept, 1: all, 2: radix select
+  int sel;            // 0: no competitor kept, 1: all, 2: select
   int ns;             // sinks of the group's sequence
+  int band;           // sampled band: 0 none (radix passes), 1 set, 2 T found in it
+  unsigned lo, hi;    // the band's keys
+  unsigned list_n;    // band keys listed (may exceed the list)
   int pad;
 };
 
@@ -864,8 +867,252 @@ __global__ __launch_bounds__(64) void heads_init_kernel(Dev p, int n_sink, const
   x.prefix = 0;
   x.sel = (kt == 0) ? 0 : (kt == (int64_t)p.Hkv * M ? 1 : 2);
   x.ns = (int)ns;
+  x.band = 0;
+  x.lo = 0;
+  x.hi = 0;
+  x.list_n = 0;
   x.pad = 0;
   st[grp] = x;
+}
+
+// The joint select in one read when a sample allows, as the per-unit select does: a
+// strided sample over the group's heads (four 4-key runs per thread, the heads taking runs
+// in turn) sets a band [lo, hi] around the threshold's expected rank (heads_band_kernel,
+// one workgroup per group); every chunk counts its keys above the band and appends the
+// band's keys to the group's list in global memory, one slot reservation per workgroup
+// (heads_pass_kernel, which also writes each chunk's "above the band" bitmask); if the band
+// held the threshold and the list did not overflow, heads_bsel_kernel finds T and need_eq
+// in the list (its order, set by the reservations, does not matter: only counts do) and
+// each head's counts above and at T, and the radix passes and the count pass skip the
+// group; the emission then builds each head's bitmasks from the chunk bitmasks and the
+// list, and reads no score. Otherwise the radix passes run.
+constexpr int kHeadsRuns = 4;             // sampled 4-key runs per thread
+constexpr int kGroupListCap = 32768;      // band keys a group may list
+constexpr int kMaxBandHeads = 64;         // KV heads a band select handles
+constexpr int kHeadShift = 18;            // list position: head << 18 | competitor index
+static_assert(HCH % NWAVES == 0 && HCH % 32 == 0, "chunk split over the waves and words");
+static_assert(kBitCap <= (1 << kHeadShift), "competitor index fits below the head");
+
+__global__ __launch_bounds__(NT) void heads_band_kernel(Dev p, const float* __restrict__ score,
+                                                        HeadsState* __restrict__ st) {
+  __shared__ SelectSmem sm;
+  __shared__ HistSmem hs;
+  const int grp = blockIdx.x, tid = threadIdx.x;
+  HeadsState x = st[grp];
+  if (x.sel != 2) return;  // uniform
+  int l, s;
+  group_of(p, grp, l, s);
+  const int64_t M = p.cu[s + 1] - p.cu[s] - p.W - x.ns;
+  const int Hkv = p.Hkv;
+  const int per_head = NT * kHeadsRuns / Hkv;  // runs per head
+  const int runs = per_head * Hkv;
+  const int64_t tot = (int64_t)Hkv * M;
+  const float MS = 4.f * (float)runs;  // sampled keys
+  const float q = (float)x.kr / (float)tot;
+  const float band = 2.f * (4.f * sqrtf(MS * q * (1.f - q)) + 16.f) * (float)tot / MS;
+  if ((M >> 2) < per_head || M > kBitCap || Hkv > kMaxBandHeads || band > 0.85f * kGroupListCap)
+    return;  // uniform: radix passes
+  unsigned xk[kHeadsRuns][4];
+  bool ok[kHeadsRuns];
+#pragma unroll
+  for (int i = 0; i < kHeadsRuns; ++i) {
+    const int r = tid + NT * i;
+    ok[i] = r < runs;
+    const int h = ok[i] ? r % Hkv : 0, ri = ok[i] ? r / Hkv : 0;
+    const int64_t j = (int64_t)ri * (M >> 2) / per_head * 4;  // <= M - 4
+    const float* c0 = score + (int64_t)(l * Hkv + h) * p.N + p.cu[s] + x.ns + j;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xk[i][e] = f2key(c0[e]);
+  }
+  const float rho = (float)x.kr * MS / (float)tot;
+  const float half = 4.f * sqrtf(rho * (1.f - rho / MS)) + 16.f;
+  const int64_t nms = (int64_t)MS;
+  const int64_t rh = (int64_t)floorf(rho - half), rl = (int64_t)ceilf(rho + half);
+  const int64_t r0 = rh < 1 ? 1 : (rh > nms ? nms : rh), r1 = rl < 1 ? 1 : (rl > nms ? nms : rl);
+  constexpr int sh0 = 32 - kBits0, sh1 = sh0 - kBits12;
+  for (int i = tid; i < (1 << kBits0); i += NT) hs.hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kHeadsRuns; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hist_add(hs.hist, ok[i], xk[i][e] >> sh0);
+  __syncthreads();
+  const int64_t rr[2] = {r0, r1};
+  scan_digit<kPer0, 2>(sm, hs, hs.hist, 1 << kBits0, rr);
+  const unsigned d0 = sm.s_digit[0], d1 = sm.s_digit[1];
+  const int64_t qq[2] = {r0 - sm.s_above[0], r1 - sm.s_above[1] + (d0 != d1 ? sm.s_count[0] : 0u)};
+  for (int i = tid; i < 2 << kBits12; i += NT) hs.hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kHeadsRuns; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned top = xk[i][e] >> sh0;
+      const unsigned dg = ((xk[i][e] >> sh1) & ((1u << kBits12) - 1u)) | (top == d0 ? 1u << kBits12 : 0u);
+      hist_add(hs.hist, ok[i] && (top == d0 || top == d1), dg);
+    }
+  __syncthreads();
+  scan_digit<1, 2>(sm, hs, hs.hist, 2 << kBits12, qq);
+  const unsigned e0 = sm.s_digit[0] & ((1u << kBits12) - 1u), e1 = sm.s_digit[1] & ((1u << kBits12) - 1u);
+  if (tid == 0) {
+    x.hi = rh >= 1 ? (d0 << sh0) | (e0 << sh1) | ((1u << sh1) - 1u) : ~0u;
+    x.lo = rl <= nms ? (d1 << sh0) | (e1 << sh1) : 0u;
+    x.band = 1;
+    x.list_n = 0;
+    st[grp] = x;
+  }
+}
+
+// per chunk of one head: the keys above the band (counted, and marked in the chunk's
+// bitmask) and in it (listed with head and competitor index); each wave lists into its own
+// LDS region (a wave visits at most HCH / NWAVES keys), then one reservation in the group's
+// list
+__global__ __launch_bounds__(NT) void heads_pass_kernel(Dev p, const float* __restrict__ score,
+                                                        HeadsState* __restrict__ st, int nch,
+                                                        unsigned* __restrict__ above_cnt,
+                                                        unsigned* __restrict__ gsure, unsigned* __restrict__ gkey,
+                                                        unsigned* __restrict__ ghp) {
+  constexpr int WR = HCH / NWAVES;
+  __shared__ unsigned wl[NWAVES][WR], wp[NWAVES][WR];
+  __shared__ unsigned bits[HCH / 32];
+  __shared__ unsigned wn[NWAVES], wa[NWAVES];
+  __shared__ unsigned s_base;
+  const int u = blockIdx.y, c = blockIdx.x;
+  const int grp = u / p.Hkv, g = u % p.Hkv;
+  const HeadsState x = st[grp];
+  if (x.sel != 2 || x.band != 1) return;  // uniform
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int l, s;
+  group_of(p, grp, l, s);
+  const int64_t cand = p.cu[s + 1] - p.cu[s] - p.W;
+  const int64_t j0 = x.ns + (int64_t)c * HCH;
+  const int64_t j1 = (j0 + HCH < cand) ? j0 + HCH : cand;
+  const float* sc = score + (int64_t)(l * p.Hkv + g) * p.N + p.cu[s];
+  for (int i = tid; i < HCH / 32; i += NT) bits[i] = 0;
+  __syncthreads();
+  unsigned above = 0, n_w = 0;  // n_w: this wave's listed keys (uniform)
+  // key at j0 + r (r < HCH), if in range
+  auto visit = [&](float v, int r, bool in_range) __attribute__((always_inline)) {
+    const unsigned key = f2key(v);
+    if (in_range && key > x.hi) {
+      ++above;
+      atomicOr(&bits[r >> 5], 1u << (r & 31));
+    }
+    const bool in = in_range && key >= x.lo && key <= x.hi;
+    const unsigned long long msk = __ballot(in);
+    if (in) {
+      const unsigned slot =
+          n_w + __builtin_amdgcn_mbcnt_hi((unsigned)(msk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)msk, 0u));
+      wl[wave][slot] = key;
+      wp[wave][slot] = (unsigned)(j0 - x.ns) + (unsigned)r;
+    }
+    n_w += (unsigned)__popcll(msk);
+  };
+  static_assert(HCH == 8 * NT, "eight keys per thread");
+  if (j1 - j0 == HCH && (((size_t)(sc + j0)) & 15) == 0) {  // a whole aligned chunk: 16-byte loads
+    const int r = 8 * tid;
+    const float4 a = *(const float4*)(sc + j0 + r), b = *(const float4*)(sc + j0 + r + 4);
+    visit(a.x, r, true);
+    visit(a.y, r + 1, true);
+    visit(a.z, r + 2, true);
+    visit(a.w, r + 3, true);
+    visit(b.x, r + 4, true);
+    visit(b.y, r + 5, true);
+    visit(b.z, r + 6, true);
+    visit(b.w, r + 7, true);
+  } else {  // whole waves, at most HCH / NT keys per thread
+    for (int rb = 0; j0 + rb < j1; rb += NT) {
+      const int r = rb + tid;
+      const bool ok = j0 + r < j1;
+      visit(ok ? sc[j0 + r] : 0.f, r, ok);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) above += __shfl_xor(above, o, 64);
+  if (lane == 0) {
+    wa[wave] = above;
+    wn[wave] = n_w;
+  }
+  __syncthreads();
+  // the chunk's bitmask (zeros for a chunk past the head's competitors)
+  for (int i = tid; i < HCH / 32; i += NT) gsure[((int64_t)u * nch + c) * (HCH / 32) + i] = bits[i];
+  if (tid == 0) {
+    unsigned ta = 0, tn = 0;
+    for (int w = 0; w < NWAVES; ++w) {
+      ta += wa[w];
+      tn += wn[w];
+    }
+    above_cnt[(int64_t)u * nch + c] = ta;
+    s_base = tn ? atomicAdd(&st[grp].list_n, tn) : 0u;
+  }
+  __syncthreads();
+  unsigned before = s_base;
+  for (int w = 0; w < wave; ++w) before += wn[w];
+  for (unsigned i = lane; i < wn[wave]; i += 64) {
+    const unsigned pos = before + i;
+    if (pos < (unsigned)kGroupListCap) {
+      gkey[(int64_t)grp * kGroupListCap + pos] = wl[wave][i];
+      ghp[(int64_t)grp * kGroupListCap + pos] = ((unsigned)g << kHeadShift) | wp[wave][i];
+    }
+  }
+}
+
+// per group: did the band hold T? Then T and need_eq from the listed keys, and each head's
+// counts above T and at T (into the count pass's slots: chunk 0 of the head, the others 0)
+__global__ __launch_bounds__(NT) void heads_bsel_kernel(Dev p, HeadsState* __restrict__ st, int nch,
+                                                        const unsigned* __restrict__ above_cnt,
+                                                        const unsigned* __restrict__ gkey,
+                                                        const unsigned* __restrict__ ghp, unsigned* __restrict__ cnt) {
+  __shared__ SelectSmem sm;
+  __shared__ HistSmem hs;
+  __shared__ unsigned hc[3][kMaxBandHeads];  // per head: above the band, above T, at T
+  const int grp = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  HeadsState x = st[grp];
+  if (x.sel != 2 || x.band != 1) return;  // uniform
+  const int Hkv = p.Hkv, nc = Hkv * nch;
+  for (int i = tid; i < 3 * kMaxBandHeads; i += NT) (&hc[0][0])[i] = 0;
+  __syncthreads();
+  unsigned a = 0;
+  for (int i = tid; i < nc; i += NT) {
+    const unsigned v = above_cnt[(int64_t)grp * nc + i];
+    a += v;
+    if (v) atomicAdd(&hc[0][i / nch], v);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
+  if (lane == 0) sm.wsum[0][wave] = (int)a;
+  __syncthreads();
+  int64_t A = 0;
+  for (int w = 0; w < NWAVES; ++w) A += (unsigned)sm.wsum[0][w];
+  const int64_t L = x.list_n;
+  if (L > kGroupListCap || A >= x.kr || x.kr > A + L) {  // uniform: the radix passes run
+    if (tid == 0) st[grp].band = 0;
+    return;
+  }
+  const unsigned* lk = gkey + (int64_t)grp * kGroupListCap;
+  const unsigned* lh = ghp + (int64_t)grp * kGroupListCap;
+  const unsigned dif = x.lo ^ x.hi;
+  const int hb = dif ? 32 - __clz((int)dif) : 0;
+  unsigned T;
+  int64_t need_eq;
+  list_select(sm, hs, lk, (int)L, x.kr - A, hb >= 32 ? 0u : x.lo & (~0u << hb), hb, T, need_eq);
+  for (int i = tid; i < (int)L; i += NT) {
+    const unsigned key = lk[i], h = lh[i] >> kHeadShift;
+    if (key > T) atomicAdd(&hc[1][h], 1u);
+    else if (key == T) atomicAdd(&hc[2][h], 1u);
+  }
+  __syncthreads();
+  for (int i = tid; i < nc; i += NT) {
+    const int h = i / nch, c = i % nch;
+    cnt[((int64_t)grp * nc + i) * 2] = c == 0 ? hc[0][h] + hc[1][h] : 0u;
+    cnt[((int64_t)grp * nc + i) * 2 + 1] = c == 0 ? hc[2][h] : 0u;
+  }
+  if (tid == 0) {
+    x.prefix = T;
+    x.need_eq = need_eq;
+    x.band = 2;
+    st[grp] = x;
+  }
 }
 
 // pass `pass` of the select: histogram of the 8-bit digit of the keys of one chunk of one
@@ -879,7 +1126,7 @@ __global__ __launch_bounds__(NT) void heads_hist_kernel(Dev p, const float* __re
   const HeadsState x = st[grp];
   unsigned* out = whist + ((int64_t)u * nch + c) * 256;
   const int tid = threadIdx.x, wave = tid >> 6;
-  if (x.sel != 2) return;  // uniform
+  if (x.sel != 2 || x.band == 2) return;  // uniform
   int l, s;
   group_of(p, grp, l, s);
   const int64_t cand = p.cu[s + 1] - p.cu[s] - p.W;
@@ -927,7 +1174,7 @@ __global__ __launch_bounds__(1024) void heads_digit_kernel(Dev p, HeadsState* __
   __shared__ long long s_above;
   const int grp = blockIdx.x;
   HeadsState x = st[grp];
-  if (x.sel != 2) return;  // uniform
+  if (x.sel != 2 || x.band == 2) return;  // uniform
   // bin b of histogram i (i = head * nch + chunk) is summed by the threads b + 256q for
   // q = i % 4; integer counts, so the order of the sums does not matter
   const int t = threadIdx.x & 255, q = threadIdx.x >> 8;
@@ -987,7 +1234,7 @@ __global__ __launch_bounds__(NT) void heads_count_kernel(Dev p, const float* __r
   const int u = blockIdx.y, c = blockIdx.x;
   const int grp = u / p.Hkv, g = u % p.Hkv;
   const HeadsState x = st[grp];
-  if (x.sel != 2) return;  // uniform
+  if (x.sel != 2 || x.band == 2) return;  // uniform (a band select wrote the counts)
   int l, s;
   group_of(p, grp, l, s);
   const int64_t cand = p.cu[s + 1] - p.cu[s] - p.W;
@@ -1028,8 +1275,12 @@ __global__ __launch_bounds__(NT) void heads_emit_kernel(Dev p, const float* __re
                                                         const HeadsState* __restrict__ st, int nch,
                                                         const unsigned* __restrict__ cnt,
                                                         const int64_t* __restrict__ seg_off,
-                                                        int64_t* __restrict__ head_off, int32_t* __restrict__ kept) {
+                                                        int64_t* __restrict__ head_off, int32_t* __restrict__ kept,
+                                                        const unsigned* __restrict__ gsure,
+                                                        const unsigned* __restrict__ gkey,
+                                                        const unsigned* __restrict__ ghp) {
   __shared__ SelectSmem sm;
+  __shared__ unsigned bm[2 * kBitWords];
   const int u = blockIdx.x;
   const int grp = u / p.Hkv, g = u % p.Hkv;
   const HeadsState x = st[grp];
@@ -1065,6 +1316,30 @@ __global__ __launch_bounds__(NT) void heads_emit_kernel(Dev p, const float* __re
     head_off[u] = off;
     if (u == p.U - 1) head_off[p.U] = off + bg;
   }
+  if (x.sel == 2 && x.band == 2) {
+    // the head's bitmasks: its chunks' "above the band" words, then its listed keys against T
+    const int tid = threadIdx.x;
+    unsigned* sure = bm;
+    unsigned* tie = bm + kBitWords;
+    const int nw = (int)((M + 31) >> 5);  // M <= kBitCap
+    for (int i = tid; i < nw; i += NT) {
+      sure[i] = gsure[(int64_t)u * nch * (HCH / 32) + i];
+      tie[i] = 0;
+    }
+    __syncthreads();
+    const unsigned* lk = gkey + (int64_t)grp * kGroupListCap;
+    const unsigned* lh = ghp + (int64_t)grp * kGroupListCap;
+    for (int i = tid; i < (int)x.list_n; i += NT) {
+      const unsigned hp = lh[i];
+      if ((int)(hp >> kHeadShift) != g) continue;
+      const unsigned key = lk[i], c = hp & ((1u << kHeadShift) - 1u);
+      if (key > x.prefix) atomicOr(&sure[c >> 5], 1u << (c & 31));
+      else if (key == x.prefix) atomicOr(&tie[c >> 5], 1u << (c & 31));
+    }
+    __syncthreads();
+    emit_words(sm, kept + off, bg, take, sure, tie, n, cand, ns);
+    return;
+  }
   const float* sc = score + (int64_t)(l * p.Hkv + g) * p.N + p.cu[s];
   emit_segment(sm, kept + off, bg, x.sel, x.prefix, take, sc, n, cand, ns);
 }
@@ -1083,13 +1358,23 @@ hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off,
     hipLaunchKernelGGL(topk_kernel, dim3(p.U), dim3(NT), 0, st, p, key, n_sink, seg_off, kept);
     return hipGetLastError();
   }
-  // head budgets chosen jointly; scratch: states | chunk histograms | chunk counts
+  // head budgets chosen jointly; scratch: states | chunk histograms | chunk counts | chunk
+  // counts above the band | chunk bitmasks above the band | the groups' band lists (keys,
+  // then head and competitor index)
   const int groups = p.U / p.Hkv;
   const int nch = heads_chunks(p);
   HeadsState* hs = (HeadsState*)heads_ws;
   unsigned* whist = (unsigned*)((char*)heads_ws + heads_state_bytes(p));
   unsigned* cnt = whist + (size_t)p.U * nch * 256;
+  unsigned* above = cnt + (size_t)p.U * nch * 2;
+  unsigned* gsure = above + (size_t)p.U * nch;
+  unsigned* gkey = gsure + (size_t)p.U * nch * (HCH / 32);
+  unsigned* ghp = gkey + (size_t)groups * kGroupListCap;
   hipLaunchKernelGGL(heads_init_kernel, dim3(groups), dim3(64), 0, st, p, n_sink, seg_off, hs);
+  hipLaunchKernelGGL(heads_band_kernel, dim3(groups), dim3(NT), 0, st, p, key, hs);
+  hipLaunchKernelGGL(heads_pass_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, hs, nch, above, gsure, gkey, ghp);
+  hipLaunchKernelGGL(heads_bsel_kernel, dim3(groups), dim3(NT), 0, st, p, hs, nch, (const unsigned*)above,
+                     (const unsigned*)gkey, (const unsigned*)ghp, cnt);
   for (int pass = 0; pass < 4; ++pass) {
     hipLaunchKernelGGL(heads_hist_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, pass, nch,
                        whist);
@@ -1097,7 +1382,8 @@ hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off,
   }
   hipLaunchKernelGGL(heads_count_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, nch, cnt);
   hipLaunchKernelGGL(heads_emit_kernel, dim3(p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, nch,
-                     (const unsigned*)cnt, seg_off, head_off, kept);
+                     (const unsigned*)cnt, seg_off, head_off, kept, (const unsigned*)gsure, (const unsigned*)gkey,
+                     (const unsigned*)ghp);
   return hipGetLastError();
 }
 
@@ -1105,7 +1391,8 @@ int heads_chunks(const Dev& p) { return (int)((p.max_n - p.W + HCH - 1) / HCH); 
 size_t heads_state_bytes(const Dev& p) { return ((size_t)(p.U / p.Hkv) * sizeof(HeadsState) + 255) / 256 * 256; }
 size_t heads_ws_bytes(const Dev& p) {
   const size_t nch = (size_t)heads_chunks(p);
-  return heads_state_bytes(p) + ((size_t)p.U * nch * 256 * 4 + (size_t)p.U * nch * 2 * 4 + 255) / 256 * 256;
+  return heads_state_bytes(p) + ((size_t)p.U * nch * (256 + 2 + 1 + HCH / 32) * 4 +
+                                 (size_t)(p.U / p.Hkv) * kGroupListCap * 2 * 4 + 255) / 256 * 256;
 }
 
 }  // namespace kvs

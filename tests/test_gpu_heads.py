@@ -111,3 +111,57 @@ def test_heads_full_size_own_scores():
     run = run_gpu(w, heads=True)
     for l in (0, 31):
         _check_group(w, run, l, 0, with_oracle=False)
+
+
+def _hand_scores(kind, n, rng):
+    j = np.arange(n)
+    if kind == "all_equal":
+        return np.full(n, 3.0, dtype=np.float32)
+    if kind == "high":
+        return rng.uniform(4.0, 8.0, n).astype(np.float32)
+    if kind == "low":
+        return rng.uniform(0.0, 1.0, n).astype(np.float32)
+    if kind == "log_uniform":
+        return np.exp2(rng.uniform(-60.0, 0.0, n)).astype(np.float32)
+    if kind == "periodic":  # high in the second half of every 128 positions
+        return np.where(j % 128 >= 64, rng.uniform(4.0, 8.0, n), rng.uniform(0.0, 1.0, n)).astype(np.float32)
+    raise ValueError(kind)
+
+
+# Most groups are selected in one read: a strided sample over the group's heads sets a band
+# around the joint threshold, the chunks count the keys above it and list the keys in it,
+# and the threshold is found in that list; when the band misses the threshold or the list
+# overflows, the radix passes run instead. These score sets steer both ways: heads on
+# different scales (the band held), every key equal (the band holds everything: overflow),
+# and a periodic pattern whose high half falls between the sampled runs of 2^17 competitors
+# (the band misses).
+@pytest.mark.parametrize("kinds,n,extra", [
+    (("high", "low", "log_uniform", "periodic"), 60011, 9000),
+    (("all_equal", "all_equal", "all_equal", "all_equal"), 60011, 9000),
+    (("periodic", "periodic", "periodic", "periodic"), 131088, 20000),
+    (("low", "high", "periodic", "log_uniform"), 131088, 50000),
+])
+def test_heads_hand_made_scores(kinds, n, extra):
+    import torch
+    from kv_cache_eviction_kvscore_amd import api
+    L, S, Hkv, Hq, d, W = 1, 1, len(kinds), len(kinds), 128, 16
+    rng = np.random.default_rng(n + extra)
+    p = api.Problem(num_seqs=S, num_layers=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, window=W,
+                    cu_seqlens=[0, n], k_strides=(Hkv * n * d, n * d, d), v_strides=(Hkv * n * d, n * d, d))
+    sc = np.stack([_hand_scores(kind, n, rng) for kind in kinds])  # [Hkv][n]
+    b = min(W + extra, n)
+    budgets = np.full((S, L), b, dtype=np.int32)
+    off = api.segment_offsets(p, budgets)
+    kept = torch.full((int(off[-1]),), -7, dtype=torch.int32, device="cuda")
+    head_off = torch.zeros(p.units + 1, dtype=torch.int64, device="cuda")
+    nb = p.workspace_size(api.WS_TOPK_HEADS) - p.workspace_size(api.WS_TOPK)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    say(f"joint head select on hand-made scores: n={n}, budget {b}, kinds {kinds}")
+    api.topk_heads(p, torch.from_numpy(sc.reshape(-1)).cuda(), budgets, torch.from_numpy(off).cuda(), head_off, kept,
+                   ws=ws)
+    torch.cuda.synchronize()
+    ho = head_off.cpu().numpy()
+    got = kept.cpu().numpy()
+    want = oracle.kept_positions_heads([sc[g].astype(np.float64) for g in range(Hkv)], n, W, b, 1, 0)
+    for g in range(Hkv):
+        np.testing.assert_array_equal(got[ho[g]:ho[g + 1]], want[g], err_msg=f"head {g} ({kinds[g]})")
