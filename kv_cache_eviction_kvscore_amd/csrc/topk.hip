@@ -161,8 +161,8 @@ constexpr int64_t kBitCap = (int64_t)kBitWords * 32;       // competitors the bi
 // PER > 1, nb = PER * NT and thread t owns bins nb-1-PER*t .. nb-PER*(t+1) (descending);
 // with PER = 1, thread t < nb owns bin nb-1-t. A scan over the threads' totals finds the
 // owning thread, and that thread the bin.
-template <int PER, int NR>
-__device__ __attribute__((always_inline)) void scan_digit(SelectSmem& sm, HistSmem& hs, const unsigned* h, int nb,
+template <int PER, int NR, class Hist>
+__device__ __attribute__((always_inline)) void scan_digit(SelectSmem& sm, Hist& hs, const unsigned* h, int nb,
                                                           const int64_t (&kr)[NR]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool owns = tid * PER < nb;
@@ -292,7 +292,8 @@ __device__ __attribute__((always_inline)) void radix_select(SelectSmem& sm, Hist
 // hs.hist[0, 512), below kBitBase, so the bitmasks are kept. Once at most kFew keys share
 // the prefix found so far, they are gathered and one wave ranks them directly: the key
 // with fewer than kr keys above it and at least kr at or above it.
-__device__ __attribute__((always_inline)) void list_select(SelectSmem& sm, HistSmem& hs, const unsigned* key, int cnt,
+template <class Hist>
+__device__ __attribute__((always_inline)) void list_select(SelectSmem& sm, Hist& hs, const unsigned* key, int cnt,
                                                            int64_t kr, unsigned prefix, int hb, unsigned& T,
                                                            int64_t& need_eq) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -963,68 +964,86 @@ __global__ __launch_bounds__(NT) void heads_band_kernel(Dev p, const float* __re
   }
 }
 
-// per chunk of one head: the keys above the band (counted, and marked in the chunk's
-// bitmask) and in it (listed with head and competitor index); each wave lists into its own
-// LDS region (a wave visits at most HCH / NWAVES keys), then one reservation in the group's
-// list
+// per PCH competitors of one head (four histogram chunks): the keys above the band
+// (counted, and set in the head's "surely kept" bitmask in global memory; the "tied"
+// bitmask's words are cleared) and in it (listed with head and competitor index in the
+// group's list). Every thread has its eight float4 loads in flight at once; a word of a
+// bitmask is the OR of eight lanes' nibbles. Each wave lists into an LDS region of its own
+// (ballots, no atomics), then one reservation per workgroup in the group's list and
+// coalesced copies; a region that overflows makes the reservation exceed the list, so the
+// group takes the radix passes.
+constexpr int PCH = 4 * HCH;
+constexpr int kPassWaveCap = 512;  // listed keys per wave region (of the wave's 2048)
+static_assert(PCH == 32 * NT, "eight float4s per thread");
 __global__ __launch_bounds__(NT) void heads_pass_kernel(Dev p, const float* __restrict__ score,
-                                                        HeadsState* __restrict__ st, int nch,
+                                                        HeadsState* __restrict__ st, int n_sink, int npc,
                                                         unsigned* __restrict__ above_cnt,
-                                                        unsigned* __restrict__ gsure, unsigned* __restrict__ gkey,
-                                                        unsigned* __restrict__ ghp) {
-  constexpr int WR = HCH / NWAVES;
-  __shared__ unsigned wl[NWAVES][WR], wp[NWAVES][WR];
-  __shared__ unsigned bits[HCH / 32];
+                                                        unsigned* __restrict__ gsure, unsigned* __restrict__ gtie,
+                                                        unsigned* __restrict__ gkey, unsigned* __restrict__ ghp) {
+  __shared__ unsigned wl[NWAVES][kPassWaveCap], wp[NWAVES][kPassWaveCap];
   __shared__ unsigned wn[NWAVES], wa[NWAVES];
   __shared__ unsigned s_base;
-  const int u = blockIdx.y, c = blockIdx.x;
+  const int u = blockIdx.y, pc = blockIdx.x;
   const int grp = u / p.Hkv, g = u % p.Hkv;
-  const HeadsState x = st[grp];
-  if (x.sel != 2 || x.band != 1) return;  // uniform
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int l, s;
   group_of(p, grp, l, s);
+  // the loads need nothing from the group's state (ns as heads_init_kernel sets it), so they
+  // are issued before it arrives; a group without a band ignores them
   const int64_t cand = p.cu[s + 1] - p.cu[s] - p.W;
-  const int64_t j0 = x.ns + (int64_t)c * HCH;
-  const int64_t j1 = (j0 + HCH < cand) ? j0 + HCH : cand;
-  const float* sc = score + (int64_t)(l * p.Hkv + g) * p.N + p.cu[s];
-  for (int i = tid; i < HCH / 32; i += NT) bits[i] = 0;
-  __syncthreads();
-  unsigned above = 0, n_w = 0;  // n_w: this wave's listed keys (uniform)
-  // key at j0 + r (r < HCH), if in range
-  auto visit = [&](float v, int r, bool in_range) __attribute__((always_inline)) {
-    const unsigned key = f2key(v);
-    if (in_range && key > x.hi) {
-      ++above;
-      atomicOr(&bits[r >> 5], 1u << (r & 31));
+  const int64_t ns = n_sink < cand ? n_sink : cand;
+  const int64_t M = cand - ns;
+  const int c0 = pc * PCH;  // first competitor of this workgroup (M <= kBitCap here: ints)
+  const int mi = M < (int64_t)kBitCap ? (int)M : (int)kBitCap;
+  const float* cb = score + (int64_t)(l * p.Hkv + g) * p.N + p.cu[s] + ns;
+  const bool vec = (((size_t)cb) & 15) == 0;
+  float v[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = c0 + 4 * (tid + NT * i);  // competitors j .. j+3
+    if (vec && j + 4 <= mi) {
+      const float4 f = *(const float4*)(cb + j);
+      v[i][0] = f.x;
+      v[i][1] = f.y;
+      v[i][2] = f.z;
+      v[i][3] = f.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[i][e] = j + e < mi ? cb[j + e] : 0.f;
     }
-    const bool in = in_range && key >= x.lo && key <= x.hi;
-    const unsigned long long msk = __ballot(in);
-    if (in) {
+  }
+  const HeadsState x = st[grp];
+  if (x.sel != 2 || x.band != 1) return;  // uniform
+  unsigned above = 0, n_w = 0;             // n_w: this wave's listed keys (uniform)
+  const int64_t wb = ((int64_t)u * npc + pc) * (PCH / 32);  // this workgroup's bitmask words
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = c0 + 4 * (tid + NT * i);
+    unsigned nib = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = j + e < mi;
+      const unsigned key = f2key(v[i][e]);
+      nib |= (ok && key > x.hi) ? 1u << e : 0u;
+      const bool in = ok && key >= x.lo && key <= x.hi;
+      const unsigned long long msk = __ballot(in);
       const unsigned slot =
           n_w + __builtin_amdgcn_mbcnt_hi((unsigned)(msk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)msk, 0u));
-      wl[wave][slot] = key;
-      wp[wave][slot] = (unsigned)(j0 - x.ns) + (unsigned)r;
+      if (in && slot < (unsigned)kPassWaveCap) {
+        wl[wave][slot] = key;
+        wp[wave][slot] = (unsigned)(j + e);
+      }
+      n_w += (unsigned)__popcll(msk);
     }
-    n_w += (unsigned)__popcll(msk);
-  };
-  static_assert(HCH == 8 * NT, "eight keys per thread");
-  if (j1 - j0 == HCH && (((size_t)(sc + j0)) & 15) == 0) {  // a whole aligned chunk: 16-byte loads
-    const int r = 8 * tid;
-    const float4 a = *(const float4*)(sc + j0 + r), b = *(const float4*)(sc + j0 + r + 4);
-    visit(a.x, r, true);
-    visit(a.y, r + 1, true);
-    visit(a.z, r + 2, true);
-    visit(a.w, r + 3, true);
-    visit(b.x, r + 4, true);
-    visit(b.y, r + 5, true);
-    visit(b.z, r + 6, true);
-    visit(b.w, r + 7, true);
-  } else {  // whole waves, at most HCH / NT keys per thread
-    for (int rb = 0; j0 + rb < j1; rb += NT) {
-      const int r = rb + tid;
-      const bool ok = j0 + r < j1;
-      visit(ok ? sc[j0 + r] : 0.f, r, ok);
+    above += __popc(nib);
+    unsigned w = nib << (4 * (lane & 7));
+    w |= __shfl_xor(w, 1, 64);
+    w |= __shfl_xor(w, 2, 64);
+    w |= __shfl_xor(w, 4, 64);
+    if ((lane & 7) == 0) {
+      const int64_t wi = wb + (tid + NT * i) / 8;
+      gsure[wi] = w;
+      gtie[wi] = 0u;
     }
   }
 #pragma unroll
@@ -1034,21 +1053,23 @@ __global__ __launch_bounds__(NT) void heads_pass_kernel(Dev p, const float* __re
     wn[wave] = n_w;
   }
   __syncthreads();
-  // the chunk's bitmask (zeros for a chunk past the head's competitors)
-  for (int i = tid; i < HCH / 32; i += NT) gsure[((int64_t)u * nch + c) * (HCH / 32) + i] = bits[i];
   if (tid == 0) {
     unsigned ta = 0, tn = 0;
+    bool over = false;
     for (int w = 0; w < NWAVES; ++w) {
       ta += wa[w];
       tn += wn[w];
+      over = over || wn[w] > (unsigned)kPassWaveCap;
     }
-    above_cnt[(int64_t)u * nch + c] = ta;
+    above_cnt[(int64_t)u * npc + pc] = ta;
+    if (over) tn = kGroupListCap + 1;  // the list cannot hold the band: radix passes
     s_base = tn ? atomicAdd(&st[grp].list_n, tn) : 0u;
   }
   __syncthreads();
   unsigned before = s_base;
   for (int w = 0; w < wave; ++w) before += wn[w];
-  for (unsigned i = lane; i < wn[wave]; i += 64) {
+  const unsigned mine = wn[wave] < (unsigned)kPassWaveCap ? wn[wave] : (unsigned)kPassWaveCap;
+  for (unsigned i = lane; i < mine; i += 64) {
     const unsigned pos = before + i;
     if (pos < (unsigned)kGroupListCap) {
       gkey[(int64_t)grp * kGroupListCap + pos] = wl[wave][i];
@@ -1057,26 +1078,33 @@ __global__ __launch_bounds__(NT) void heads_pass_kernel(Dev p, const float* __re
   }
 }
 
-// per group: did the band hold T? Then T and need_eq from the listed keys, and each head's
-// counts above T and at T (into the count pass's slots: chunk 0 of the head, the others 0)
-__global__ __launch_bounds__(NT) void heads_bsel_kernel(Dev p, HeadsState* __restrict__ st, int nch,
+// per group: did the band hold T? Then T and need_eq from the listed keys (in LDS), each
+// head's counts above T and at T (into the count pass's slots: chunk 0 of the head, the
+// others 0), and the listed keys above T and at T set in the heads' bitmasks
+struct SmallHist {
+  unsigned hist[1 << kBits12];
+  int tsum[NWAVES];
+};
+__global__ __launch_bounds__(NT) void heads_bsel_kernel(Dev p, HeadsState* __restrict__ st, int nch, int npc,
                                                         const unsigned* __restrict__ above_cnt,
                                                         const unsigned* __restrict__ gkey,
-                                                        const unsigned* __restrict__ ghp, unsigned* __restrict__ cnt) {
+                                                        const unsigned* __restrict__ ghp, unsigned* __restrict__ cnt,
+                                                        unsigned* __restrict__ gsure, unsigned* __restrict__ gtie) {
   __shared__ SelectSmem sm;
-  __shared__ HistSmem hs;
+  __shared__ SmallHist hs;
+  __shared__ unsigned lk[kGroupListCap];
   __shared__ unsigned hc[3][kMaxBandHeads];  // per head: above the band, above T, at T
   const int grp = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   HeadsState x = st[grp];
   if (x.sel != 2 || x.band != 1) return;  // uniform
-  const int Hkv = p.Hkv, nc = Hkv * nch;
+  const int Hkv = p.Hkv, nc = Hkv * npc;
   for (int i = tid; i < 3 * kMaxBandHeads; i += NT) (&hc[0][0])[i] = 0;
   __syncthreads();
   unsigned a = 0;
   for (int i = tid; i < nc; i += NT) {
     const unsigned v = above_cnt[(int64_t)grp * nc + i];
     a += v;
-    if (v) atomicAdd(&hc[0][i / nch], v);
+    if (v) atomicAdd(&hc[0][i / npc], v);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
@@ -1089,23 +1117,34 @@ __global__ __launch_bounds__(NT) void heads_bsel_kernel(Dev p, HeadsState* __res
     if (tid == 0) st[grp].band = 0;
     return;
   }
-  const unsigned* lk = gkey + (int64_t)grp * kGroupListCap;
-  const unsigned* lh = ghp + (int64_t)grp * kGroupListCap;
+  const unsigned* gk = gkey + (int64_t)grp * kGroupListCap;
+  const unsigned* gh = ghp + (int64_t)grp * kGroupListCap;
+  for (int i = tid; i < (int)L; i += NT) lk[i] = gk[i];
+  __syncthreads();
   const unsigned dif = x.lo ^ x.hi;
   const int hb = dif ? 32 - __clz((int)dif) : 0;
   unsigned T;
   int64_t need_eq;
   list_select(sm, hs, lk, (int)L, x.kr - A, hb >= 32 ? 0u : x.lo & (~0u << hb), hb, T, need_eq);
+  const int64_t hw = (int64_t)npc * (PCH / 32);  // bitmask words per head
   for (int i = tid; i < (int)L; i += NT) {
-    const unsigned key = lk[i], h = lh[i] >> kHeadShift;
-    if (key > T) atomicAdd(&hc[1][h], 1u);
-    else if (key == T) atomicAdd(&hc[2][h], 1u);
+    const unsigned key = lk[i];
+    if (key < T) continue;
+    const unsigned hp = gh[i], h = hp >> kHeadShift, c = hp & ((1u << kHeadShift) - 1u);
+    const int64_t wi = (int64_t)(grp * Hkv + (int)h) * hw + (c >> 5);
+    if (key > T) {
+      atomicAdd(&hc[1][h], 1u);
+      atomicOr(&gsure[wi], 1u << (c & 31));
+    } else {
+      atomicAdd(&hc[2][h], 1u);
+      atomicOr(&gtie[wi], 1u << (c & 31));
+    }
   }
   __syncthreads();
-  for (int i = tid; i < nc; i += NT) {
+  for (int i = tid; i < Hkv * nch; i += NT) {
     const int h = i / nch, c = i % nch;
-    cnt[((int64_t)grp * nc + i) * 2] = c == 0 ? hc[0][h] + hc[1][h] : 0u;
-    cnt[((int64_t)grp * nc + i) * 2 + 1] = c == 0 ? hc[2][h] : 0u;
+    cnt[((int64_t)grp * Hkv * nch + i) * 2] = c == 0 ? hc[0][h] + hc[1][h] : 0u;
+    cnt[((int64_t)grp * Hkv * nch + i) * 2 + 1] = c == 0 ? hc[2][h] : 0u;
   }
   if (tid == 0) {
     x.prefix = T;
@@ -1276,9 +1315,8 @@ __global__ __launch_bounds__(NT) void heads_emit_kernel(Dev p, const float* __re
                                                         const unsigned* __restrict__ cnt,
                                                         const int64_t* __restrict__ seg_off,
                                                         int64_t* __restrict__ head_off, int32_t* __restrict__ kept,
-                                                        const unsigned* __restrict__ gsure,
-                                                        const unsigned* __restrict__ gkey,
-                                                        const unsigned* __restrict__ ghp) {
+                                                        int npc, const unsigned* __restrict__ gsure,
+                                                        const unsigned* __restrict__ gtie) {
   __shared__ SelectSmem sm;
   __shared__ unsigned bm[2 * kBitWords];
   const int u = blockIdx.x;
@@ -1317,24 +1355,15 @@ __global__ __launch_bounds__(NT) void heads_emit_kernel(Dev p, const float* __re
     if (u == p.U - 1) head_off[p.U] = off + bg;
   }
   if (x.sel == 2 && x.band == 2) {
-    // the head's bitmasks: its chunks' "above the band" words, then its listed keys against T
+    // the head's bitmasks, complete in global memory
     const int tid = threadIdx.x;
     unsigned* sure = bm;
     unsigned* tie = bm + kBitWords;
     const int nw = (int)((M + 31) >> 5);  // M <= kBitCap
+    const int64_t hw = (int64_t)u * npc * (PCH / 32);
     for (int i = tid; i < nw; i += NT) {
-      sure[i] = gsure[(int64_t)u * nch * (HCH / 32) + i];
-      tie[i] = 0;
-    }
-    __syncthreads();
-    const unsigned* lk = gkey + (int64_t)grp * kGroupListCap;
-    const unsigned* lh = ghp + (int64_t)grp * kGroupListCap;
-    for (int i = tid; i < (int)x.list_n; i += NT) {
-      const unsigned hp = lh[i];
-      if ((int)(hp >> kHeadShift) != g) continue;
-      const unsigned key = lk[i], c = hp & ((1u << kHeadShift) - 1u);
-      if (key > x.prefix) atomicOr(&sure[c >> 5], 1u << (c & 31));
-      else if (key == x.prefix) atomicOr(&tie[c >> 5], 1u << (c & 31));
+      sure[i] = gsure[hw + i];
+      tie[i] = gtie[hw + i];
     }
     __syncthreads();
     emit_words(sm, kept + off, bg, take, sure, tie, n, cand, ns);
@@ -1358,23 +1387,26 @@ hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off,
     hipLaunchKernelGGL(topk_kernel, dim3(p.U), dim3(NT), 0, st, p, key, n_sink, seg_off, kept);
     return hipGetLastError();
   }
-  // head budgets chosen jointly; scratch: states | chunk histograms | chunk counts | chunk
-  // counts above the band | chunk bitmasks above the band | the groups' band lists (keys,
-  // then head and competitor index)
+  // head budgets chosen jointly; scratch: states | chunk histograms | chunk counts | counts
+  // above the band | the heads' "surely kept" and "tied" bitmasks | the groups' band lists
+  // (keys, then head and competitor index)
   const int groups = p.U / p.Hkv;
   const int nch = heads_chunks(p);
   HeadsState* hs = (HeadsState*)heads_ws;
   unsigned* whist = (unsigned*)((char*)heads_ws + heads_state_bytes(p));
   unsigned* cnt = whist + (size_t)p.U * nch * 256;
+  const int npc = (nch + 3) / 4;  // band-pass workgroups per head (PCH competitors each)
   unsigned* above = cnt + (size_t)p.U * nch * 2;
-  unsigned* gsure = above + (size_t)p.U * nch;
-  unsigned* gkey = gsure + (size_t)p.U * nch * (HCH / 32);
+  unsigned* gsure = above + (size_t)p.U * npc;
+  unsigned* gtie = gsure + (size_t)p.U * npc * (PCH / 32);
+  unsigned* gkey = gtie + (size_t)p.U * npc * (PCH / 32);
   unsigned* ghp = gkey + (size_t)groups * kGroupListCap;
   hipLaunchKernelGGL(heads_init_kernel, dim3(groups), dim3(64), 0, st, p, n_sink, seg_off, hs);
   hipLaunchKernelGGL(heads_band_kernel, dim3(groups), dim3(NT), 0, st, p, key, hs);
-  hipLaunchKernelGGL(heads_pass_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, hs, nch, above, gsure, gkey, ghp);
-  hipLaunchKernelGGL(heads_bsel_kernel, dim3(groups), dim3(NT), 0, st, p, hs, nch, (const unsigned*)above,
-                     (const unsigned*)gkey, (const unsigned*)ghp, cnt);
+  hipLaunchKernelGGL(heads_pass_kernel, dim3(npc, p.U), dim3(NT), 0, st, p, key, hs, n_sink, npc, above, gsure, gtie,
+                     gkey, ghp);
+  hipLaunchKernelGGL(heads_bsel_kernel, dim3(groups), dim3(NT), 0, st, p, hs, nch, npc, (const unsigned*)above,
+                     (const unsigned*)gkey, (const unsigned*)ghp, cnt, gsure, gtie);
   for (int pass = 0; pass < 4; ++pass) {
     hipLaunchKernelGGL(heads_hist_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, pass, nch,
                        whist);
@@ -1382,8 +1414,8 @@ hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off,
   }
   hipLaunchKernelGGL(heads_count_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, nch, cnt);
   hipLaunchKernelGGL(heads_emit_kernel, dim3(p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, nch,
-                     (const unsigned*)cnt, seg_off, head_off, kept, (const unsigned*)gsure, (const unsigned*)gkey,
-                     (const unsigned*)ghp);
+                     (const unsigned*)cnt, seg_off, head_off, kept, npc, (const unsigned*)gsure,
+                     (const unsigned*)gtie);
   return hipGetLastError();
 }
 
@@ -1391,7 +1423,8 @@ int heads_chunks(const Dev& p) { return (int)((p.max_n - p.W + HCH - 1) / HCH); 
 size_t heads_state_bytes(const Dev& p) { return ((size_t)(p.U / p.Hkv) * sizeof(HeadsState) + 255) / 256 * 256; }
 size_t heads_ws_bytes(const Dev& p) {
   const size_t nch = (size_t)heads_chunks(p);
-  return heads_state_bytes(p) + ((size_t)p.U * nch * (256 + 2 + 1 + HCH / 32) * 4 +
+  const size_t npc = (nch + 3) / 4;
+  return heads_state_bytes(p) + ((size_t)p.U * nch * (256 + 2) * 4 + (size_t)p.U * npc * (1 + 2 * PCH / 32) * 4 +
                                  (size_t)(p.U / p.Hkv) * kGroupListCap * 2 * 4 + 255) / 256 * 256;
 }
 
