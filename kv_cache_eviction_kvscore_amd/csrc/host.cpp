@@ -414,7 +414,7 @@ int kvscore_topk(const kvscore_problem* p, const float* score, const int32_t* bu
     if (int rc = check_ws(workspace, workspace_bytes, ws_topk(d))) return rc;
   }
   return launched(kvs::launch_topk(d, score, seg_offsets, kept_pos, pool, n_sink, (float*)workspace, nullptr, nullptr,
-                                   (hipStream_t)stream),
+                                   nullptr, (hipStream_t)stream),
                   "kvscore_topk");
 }
 
@@ -429,7 +429,7 @@ int kvscore_topk_heads(const kvscore_problem* p, const float* score, const int32
   const size_t hb = kvs::heads_ws_bytes(d);
   if (int rc = check_ws(workspace, workspace_bytes, hb + (pool > 1 ? ws_topk(d) : 0))) return rc;
   return launched(kvs::launch_topk(d, score, seg_offsets, kept_pos, pool, n_sink, (float*)((char*)workspace + hb),
-                                   head_offsets, workspace, (hipStream_t)stream),
+                                   head_offsets, workspace, budgets, (hipStream_t)stream),
                   "kvscore_topk_heads");
 }
 

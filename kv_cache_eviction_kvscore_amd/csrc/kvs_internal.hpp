@@ -171,9 +171,10 @@ hipError_t launch_score(const Dev& p, const void* q, const void* k, const void* 
 hipError_t launch_merge(const Dev& p, const float* partial, const int32_t* jstar, const float* dom, float* score,
                         hipStream_t st);
 // head_off != nullptr: head budgets chosen jointly per (sequence, layer), their offsets
-// written to head_off [U+1], using heads_ws (heads_ws_bytes(p) bytes) as scratch
+// written to head_off [U+1], using heads_ws (heads_ws_bytes(p) bytes) as scratch; budgets
+// (host [S][L], the segment lengths) then choose which kernels are launched
 hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off, int32_t* kept, int pool, int n_sink,
-                       float* pooled, int64_t* head_off, void* heads_ws, hipStream_t st);
+                       float* pooled, int64_t* head_off, void* heads_ws, const int32_t* budgets, hipStream_t st);
 int heads_chunks(const Dev& p);
 size_t heads_state_bytes(const Dev& p);
 size_t heads_ws_bytes(const Dev& p);

@@ -36,6 +36,8 @@
 // heads_*_kernel (head budgets chosen jointly over a layer's KV heads) run a select of
 // their own, spread over many workgroups: four passes of 8 bits, one 256-bin histogram
 // per (chunk, head) summed per layer in a fixed order (described at those kernels).
+#include <cmath>
+
 #include "kvs_internal.hpp"
 
 namespace kvs {
@@ -895,7 +897,7 @@ static_assert(HCH % NWAVES == 0 && HCH % 32 == 0, "chunk split over the waves an
 static_assert(kBitCap <= (1 << kHeadShift), "competitor index fits below the head");
 
 __global__ __launch_bounds__(NT) void heads_band_kernel(Dev p, const float* __restrict__ score,
-                                                        HeadsState* __restrict__ st) {
+                                                        HeadsState* __restrict__ st, int inner) {
   __shared__ SelectSmem sm;
   __shared__ HistSmem hs;
   const int grp = blockIdx.x, tid = threadIdx.x;
@@ -911,8 +913,20 @@ __global__ __launch_bounds__(NT) void heads_band_kernel(Dev p, const float* __re
   const float MS = 4.f * (float)runs;  // sampled keys
   const float q = (float)x.kr / (float)tot;
   const float band = 2.f * (4.f * sqrtf(MS * q * (1.f - q)) + 16.f) * (float)tot / MS;
-  if ((M >> 2) < per_head || M > kBitCap || Hkv > kMaxBandHeads || band > 0.85f * kGroupListCap)
-    return;  // uniform: radix passes
+  // with inner, the host has checked every group (heads_fast) and no radix pass follows: a
+  // group that still fails the exact checks (segment offsets that disagree with the budgets)
+  // gets a band that cannot hold T, so the select's own fallback runs
+  const bool fits = (M >> 2) >= per_head && M <= kBitCap && Hkv <= kMaxBandHeads;
+  if (!fits || (!inner && band > 0.85f * kGroupListCap)) {  // uniform
+    if (inner && tid == 0) {
+      x.band = 1;
+      x.lo = 1u;
+      x.hi = 0u;
+      x.list_n = kGroupListCap + 1;
+      st[grp] = x;
+    }
+    return;
+  }
   unsigned xk[kHeadsRuns][4];
   bool ok[kHeadsRuns];
 #pragma unroll
@@ -1080,19 +1094,26 @@ __global__ __launch_bounds__(NT) void heads_pass_kernel(Dev p, const float* __re
 
 // per group: did the band hold T? Then T and need_eq from the listed keys (in LDS), each
 // head's counts above T and at T (into the count pass's slots: chunk 0 of the head, the
-// others 0), and the listed keys above T and at T set in the heads' bitmasks
+// others 0), and the listed keys above T and at T set in the heads' bitmasks. If not: with
+// `inner`, the select runs here from scratch over the group's keys (three reads, then a
+// count per head: slow, for data the sample misjudges) and the emission reads the scores;
+// else the radix passes that follow do it.
 struct SmallHist {
   unsigned hist[1 << kBits12];
   int tsum[NWAVES];
 };
-__global__ __launch_bounds__(NT) void heads_bsel_kernel(Dev p, HeadsState* __restrict__ st, int nch, int npc,
+__global__ __launch_bounds__(NT) void heads_bsel_kernel(Dev p, const float* __restrict__ score,
+                                                        HeadsState* __restrict__ st, int nch, int npc, int inner,
                                                         const unsigned* __restrict__ above_cnt,
                                                         const unsigned* __restrict__ gkey,
                                                         const unsigned* __restrict__ ghp, unsigned* __restrict__ cnt,
                                                         unsigned* __restrict__ gsure, unsigned* __restrict__ gtie) {
   __shared__ SelectSmem sm;
-  __shared__ SmallHist hs;
-  __shared__ unsigned lk[kGroupListCap];
+  __shared__ SmallHist shs;
+  __shared__ union {
+    unsigned lk[kGroupListCap];
+    HistSmem hs;
+  } bu;
   __shared__ unsigned hc[3][kMaxBandHeads];  // per head: above the band, above T, at T
   const int grp = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   HeadsState x = st[grp];
@@ -1113,22 +1134,68 @@ __global__ __launch_bounds__(NT) void heads_bsel_kernel(Dev p, HeadsState* __res
   int64_t A = 0;
   for (int w = 0; w < NWAVES; ++w) A += (unsigned)sm.wsum[0][w];
   const int64_t L = x.list_n;
-  if (L > kGroupListCap || A >= x.kr || x.kr > A + L) {  // uniform: the radix passes run
-    if (tid == 0) st[grp].band = 0;
+  unsigned T;
+  int64_t need_eq;
+  if (L > kGroupListCap || A >= x.kr || x.kr > A + L) {  // uniform: the band did not hold T
+    if (!inner) {
+      if (tid == 0) st[grp].band = 0;
+      return;
+    }
+    int l, s;
+    group_of(p, grp, l, s);
+    const int64_t M = p.cu[s + 1] - p.cu[s] - p.W - x.ns;
+    const float* gb = score + (int64_t)l * Hkv * p.N + p.cu[s] + x.ns;  // head h: gb + h * N
+    // every competitor of the group's heads, whole waves, eight loads in flight per thread
+    auto each = [&](auto f) __attribute__((always_inline)) {
+      for (int h = 0; h < Hkv; ++h) {
+        const float* hb = gb + (int64_t)h * p.N;
+        for (int64_t j0 = 0; j0 < M; j0 += 8 * NT) {
+          float vv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int64_t j = j0 + tid + (int64_t)NT * e;
+            vv[e] = j < M ? hb[j] : 0.f;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f(f2key(vv[e]), h, j0 + tid + (int64_t)NT * e < M);
+        }
+      }
+    };
+    bool listed = false;
+    radix_select(sm, bu.hs, [&](auto f) { each([&](unsigned key, int, bool ok) { if (ok) f(key, 0); }); }, x.kr, T,
+                 need_eq, nullptr, nullptr, listed);
+    // each head's keys above T and at T (counted per wave, added in LDS)
+    each([&](unsigned key, int h, bool ok) {
+      const unsigned long long gt = __ballot(ok && key > T), eq = __ballot(ok && key == T);
+      if (lane == 0) {
+        if (gt) atomicAdd(&hc[1][h], (unsigned)__popcll(gt));
+        if (eq) atomicAdd(&hc[2][h], (unsigned)__popcll(eq));
+      }
+    });
+    __syncthreads();
+    for (int i = tid; i < Hkv * nch; i += NT) {
+      const int h = i / nch, c = i % nch;
+      cnt[((int64_t)grp * Hkv * nch + i) * 2] = c == 0 ? hc[1][h] : 0u;
+      cnt[((int64_t)grp * Hkv * nch + i) * 2 + 1] = c == 0 ? hc[2][h] : 0u;
+    }
+    if (tid == 0) {
+      x.prefix = T;
+      x.need_eq = need_eq;
+      x.band = 3;
+      st[grp] = x;
+    }
     return;
   }
   const unsigned* gk = gkey + (int64_t)grp * kGroupListCap;
   const unsigned* gh = ghp + (int64_t)grp * kGroupListCap;
-  for (int i = tid; i < (int)L; i += NT) lk[i] = gk[i];
+  for (int i = tid; i < (int)L; i += NT) bu.lk[i] = gk[i];
   __syncthreads();
   const unsigned dif = x.lo ^ x.hi;
   const int hb = dif ? 32 - __clz((int)dif) : 0;
-  unsigned T;
-  int64_t need_eq;
-  list_select(sm, hs, lk, (int)L, x.kr - A, hb >= 32 ? 0u : x.lo & (~0u << hb), hb, T, need_eq);
+  list_select(sm, shs, bu.lk, (int)L, x.kr - A, hb >= 32 ? 0u : x.lo & (~0u << hb), hb, T, need_eq);
   const int64_t hw = (int64_t)npc * (PCH / 32);  // bitmask words per head
   for (int i = tid; i < (int)L; i += NT) {
-    const unsigned key = lk[i];
+    const unsigned key = bu.lk[i];
     if (key < T) continue;
     const unsigned hp = gh[i], h = hp >> kHeadShift, c = hp & ((1u << kHeadShift) - 1u);
     const int64_t wi = (int64_t)(grp * Hkv + (int)h) * hw + (c >> 5);
@@ -1375,8 +1442,30 @@ __global__ __launch_bounds__(NT) void heads_emit_kernel(Dev p, const float* __re
 
 }  // namespace
 
+// Whether every group of a joint select can take the sampled band with the select's own
+// fallback (no radix pass launched): competitors within the bitmasks, few enough heads,
+// enough competitors for the sample, a band expected to fit the list. budgets: host
+// [S][L], the segment lengths.
+bool heads_fast(const Dev& p, const int32_t* budgets, int n_sink) {
+  const int Hkv = p.Hkv, per_head = NT * kHeadsRuns / Hkv;
+  if (Hkv > kMaxBandHeads) return false;
+  for (int l = 0; l < p.L; ++l)
+    for (int s = 0; s < p.S; ++s) {
+      const int64_t cand = p.cu[s + 1] - p.cu[s] - p.W;
+      const int64_t ns = n_sink < cand ? n_sink : cand;
+      const int64_t M = cand - ns;
+      int64_t kt = (int64_t)Hkv * ((int64_t)budgets[(int64_t)s * p.L + l] - p.W - ns);
+      if (kt <= 0 || kt >= (int64_t)Hkv * M) continue;  // nothing to select
+      if ((M >> 2) < per_head || M > kBitCap) return false;
+      const double tot = (double)Hkv * (double)M, MS = 4.0 * per_head * Hkv, q = (double)kt / tot;
+      const double band = 2.0 * (4.0 * std::sqrt(MS * q * (1.0 - q)) + 16.0) * tot / MS;
+      if (band > 0.8 * kGroupListCap) return false;
+    }
+  return true;
+}
+
 hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off, int32_t* kept, int pool, int n_sink,
-                       float* pooled, int64_t* head_off, void* heads_ws, hipStream_t st) {
+                       float* pooled, int64_t* head_off, void* heads_ws, const int32_t* budgets, hipStream_t st) {
   const float* key = score;
   if (pool > 1) {
     const dim3 gp((unsigned)((p.max_n + PT - 1) / PT), p.U);
@@ -1401,18 +1490,21 @@ hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off,
   unsigned* gtie = gsure + (size_t)p.U * npc * (PCH / 32);
   unsigned* gkey = gtie + (size_t)p.U * npc * (PCH / 32);
   unsigned* ghp = gkey + (size_t)groups * kGroupListCap;
+  const int inner = heads_fast(p, budgets, n_sink) ? 1 : 0;
   hipLaunchKernelGGL(heads_init_kernel, dim3(groups), dim3(64), 0, st, p, n_sink, seg_off, hs);
-  hipLaunchKernelGGL(heads_band_kernel, dim3(groups), dim3(NT), 0, st, p, key, hs);
+  hipLaunchKernelGGL(heads_band_kernel, dim3(groups), dim3(NT), 0, st, p, key, hs, inner);
   hipLaunchKernelGGL(heads_pass_kernel, dim3(npc, p.U), dim3(NT), 0, st, p, key, hs, n_sink, npc, above, gsure, gtie,
                      gkey, ghp);
-  hipLaunchKernelGGL(heads_bsel_kernel, dim3(groups), dim3(NT), 0, st, p, hs, nch, npc, (const unsigned*)above,
-                     (const unsigned*)gkey, (const unsigned*)ghp, cnt, gsure, gtie);
-  for (int pass = 0; pass < 4; ++pass) {
-    hipLaunchKernelGGL(heads_hist_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, pass, nch,
-                       whist);
-    hipLaunchKernelGGL(heads_digit_kernel, dim3(groups), dim3(1024), 0, st, p, hs, pass, nch, (const unsigned*)whist);
+  hipLaunchKernelGGL(heads_bsel_kernel, dim3(groups), dim3(NT), 0, st, p, key, hs, nch, npc, inner,
+                     (const unsigned*)above, (const unsigned*)gkey, (const unsigned*)ghp, cnt, gsure, gtie);
+  if (!inner) {  // groups without a band: the radix passes, then the count
+    for (int pass = 0; pass < 4; ++pass) {
+      hipLaunchKernelGGL(heads_hist_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, pass, nch,
+                         whist);
+      hipLaunchKernelGGL(heads_digit_kernel, dim3(groups), dim3(1024), 0, st, p, hs, pass, nch, (const unsigned*)whist);
+    }
+    hipLaunchKernelGGL(heads_count_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, nch, cnt);
   }
-  hipLaunchKernelGGL(heads_count_kernel, dim3(nch, p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, nch, cnt);
   hipLaunchKernelGGL(heads_emit_kernel, dim3(p.U), dim3(NT), 0, st, p, key, (const HeadsState*)hs, nch,
                      (const unsigned*)cnt, seg_off, head_off, kept, npc, (const unsigned*)gsure,
                      (const unsigned*)gtie);
