@@ -850,10 +850,8 @@ __device__ inline void group_of(const Dev& p, int grp, int& l, int& s) {
   s = grp % p.S;
 }
 
-__global__ __launch_bounds__(64) void heads_init_kernel(Dev p, int n_sink, const int64_t* __restrict__ seg_off,
-                                                        HeadsState* __restrict__ st) {
-  const int grp = blockIdx.x;
-  if (threadIdx.x != 0) return;
+// a group's initial state: its rank to place, its selection kind, its sinks
+__device__ inline HeadsState heads_state0(const Dev& p, int grp, int n_sink, const int64_t* __restrict__ seg_off) {
   int l, s;
   group_of(p, grp, l, s);
   const int64_t n = p.cu[s + 1] - p.cu[s];
@@ -875,8 +873,9 @@ __global__ __launch_bounds__(64) void heads_init_kernel(Dev p, int n_sink, const
   x.hi = 0;
   x.list_n = 0;
   x.pad = 0;
-  st[grp] = x;
+  return x;
 }
+
 
 // The joint select in one read when a sample allows, as the per-unit select does: a
 // strided sample over the group's heads (four 4-key runs per thread, the heads taking runs
@@ -896,13 +895,16 @@ constexpr int kHeadShift = 18;            // list position: head << 18 | competi
 static_assert(HCH % NWAVES == 0 && HCH % 32 == 0, "chunk split over the waves and words");
 static_assert(kBitCap <= (1 << kHeadShift), "competitor index fits below the head");
 
-__global__ __launch_bounds__(NT) void heads_band_kernel(Dev p, const float* __restrict__ score,
+// (it also writes the group's initial state: no separate init launch)
+__global__ __launch_bounds__(NT) void heads_band_kernel(Dev p, const float* __restrict__ score, int n_sink,
+                                                        const int64_t* __restrict__ seg_off,
                                                         HeadsState* __restrict__ st, int inner) {
   __shared__ SelectSmem sm;
   __shared__ HistSmem hs;
   const int grp = blockIdx.x, tid = threadIdx.x;
-  HeadsState x = st[grp];
-  if (x.sel != 2) return;  // uniform
+  HeadsState x = heads_state0(p, grp, n_sink, seg_off);
+  if (tid == 0) st[grp] = x;  // overwritten below when a band is set
+  if (x.sel != 2) return;     // uniform
   int l, s;
   group_of(p, grp, l, s);
   const int64_t M = p.cu[s + 1] - p.cu[s] - p.W - x.ns;
@@ -1002,7 +1004,7 @@ __global__ __launch_bounds__(NT) void heads_pass_kernel(Dev p, const float* __re
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int l, s;
   group_of(p, grp, l, s);
-  // the loads need nothing from the group's state (ns as heads_init_kernel sets it), so they
+  // the loads need nothing from the group's state (ns as heads_state0 sets it), so they
   // are issued before it arrives; a group without a band ignores them
   const int64_t cand = p.cu[s + 1] - p.cu[s] - p.W;
   const int64_t ns = n_sink < cand ? n_sink : cand;
@@ -1397,10 +1399,11 @@ __global__ __launch_bounds__(NT) void heads_emit_kernel(Dev p, const float* __re
   const int64_t M = cand - ns;
   // the kept competitors of head h: above T plus its share of the ties
   int64_t ties_before = 0, off = seg_off[grp * p.Hkv], kg = 0, take = 0;
+  const int ncs = x.band >= 2 ? 1 : nch;  // the select kernel wrote each head's totals to chunk 0
   for (int h = 0; h <= g; ++h) {
     int64_t sure = 0, eq = 0;
     if (x.sel == 2) {
-      for (int c = 0; c < nch; ++c) {
+      for (int c = 0; c < ncs; ++c) {
         sure += cnt[((int64_t)(grp * p.Hkv + h) * nch + c) * 2];
         eq += cnt[((int64_t)(grp * p.Hkv + h) * nch + c) * 2 + 1];
       }
@@ -1491,8 +1494,7 @@ hipError_t launch_topk(const Dev& p, const float* score, const int64_t* seg_off,
   unsigned* gkey = gtie + (size_t)p.U * npc * (PCH / 32);
   unsigned* ghp = gkey + (size_t)groups * kGroupListCap;
   const int inner = heads_fast(p, budgets, n_sink) ? 1 : 0;
-  hipLaunchKernelGGL(heads_init_kernel, dim3(groups), dim3(64), 0, st, p, n_sink, seg_off, hs);
-  hipLaunchKernelGGL(heads_band_kernel, dim3(groups), dim3(NT), 0, st, p, key, hs, inner);
+  hipLaunchKernelGGL(heads_band_kernel, dim3(groups), dim3(NT), 0, st, p, key, n_sink, seg_off, hs, inner);
   hipLaunchKernelGGL(heads_pass_kernel, dim3(npc, p.U), dim3(NT), 0, st, p, key, hs, n_sink, npc, above, gsure, gtie,
                      gkey, ghp);
   hipLaunchKernelGGL(heads_bsel_kernel, dim3(groups), dim3(NT), 0, st, p, key, hs, nch, npc, inner,
