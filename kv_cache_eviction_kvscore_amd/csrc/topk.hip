@@ -108,9 +108,19 @@ __global__ __launch_bounds__(256) void pool_kernel(Dev p, const float* __restric
   const int h = pool >> 1;
   const int64_t base = (int64_t)(l * p.Hkv + g) * p.N + p.cu[s];
   const float* sc = score + base;
-  for (int i = threadIdx.x; i < PT + 2 * h; i += 256) {
+  // every load of the tile and its halo in flight before the first LDS write
+  constexpr int PER = (PT + kMaxPool - 1 + 255) / 256;
+  float vals[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = threadIdx.x + 256 * k;
     const int64_t j = j0 - h + i;
-    tile[i] = (j >= 0 && j < cand) ? sc[j] : -INFINITY;
+    vals[k] = (i < PT + 2 * h && j >= 0 && j < cand) ? sc[j] : -INFINITY;
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < PT + 2 * h) tile[i] = vals[k];
   }
   __syncthreads();
   for (int i = threadIdx.x; i < PT; i += 256) {
