@@ -245,8 +245,11 @@ int kvscore_topk(const kvscore_problem* p, const float* score, const int32_t* bu
  * kvscore_topk), ties to the lower head, then the lower position.
  * workspace: device, kvscore_workspace_size(p, KVSCORE_WS_TOPK_HEADS) bytes, 256-byte
  * aligned: the select's scratch (per-layer state, per-chunk histograms, counts and
- * bitmasks, each layer's list of sampled-band keys), then the pooled keys; with pool = 1 only the scratch part (that size minus
- * kvscore_workspace_size(p, KVSCORE_WS_TOPK)) is needed. Calls on one stream reuse it.
+ * bitmasks, each layer's list of sampled-band keys), then the pooled keys; with pool = 1
+ * only the scratch part (that size minus kvscore_workspace_size(p, KVSCORE_WS_TOPK)) is
+ * needed. Calls on one stream reuse it. budgets (host) also choose which kernels are
+ * launched (a sampled band for every layer, or histogram passes for those without one);
+ * the result does not depend on that choice.
  * The other arguments as kvscore_topk; seg_offsets is still the DEVICE copy of
  * kvscore_segment_offsets(p, budgets) (it gives each layer's block). The heads' own
  * segments are data-dependent: their offsets go to head_offsets (device int64 [U+1],
