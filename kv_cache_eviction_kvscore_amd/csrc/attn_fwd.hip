@@ -543,6 +543,40 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
   }
 }
 
+// A row's outputs from its merged records: acc = the rest's weighted sum and lr its weight
+// (both relative to M2, the max over every key but the argmax), vs the argmax's value row.
+// p* = 1 / (1 + rel * lr), rel = exp2(M2 - M): the rest's total weight relative to the max.
+constexpr int kCombineMax = 8;  // chunks a row's records are merged from in one load round
+template <int PER>
+__device__ __attribute__((always_inline)) void combine_out(const Dev& p, float* __restrict__ a,
+                                                           float* __restrict__ lse, int32_t* __restrict__ jstar,
+                                                           float* __restrict__ dom, size_t ro, int lane, float M,
+                                                           float M2, float lr, const float (&acc)[PER],
+                                                           const float (&vs)[PER], int jwin) {
+  constexpr int D = 64 * PER;
+  const float rel = (M2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M2 - M);
+  const float lt = rel * lr;
+  const float pstar = 1.f / (1.f + lt);
+  float d2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    a[ro * D + e] = (rel * acc[i] + vs[i]) * pstar;
+    const float df = (lr > 0.f ? acc[i] / lr : vs[i]) - vs[i];
+    d2 += df * df;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) d2 += __shfl_xor(d2, off, 64);
+  if (lane == 0) {
+    const float shift = pstar * sqrtf(d2);
+    // the isolated pair's term in the call's score: its shift (L2), squared (SQ), or its
+    // attention weight p* (attention sum)
+    dom[ro] = (p.mode == 1) ? shift * shift : (p.mode == 2 ? pstar : shift);
+    lse[ro] = (M + __log2f(1.f + lt)) * 0.69314718055994531f;
+    jstar[ro] = jwin;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __restrict__ ws,
                                                           float* __restrict__ a, float* __restrict__ lse,
@@ -564,6 +598,78 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
   // stat(c, 0) = m (max), 1 = m2 (max of the rest), 2 = l_rest (relative to m2), 3 = j*
   const size_t ro = (size_t)u * p.R + row;
   if (nch == 1) return;  // uniform: fwd_partial wrote this row's outputs
+  if (nch <= kCombineMax) {
+    // every chunk's statistics and row loaded at once (one memory latency instead of one
+    // per chunk and pass), then the same arithmetic in the same order as below
+    float mc[kCombineMax], m2c[kCombineMax], lc[kCombineMax], oc[kCombineMax][PER], vc[kCombineMax][PER];
+    int jc[kCombineMax];
+#pragma unroll
+    for (int c = 0; c < kCombineMax; ++c) {
+      mc[c] = m2c[c] = -INFINITY;
+      lc[c] = 0.f;
+      jc[c] = -1;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) oc[c][i] = vc[c][i] = 0.f;
+      if (c < nch) {  // uniform
+        mc[c] = *stat(c, 0);
+        m2c[c] = *stat(c, 1);
+        lc[c] = *stat(c, 2);
+        jc[c] = *(const int*)stat(c, 3);
+        const float* Oc = block(c) + (size_t)row_t * D;
+        const _Float16* Vc = (const _Float16*)(block(c) + (size_t)p.RT * D) + (size_t)row_t * D;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          oc[c][i] = Oc[lane + 64 * i];
+          vc[c][i] = (float)Vc[lane + 64 * i];
+        }
+      }
+    }
+    float M = -INFINITY;
+    int win = -1;
+#pragma unroll
+    for (int c = 0; c < kCombineMax; ++c)
+      if (jc[c] >= 0 && mc[c] > M) {
+        M = mc[c];
+        win = c;
+      }
+    if (win < 0) {  // no visible key recorded (cannot happen for valid shapes: key 0 is always visible)
+      for (int e = lane; e < D; e += 64) a[ro * D + e] = 0.f;
+      if (lane == 0) {
+        dom[ro] = 0.f;
+        lse[ro] = -INFINITY;
+        jstar[ro] = -1;
+      }
+      return;
+    }
+    float M2 = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kCombineMax; ++c) {
+      if (jc[c] < 0) continue;
+      M2 = fmaxf(M2, m2c[c]);
+      if (c != win) M2 = fmaxf(M2, mc[c]);
+    }
+    float acc[PER], vs[PER];
+    float lr = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      acc[i] = 0.f;
+      vs[i] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < kCombineMax; ++c) {
+      if (jc[c] < 0) continue;
+      const float w2 = (m2c[c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2c[c] - M2);
+      const float w1 = (c != win) ? __builtin_amdgcn_exp2f(mc[c] - M2) : 0.f;
+      lr += w2 * lc[c] + w1;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        acc[i] += w2 * oc[c][i] + w1 * vc[c][i];
+        if (c == win) vs[i] = vc[c][i];
+      }
+    }
+    combine_out(p, a, lse, jstar, dom, ro, lane, M, M2, lr, acc, vs, jc[win]);
+    return;
+  }
   float M = -INFINITY;
   int win = -1;
   for (int c = 0; c < nch; ++c) {
@@ -610,28 +716,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
       if (c == win) vs[i] = vv;
     }
   }
-  // p* = 1 / (1 + rel * lr), rel = exp2(M2 - M): the rest's total weight relative to the max
-  const float rel = (M2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M2 - M);
-  const float lt = rel * lr;
-  const float pstar = 1.f / (1.f + lt);
-  float d2 = 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
-    a[ro * D + e] = (rel * acc[i] + vs[i]) * pstar;
-    const float df = (lr > 0.f ? acc[i] / lr : vs[i]) - vs[i];
-    d2 += df * df;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) d2 += __shfl_xor(d2, off, 64);
-  if (lane == 0) {
-    const float shift = pstar * sqrtf(d2);
-    // the isolated pair's term in the call's score: its shift (L2), squared (SQ), or its
-    // attention weight p* (attention sum)
-    dom[ro] = (p.mode == 1) ? shift * shift : (p.mode == 2 ? pstar : shift);
-    lse[ro] = (M + __log2f(1.f + lt)) * 0.69314718055994531f;
-    jstar[ro] = *(const int*)stat(win, 3);
-  }
+  combine_out(p, a, lse, jstar, dom, ro, lane, M, M2, lr, acc, vs, *(const int*)stat(win, 3));
 }
 
 }  // namespace
