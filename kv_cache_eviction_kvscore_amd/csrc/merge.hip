@@ -7,6 +7,8 @@
 // partials); PyramidKV page, aggregated window score (the sum over the heads that share
 // the KV head is part of the per-tile partial). No atomics: every token has one writer
 // and every sum has a fixed order.
+#include <climits>
+
 #include "kvs_internal.hpp"
 
 namespace kvs {
@@ -83,31 +85,42 @@ __global__ __launch_bounds__(256) void merge_sum_kernel(Dev p, const float* __re
 __global__ __launch_bounds__(256) void merge_isolated_kernel(Dev p, const int32_t* __restrict__ jstar,
                                                              const float* __restrict__ dom,
                                                              float* __restrict__ score) {
-  __shared__ int js[kMaxRows];
-  __shared__ float ds[kMaxRows];
+  // rows padded to a multiple of 8 with an argmax no row has (so the scan reads 16 bytes at
+  // a time, two reads in flight)
+  __shared__ __align__(16) int js[kMaxRows];
+  __shared__ __align__(16) float ds[kMaxRows];
   const int u = blockIdx.x;
   int l, s, g;
   unit_coords(p, u, l, s, g);
   const int tid = threadIdx.x;
   const int64_t rb = (int64_t)u * p.R;
-  for (int r = tid; r < p.R; r += 256) {
-    js[r] = jstar[rb + r];
-    ds[r] = dom[rb + r];
+  const int Rp = (p.R + 7) & ~7;
+  for (int r = tid; r < Rp; r += 256) {
+    const bool ok = r < p.R;
+    js[r] = ok ? jstar[rb + r] : INT_MIN;
+    ds[r] = ok ? dom[rb + r] : 0.f;
   }
   __syncthreads();
   float* out = score + (int64_t)(l * p.Hkv + g) * p.N + p.cu[s];
   const int64_t n = p.cu[s + 1] - p.cu[s];
   for (int r = tid; r < p.R; r += 256) {
     const int jj = js[r];
-    // one pass over all rows, the same for every lane (so the LDS reads pipeline): whether
-    // an earlier row has this argmax (then that row writes), and the sum over this row and
-    // the later ones that have it, in row order
+    // one pass over all rows, the same for every lane (so the LDS reads are broadcasts):
+    // whether an earlier row has this argmax (then that row writes), and the sum over this
+    // row and the later ones that have it, in row order
     bool earlier = false;
     float a1 = 0.f;
-    for (int r2 = 0; r2 < p.R; ++r2) {
-      const bool same = js[r2] == jj;
-      earlier |= same && r2 < r;
-      a1 += (same && r2 >= r) ? ds[r2] : 0.f;
+    for (int r8 = 0; r8 < Rp; r8 += 8) {
+      const int4 ja = *(const int4*)&js[r8], jb = *(const int4*)&js[r8 + 4];
+      const float4 da = *(const float4*)&ds[r8], db = *(const float4*)&ds[r8 + 4];
+      const int jv[8] = {ja.x, ja.y, ja.z, ja.w, jb.x, jb.y, jb.z, jb.w};
+      const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool same = jv[e] == jj;
+        earlier |= same && r8 + e < r;
+        a1 += (same && r8 + e >= r) ? dv[e] : 0.f;
+      }
     }
     if (!earlier && jj >= 0 && jj < n) out[jj] += a1;  // no argmax in the sequence: nothing to add
   }
