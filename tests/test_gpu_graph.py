@@ -33,24 +33,26 @@ def _same(x, y, what):
         assert np.array_equal(x[k].view(np.uint8), y[k].view(np.uint8)), f"{what}: {k} differs"
 
 
-def _eager(prob, budgets, q, k, v):
-    p = pipeline.Pipeline(prob, budgets)
+def _eager(prob, budgets, q, k, v, heads=False):
+    p = pipeline.Pipeline(prob, budgets, heads=heads)
     p.run(q, k, v)
     torch.cuda.synchronize()
     return _snapshot(p)
 
 
-@pytest.mark.parametrize("wid", [2, 5])
-def test_pipeline_graph_replays(wid):
+# the joint head select (heads=True) keeps a counter and lists in its workspace: every replay
+# must start them afresh
+@pytest.mark.parametrize("wid,heads", [(2, False), (5, False), (2, True)])
+def test_pipeline_graph_replays(wid, heads):
     w = WORKLOADS[wid] if wid == 2 else small_variant(WORKLOADS[5], num_layers=2, seqlens=(6000, 3000, 1500, 1300))
     data = synth.generate(w, "cuda")
     q, k, v = data["q"], data["k"], data["v"]
     prob = pipeline.problem_for(w, k, v)
     budgets = pipeline.workload_budgets(w)
     torch.cuda.synchronize()
-    want = _eager(prob, budgets, q, k, v)
+    want = _eager(prob, budgets, q, k, v, heads)
 
-    pipe = pipeline.Pipeline(prob, budgets)
+    pipe = pipeline.Pipeline(prob, budgets, heads=heads)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # one run off the capture, as torch recommends before capturing
@@ -68,13 +70,13 @@ def test_pipeline_graph_replays(wid):
         graph.replay()
         torch.cuda.synchronize()
         _same(_snapshot(pipe), want, f"{w.name} replay {rep}")
-        _eager(prob, budgets, q, k, v)  # eager work between the replays
+        _eager(prob, budgets, q, k, v, heads)  # eager work between the replays
 
     # new inputs written into the captured tensors: the replay follows them
     q2 = (torch.randn(q.shape, generator=torch.Generator(device="cuda").manual_seed(7), device="cuda") * 1.5)
     q.copy_(q2.to(torch.bfloat16))
     torch.cuda.synchronize()
-    want2 = _eager(prob, budgets, q, k, v)
+    want2 = _eager(prob, budgets, q, k, v, heads)
     graph.replay()
     torch.cuda.synchronize()
     _same(_snapshot(pipe), want2, f"{w.name} replay with new queries")
