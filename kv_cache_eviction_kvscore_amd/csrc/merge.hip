@@ -53,9 +53,9 @@ __global__ __launch_bounds__(256) void merge_sum_kernel(Dev p, const float* __re
     return;
   }
   // otherwise (rows not 16-byte aligned, as with an odd total token count, or the
-  // sequence's last chunk) 4-byte pieces, NB of them per thread with every tile's loads in
-  // flight before the sums; the same order of additions as above
-  constexpr int NB = 8;
+  // sequence's last chunk) 4-byte pieces, all of the thread's share of the chunk (NB) with
+  // every load of a tile in flight before its sums; the same order of additions as above
+  constexpr int NB = kMergeChunk / 256;
   const int64_t jend = (n < j0 + kMergeChunk) ? n : j0 + kMergeChunk;
   for (int64_t jb = j0 + tid; jb < jend; jb += 256 * NB) {
     float acc[NB];
