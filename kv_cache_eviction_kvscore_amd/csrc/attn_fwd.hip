@@ -546,7 +546,6 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
 // A row's outputs from its merged records: acc = the rest's weighted sum and lr its weight
 // (both relative to M2, the max over every key but the argmax), vs the argmax's value row.
 // p* = 1 / (1 + rel * lr), rel = exp2(M2 - M): the rest's total weight relative to the max.
-constexpr int kCombineMax = 8;  // chunks a row's records are merged from in one load round
 template <int PER>
 __device__ __attribute__((always_inline)) void combine_out(const Dev& p, float* __restrict__ a,
                                                            float* __restrict__ lse, int32_t* __restrict__ jstar,
@@ -577,7 +576,9 @@ __device__ __attribute__((always_inline)) void combine_out(const Dev& p, float* 
   }
 }
 
-template <int D>
+// CM > 0: a row's records from at most CM chunks (the launch picks CM from the largest
+// chunk count) all loaded at once; CM = 0: one chunk at a time, any count
+template <int D, int CM>
 __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __restrict__ ws,
                                                           float* __restrict__ a, float* __restrict__ lse,
                                                           int32_t* __restrict__ jstar, float* __restrict__ dom) {
@@ -598,13 +599,13 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
   // stat(c, 0) = m (max), 1 = m2 (max of the rest), 2 = l_rest (relative to m2), 3 = j*
   const size_t ro = (size_t)u * p.R + row;
   if (nch == 1) return;  // uniform: fwd_partial wrote this row's outputs
-  if (nch <= kCombineMax) {
-    // every chunk's statistics and row loaded at once (one memory latency instead of one
-    // per chunk and pass), then the same arithmetic in the same order as below
-    float mc[kCombineMax], m2c[kCombineMax], lc[kCombineMax], oc[kCombineMax][PER], vc[kCombineMax][PER];
-    int jc[kCombineMax];
+  // every chunk's statistics and row loaded at once (one memory latency instead of one per
+  // chunk and pass), then the same arithmetic in the same order as the loop below
+  if constexpr (CM > 0) {
+    float mc[CM], m2c[CM], lc[CM], oc[CM][PER], vc[CM][PER];
+    int jc[CM];
 #pragma unroll
-    for (int c = 0; c < kCombineMax; ++c) {
+    for (int c = 0; c < CM; ++c) {
       mc[c] = m2c[c] = -INFINITY;
       lc[c] = 0.f;
       jc[c] = -1;
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
     float M = -INFINITY;
     int win = -1;
 #pragma unroll
-    for (int c = 0; c < kCombineMax; ++c)
+    for (int c = 0; c < CM; ++c)
       if (jc[c] >= 0 && mc[c] > M) {
         M = mc[c];
         win = c;
@@ -643,7 +644,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
     }
     float M2 = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < kCombineMax; ++c) {
+    for (int c = 0; c < CM; ++c) {
       if (jc[c] < 0) continue;
       M2 = fmaxf(M2, m2c[c]);
       if (c != win) M2 = fmaxf(M2, mc[c]);
@@ -656,7 +657,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
       vs[i] = 0.f;
     }
 #pragma unroll
-    for (int c = 0; c < kCombineMax; ++c) {
+    for (int c = 0; c < CM; ++c) {
       if (jc[c] < 0) continue;
       const float w2 = (m2c[c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2c[c] - M2);
       const float w1 = (c != win) ? __builtin_amdgcn_exp2f(mc[c] - M2) : 0.f;
@@ -669,7 +670,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
     }
     combine_out(p, a, lse, jstar, dom, ro, lane, M, M2, lr, acc, vs, jc[win]);
     return;
-  }
+  } else {
   float M = -INFINITY;
   int win = -1;
   for (int c = 0; c < nch; ++c) {
@@ -717,6 +718,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
     }
   }
   combine_out(p, a, lse, jstar, dom, ro, lane, M, M2, lr, acc, vs, *(const int*)stat(win, 3));
+  }
 }
 
 }  // namespace
@@ -727,13 +729,21 @@ hipError_t launch_attn_fwd(const Dev& p, const void* q, const void* k, const voi
   if (p.d == 128) {
     hipLaunchKernelGGL(fwd_partial_kernel<128>, g1, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
                        (const __bf16*)v, (float*)ws, a, lse, jstar, dom);
-    if (p.fwd_chunks > 1)
-      hipLaunchKernelGGL(fwd_combine_kernel<128>, g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
+    if (p.fwd_chunks > 8)
+      hipLaunchKernelGGL((fwd_combine_kernel<128, 0>), g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
+    else if (p.fwd_chunks > 4)
+      hipLaunchKernelGGL((fwd_combine_kernel<128, 8>), g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
+    else if (p.fwd_chunks > 1)
+      hipLaunchKernelGGL((fwd_combine_kernel<128, 4>), g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
   } else {
     hipLaunchKernelGGL(fwd_partial_kernel<64>, g1, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
                        (const __bf16*)v, (float*)ws, a, lse, jstar, dom);
-    if (p.fwd_chunks > 1)
-      hipLaunchKernelGGL(fwd_combine_kernel<64>, g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
+    if (p.fwd_chunks > 8)
+      hipLaunchKernelGGL((fwd_combine_kernel<64, 0>), g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
+    else if (p.fwd_chunks > 4)
+      hipLaunchKernelGGL((fwd_combine_kernel<64, 8>), g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
+    else if (p.fwd_chunks > 1)
+      hipLaunchKernelGGL((fwd_combine_kernel<64, 4>), g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
   }
   return hipGetLastError();
 }
