@@ -116,7 +116,7 @@ typedef struct kvscore_problem {
   int64_t k_strides[3];      /* layer, KV-head, token strides of k in elements (token stride < 2^22) */
   int64_t v_strides[3];      /* same for v */
   int32_t mode;              /* KVSCORE_MODE_L2, KVSCORE_MODE_SQ or KVSCORE_MODE_ATTN */
-  float softmax_scale;       /* multiplies q.k; <= 0 selects 1/sqrt(d) */
+  float softmax_scale;       /* multiplies q.k; <= 0 selects 1/sqrt(d); inf/NaN: EINVAL */
 } kvscore_problem;
 
 /* Version as major*10000 + minor*100 + patch. */

@@ -62,6 +62,8 @@ int make_dev(const kvscore_problem* p, kvs::Dev& d) {
   const int G = p->num_q_heads / p->num_kv_heads;
   if ((int64_t)G * p->window > KVSCORE_MAX_ROWS)
     return fail(KVSCORE_EINVAL, "G*W=%lld query rows per unit exceeds %d", (long long)G * p->window, KVSCORE_MAX_ROWS);
+  if (!std::isfinite(p->softmax_scale))
+    return fail(KVSCORE_EINVAL, "softmax_scale must be finite (<= 0 selects 1/sqrt(head_dim))");
   if (p->mode != KVSCORE_MODE_L2 && p->mode != KVSCORE_MODE_SQ && p->mode != KVSCORE_MODE_ATTN)
     return fail(KVSCORE_EINVAL, "mode=%d", p->mode);
   if (!p->cu_seqlens) return fail(KVSCORE_EINVAL, "cu_seqlens is NULL");
@@ -199,6 +201,8 @@ int make_decdev(const kvscore_problem* p, const int64_t* off, kvs::DecDev& d) {
   const int G = p->num_q_heads / p->num_kv_heads;
   if (G > kvs::kDecodeMaxGroup) return fail(KVSCORE_EINVAL, "decode takes at most %d query heads per KV head", kvs::kDecodeMaxGroup);
   if (p->head_dim != 64 && p->head_dim != 128) return fail(KVSCORE_EINVAL, "head_dim must be 64 or 128");
+  if (!std::isfinite(p->softmax_scale))
+    return fail(KVSCORE_EINVAL, "softmax_scale must be finite (<= 0 selects 1/sqrt(head_dim))");
   if (!off) return fail(KVSCORE_EINVAL, "host segment offsets are NULL");
   const int64_t U = (int64_t)p->num_layers * p->num_seqs * p->num_kv_heads;
   if (U > kvs::kMaxUnits) return fail(KVSCORE_EINVAL, "too many segments (%lld > %d)", (long long)U, kvs::kMaxUnits);

@@ -55,6 +55,8 @@ BAD = [
     dict(v_strides=(2 * 100 * 128, 100 * 128 + 3, 128)),
     dict(num_q_heads=1024 * 2, num_kv_heads=1, window=2),
     dict(num_seqs=0, cu_seqlens=[0]),
+    dict(softmax_scale=float("inf")),
+    dict(softmax_scale=float("nan")),
     # units (L*S*Hkv) index a launch grid dimension: at most 65535
     dict(num_layers=32768, num_q_heads=8, num_kv_heads=2),
     dict(num_layers=1366, num_seqs=3, cu_seqlens=[0, 100, 200, 300], num_q_heads=32, num_kv_heads=16),
@@ -341,6 +343,7 @@ def test_decode_validation():
     assert _decode_rc(make_problem(num_q_heads=18, num_kv_heads=2), good) == api.EINVAL  # G = 9 > 8
     assert "at most 8" in api.load().kvscore_last_error().decode()
     assert _decode_rc(make_problem(head_dim=96), good) == api.EINVAL
+    assert _decode_rc(make_problem(softmax_scale=float("inf")), good) == api.EINVAL
     with pytest.raises(api.KvscoreError):
         api.decode_attn(p, None, None, None, [0, 10, 10, 30, 40], None, None, None, None)
 
