@@ -15,7 +15,10 @@
 //   dominates a token's score could miss a 1e-3 relative bound.
 // score_kernel: grid (key chunk, query tile, unit); 8 waves of one 32-row block each, two
 //   per SIMD (the kernel also builds with 4 waves of two blocks, one per SIMD; measured
-//   slower). Orientation S = Q.K^T on v_mfma_f32_32x32x16_bf16 and X = A_hat.V^T (rows x
+//   slower). A query tile of at most seven row blocks (G = 7: 224 rows) leaves the last
+//   wave without rows; that instance (HLP) gives it the side work of every wave (all DMA,
+//   the tile's norms and V conversion, every column flush) in a loop of its own with the
+//   same barriers, and the computing waves run only their half tiles. Orientation S = Q.K^T on v_mfma_f32_32x32x16_bf16 and X = A_hat.V^T (rows x
 //   keys) on v_mfma_f32_32x32x16_f16, with the row operands held in AGPRs and the
 //   accumulators written to VGPRs. K/V tiles of 64 keys go from HBM straight into LDS
 //   (global_load_lds_dwordx4, no register staging) through a ring of four buffers, so two
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(256) void score_prep_kernel(int64_t rows, const flo
   }
 }
 
-template <int D, int MODE, int RB>
+template <int D, int MODE, int RB, bool HLP>
 __global__ __launch_bounds__(512 / RB) __attribute__((amdgpu_waves_per_eu(2 / RB, 2 / RB))) void score_kernel(
     Dev p, const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const _Float16* __restrict__ ahat, const float* __restrict__ na, const float* __restrict__ lse2,
@@ -169,6 +172,11 @@ __global__ __launch_bounds__(512 / RB) __attribute__((amdgpu_waves_per_eu(2 / RB
   const int64_t rbase = (int64_t)u * p.R + (int64_t)qt * p.RT;  // first row of this tile (global row index)
   const int rows_here = min(p.RT, p.R - qt * p.RT);
   const bool computing = wrow0 < rows_here;
+  // HLP (query tiles of at most seven row blocks): the last wave, which holds no rows, does
+  // every wave's side work (all DMA, the whole tile's norms and V conversion, every column
+  // flush), and the computing waves run their half tiles only
+  static_assert(!HLP || RB == 1, "the helper form has one row block per wave");
+  const bool helper = HLP && wave == NWAVES - 1;
 
   // fields the lambdas below use, as locals: a by-reference capture of the by-value
   // argument would be re-read from kernel-argument memory with vector loads
@@ -256,6 +264,41 @@ __global__ __launch_bounds__(512 / RB) __attribute__((amdgpu_waves_per_eu(2 / RB
     if (cg == 0) *(bf16x8*)&sm.nvx[it & 1][key][0] = w8;
   };
 
+  // the whole tile's -||v||^2/2 and fp16 V: lane = key, its CPK chunks in two rounds
+  constexpr int NLDH = NLD * NWAVES;  // DMA instructions per tile, every wave's share
+  auto norms_h = [&](int it) __attribute__((always_inline)) {
+    if constexpr (!WITH_V) return;
+    char* vt = (char*)sm.tile[it % NBUF][1];
+    const int key = lane;
+    float ss = 0.f;
+    constexpr int CH = CPK / 2;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4 w[CH];
+#pragma unroll
+      for (int e = 0; e < CH; ++e) w[e] = *(const u32x4*)(vt + key * RS + (((CH * half + e) ^ swz<D>(key)) << 4));
+#pragma unroll
+      for (int e = 0; e < CH; ++e) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const unsigned wm = w[e][m];
+          const bf16x2 x = __builtin_bit_cast(bf16x2, wm);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+        }
+        *(u32x4*)(vt + key * RS + (((CH * half + e) ^ swz<D>(key)) << 4)) = bf16x8_to_f16x8(w[e]);
+      }
+    }
+    const Split3 sp = split3(-0.5f * ss);
+    bf16x8 w8 = {};
+    w8[0] = sp.hi;
+    w8[1] = sp.mid;
+    w8[2] = sp.lo;
+    w8[3] = (__bf16)1.f;
+    w8[4] = (__bf16)1.f;
+    w8[5] = (__bf16)1.f;
+    *(bf16x8*)&sm.nvx[it & 1][key][0] = w8;
+  };
+
   // ---- per-row masks in LDS, tile flags for rows whose argmax falls in this chunk
   for (int t = tid; t < ntiles; t += NTHREADS) sm.flag[t] = 0;
   for (int t = tid; t < 3 * kMaxWaves * KT; t += NTHREADS) (&sm.red[0][0][0])[t] = 0.f;  // waves that never compute add zeros
@@ -264,7 +307,41 @@ __global__ __launch_bounds__(512 / RB) __attribute__((amdgpu_waves_per_eu(2 / RB
     sm.tlim[t] = ok ? (int)(n - W + (qt * p.RT + t) % W) : -1;
     sm.jst[t] = ok ? jstar[rbase + t] : -1;
   }
-  issue(0);
+  // the helper's DMA of tile it: every wave's share (NLDH instructions), the slot mapping of
+  // issue(); full tiles take byte offsets from a table the helper builds once (off)
+  unsigned off[HLP ? NLDH : 1];
+  auto issue_h = [&](int it) __attribute__((always_inline)) {
+    const int64_t t0 = c0 + (int64_t)it * KT;
+    const bool full = t0 + KT <= c1;
+#pragma unroll
+    for (int f = 0; f < NLDH; ++f) {
+      const int tensor = f / IPT;
+      const __bf16* base = tensor == 0 ? kb0 + t0 * kst : vb0 + t0 * vst;
+      unsigned o;
+      if (full) {
+        o = off[f];
+      } else {
+        const int slot = (f % IPT) * 64 + lane;
+        const int r = slot / CPK, c = (slot % CPK) ^ swz<D>(r);
+        const int rr = (t0 + r < c1) ? r : (int)(c1 - 1 - t0);  // rows past the chunk load its last
+        o = (unsigned)(rr * (int)(tensor == 0 ? kst : vst) + 8 * c) * 2u;
+      }
+      lds_dma16(base, o, smb + (unsigned)(((it % NBUF) * 2 + tensor) * TBYTES + (f % IPT) * 1024));
+    }
+  };
+  if constexpr (HLP) {
+    if (helper) {
+#pragma unroll
+      for (int f = 0; f < NLDH; ++f) {
+        const int tensor = f / IPT, slot = (f % IPT) * 64 + lane;
+        const int r = slot / CPK, c = (slot % CPK) ^ swz<D>(r);
+        off[f] = (unsigned)(r * (int)(tensor == 0 ? kst : vst) + 8 * c) * 2u;
+      }
+      issue_h(0);
+    }
+  } else {
+    issue(0);
+  }
   __syncthreads();
   for (int t = tid; t < rows_here; t += NTHREADS) {
     const int js = sm.jst[t];
@@ -570,15 +647,51 @@ __global__ __launch_bounds__(512 / RB) __attribute__((amdgpu_waves_per_eu(2 / RB
     const int t = 32 * lane + i;
     if (t < ntiles && sm.flag[t]) flagbits |= 1u << i;
   }
-  norms(0);
-  if (ntiles > 1) issue_any(1);
-  if (ntiles > 2) issue_any(2);
+  if constexpr (HLP) {
+    if (helper) {
+      // the helper's own loop: the same barriers as the computing waves' loop below, with
+      // the side work of every wave. One wave keeps all DMA of two tiles in flight, and at
+      // most 63 vector memory operations may be outstanding: tile 2 waits for the first of
+      // tile 1's, and each iteration waits as described at its top.
+      norms_h(0);
+      if (ntiles > 1) issue_h(1);
+      if (ntiles > 2) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLDH - 1) : "memory");
+        issue_h(2);
+      }
+      // outstanding operations at the top of iteration t, oldest first: tile t+1's NLDH
+      // DMAs, the column store of iteration t-1 (from t = 3 on), tile t+2's NLDH DMAs. Tile
+      // t+1 has landed once at most NLDH remain; fewer (HW) also leave room for the NLDH + 1
+      // the iteration adds, within the counter's 63
+      constexpr int HW = (NLDH < 62 - NLDH) ? NLDH : 62 - NLDH;
+      for (int t = 0; t < ntiles; ++t) {
+        if (t + 2 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(HW) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (t >= 2) {  // the column sums of tile t-2, added in wave order; the store first
+          const int64_t j = c0 + (int64_t)(t - 2) * KT + lane;
+          float acc = sm.red[(t - 2) % 3][0][lane];
+#pragma unroll
+          for (int w = 1; w < NWAVES; ++w) acc += sm.red[(t - 2) % 3][w][lane];
+          if (j < c1) pout[j] = acc * out_scale;
+        }
+        if (t + 3 < ntiles) issue_h(t + 3);
+        if (t + 1 < ntiles) norms_h(t + 1);
+      }
+    }
+  } else {
+    norms(0);
+    if (ntiles > 1) issue_any(1);
+    if (ntiles > 2) issue_any(2);
+  }
   // two accumulator sets with fixed roles: A holds block 0 of a tile, B block 1 (no copies
   // between half tiles)
   Half<RB> A, B;
   bool sp_prev = false;  // tile t-1 needs the masked pair work
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 2 < ntiles) {
+  for (int t = 0; t < (helper ? 0 : ntiles); ++t) {
+    if constexpr (HLP) {
+      // no DMA of this wave's own is in flight
+    } else if (t + 2 < ntiles) {
       if constexpr (NLD == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
       else if constexpr (NLD == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       else if constexpr (NLD == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
@@ -597,7 +710,7 @@ __global__ __launch_bounds__(512 / RB) __attribute__((amdgpu_waves_per_eu(2 / RB
       if (t + 1 < ntiles) norms(t + 1);
       if (t >= 2) flush_store(t - 2, fv);
     };
-    const bool early = !computing || RB == 2 || wave < NWAVES / 2;
+    const bool early = !HLP && (!computing || RB == 2 || wave < NWAVES / 2);
     if (early) side();
     if (computing) {
       const bool sp = special(t);
@@ -608,7 +721,7 @@ __global__ __launch_bounds__(512 / RB) __attribute__((amdgpu_waves_per_eu(2 / RB
         const float cs = step(sp_prev, F_{}, t, 0, A, B, t - 1, 1);
         sm.red[(t - 1) % 3][wave][KB + l32] = cs;
       }
-      if (!early) side();
+      if (!HLP && !early) side();
       // block 1 of tile t into B, with the pair work of block 0 of tile t (A)
       const float cs = step(sp, F_{}, t, 1, B, A, t, 0);
       sm.red[t % 3][wave][l32] = cs;
@@ -634,20 +747,32 @@ hipError_t launch_score(const Dev& p, const void* q, const void* k, const void* 
   float* l2 = na + rows;
   const dim3 gp((unsigned)((rows + 3) / 4)), gs(p.score_chunks, p.Tq, p.U);
   constexpr int RBL = kScoreRowBlocks;
+  // query tiles of at most seven row blocks leave a wave without rows: it takes the side work
+  const bool hlp = RBL == 1 && p.RT <= kRowsPerTileMax - 32;
   auto run = [&](auto kern) {
     hipLaunchKernelGGL(kern, gs, dim3(512 / RBL), 0, st, p, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                        (const _Float16*)ahat, (const float*)na, (const float*)l2, jstar, partial);
   };
+  auto pick = [&](auto d, auto mode) {
+    constexpr int DD = decltype(d)::value, MM = decltype(mode)::value;
+    if (hlp) run(score_kernel<DD, MM, RBL, RBL == 1>);
+    else run(score_kernel<DD, MM, RBL, false>);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   if (p.d == 128) {
+    using D = std::integral_constant<int, 128>;
     hipLaunchKernelGGL(score_prep_kernel<128>, gp, dim3(256), 0, st, rows, a, lse, ahat, na, l2);
-    if (p.mode == 0) run(score_kernel<128, 0, RBL>);
-    else if (p.mode == 1) run(score_kernel<128, 1, RBL>);
-    else run(score_kernel<128, 2, RBL>);
+    if (p.mode == 0) pick(D{}, I0{});
+    else if (p.mode == 1) pick(D{}, I1{});
+    else pick(D{}, I2{});
   } else {
+    using D = std::integral_constant<int, 64>;
     hipLaunchKernelGGL(score_prep_kernel<64>, gp, dim3(256), 0, st, rows, a, lse, ahat, na, l2);
-    if (p.mode == 0) run(score_kernel<64, 0, RBL>);
-    else if (p.mode == 1) run(score_kernel<64, 1, RBL>);
-    else run(score_kernel<64, 2, RBL>);
+    if (p.mode == 0) pick(D{}, I0{});
+    else if (p.mode == 1) pick(D{}, I1{});
+    else pick(D{}, I2{});
   }
   return hipGetLastError();
 }
