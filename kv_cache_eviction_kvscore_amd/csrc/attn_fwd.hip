@@ -10,7 +10,10 @@
 // c * ||a - v_j|| = p * ||a^(-j) - v_j||).
 //
 // Pass 1 (fwd_partial): grid (key chunk, query tile, unit). 8 waves, two per SIMD; a
-// computing wave owns 32 rows, one row per lane (both half-waves hold the row).
+// computing wave owns 32 rows, one row per lane (both half-waves hold the row). With query
+// tiles of at most seven row blocks (G = 7: 224 rows) the HLP instance runs, in which the
+// last wave, which has no rows, issues every DMA and converts every V tile in a loop of its
+// own with the same barriers, and the computing waves only compute.
 // S^T = K.Q^T on v_mfma_f32_32x32x16_bf16 and O^T += V^T.P^T on v_mfma_f32_32x32x16_f16.
 // K/V tiles of 64 keys go from HBM straight into LDS (global_load_lds_dwordx4) through
 // a ring of four buffers, three tiles in flight while one is computed; the 16-byte chunks
@@ -82,7 +85,7 @@ __device__ inline float row_max(float x) {
   return fmaxf(v.lo, v.hi);
 }
 
-template <int D>
+template <int D, bool HLP>
 __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf16* __restrict__ q,
                                                                const __bf16* __restrict__ k,
                                                                const __bf16* __restrict__ v, float* __restrict__ ws,
@@ -417,13 +420,93 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
   // at once by every wave they back up in the address unit. It reads its V share of tile
   // t+1 at the second k-step of the S^T chain and writes it back converted after the
   // chain, so the LDS round trip runs under the MFMAs.
-  issue(0);
-  if (ntiles > 1) issue_any(1);
-  if (ntiles > 2) issue_any(2);
-  if (ntiles > 2) vm_wait<2 * NLD>();
+  if constexpr (HLP) {
+    // Query tiles of at most seven row blocks (G = 7: 224 rows): the waves without rows
+    // leave the computing waves no DMA and no conversion. The last of them issues every
+    // DMA instruction of a tile and converts the whole V tile to fp16, in a loop of its own
+    // with the same barriers; any other row-less wave only keeps the barriers. One wave
+    // keeps two tiles of DMA in flight, and at most 63 vector memory operations may be
+    // outstanding: each wait below leaves room for the next tile's NLDH.
+    if (!computing) {
+      if (wave == NWAVES - 1) {
+        constexpr int NLDH = NLD * NWAVES;
+        constexpr int HW = (NLDH < 63 - NLDH) ? NLDH : 63 - NLDH;
+        unsigned off[NLDH];
+#pragma unroll
+        for (int f = 0; f < NLDH; ++f) {
+          const int tensor = f / IPT, slot = (f % IPT) * 64 + lane;
+          const int r = slot / CPK;
+          const int c = (slot % CPK) ^ (tensor == 0 ? swz_k<D>(r) : swz_v<D>(r));
+          off[f] = (unsigned)(r * (int)(tensor == 0 ? kst : vst) + 8 * c) * 2u;
+        }
+        auto issue_h = [&](int it) __attribute__((always_inline)) {
+          const int64_t t0 = c0 + (int64_t)it * KT;
+          const bool full = t0 + KT <= c1;
+#pragma unroll
+          for (int f = 0; f < NLDH; ++f) {
+            const int tensor = f / IPT;
+            const __bf16* base = tensor == 0 ? kb0 + t0 * kst : vb0 + t0 * vst;
+            unsigned o = off[f];
+            if (!full) {
+              const int slot = (f % IPT) * 64 + lane;
+              const int r = slot / CPK;
+              const int c = (slot % CPK) ^ (tensor == 0 ? swz_k<D>(r) : swz_v<D>(r));
+              const int rr = (t0 + r < c1) ? r : (int)(c1 - 1 - t0);  // rows past the chunk load its last
+              o = (unsigned)(rr * (int)(tensor == 0 ? kst : vst) + 8 * c) * 2u;
+            }
+            lds_dma16(base, o, smb + (unsigned)(((it % NBUF) * 2 + tensor) * TBYTES + (f % IPT) * 1024));
+          }
+        };
+        // every 16-byte chunk of the V tile, in place, four at a time
+        auto convert_all = [&](int it) __attribute__((always_inline)) {
+#pragma unroll
+          for (int b = 0; b < IPT; b += 4) {
+            u32x4 w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = *(const u32x4*)&sm.tile[it % NBUF][1][((b + e) * 64 + lane) * 8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *(u32x4*)&sm.tile[it % NBUF][1][((b + e) * 64 + lane) * 8] = bf16x8_to_f16x8(w[e]);
+          }
+        };
+        issue_h(0);
+        if (ntiles > 1) {
+          vm_wait<HW>();
+          issue_h(1);
+        }
+        if (ntiles > 2) {
+          vm_wait<HW>();  // tile 0 has landed
+          issue_h(2);
+        } else if (ntiles > 1) {
+          vm_wait<NLDH>();
+        } else {
+          vm_wait<0>();
+        }
+        convert_all(0);
+        for (int t = 0; t < ntiles; ++t) {
+          __syncthreads();
+          if (t + 1 < ntiles) {  // tile t+1 has landed once at most HW (t+2's) remain
+            if (t + 2 < ntiles) vm_wait<HW>();
+            else vm_wait<0>();
+          }
+          if (t + 3 < ntiles) issue_h(t + 3);
+          if (t + 1 < ntiles) convert_all(t + 1);
+        }
+      } else {
+        for (int t = 0; t < ntiles; ++t) __syncthreads();
+      }
+      return;
+    }
+  } else {
+    issue(0);
+    if (ntiles > 1) issue_any(1);
+    if (ntiles > 2) issue_any(2);
+  }
+  if constexpr (HLP) {
+    // tile 0 comes from the helper: the loop's first barrier publishes it
+  } else if (ntiles > 2) vm_wait<2 * NLD>();
   else if (ntiles > 1) vm_wait<NLD>();
   else vm_wait<0>();
-  convert_own(0);
+  if constexpr (!HLP) convert_own(0);
   for (int t = 0; t < ntiles; ++t) {
     __syncthreads();
     const bool more3 = t + 3 < ntiles, more2 = t + 2 < ntiles, more1 = t + 1 < ntiles;
@@ -438,7 +521,9 @@ __global__ __launch_bounds__(NTHREADS) void fwd_partial_kernel(Dev p, const __bf
       compute_tile(t, [&](auto pc) __attribute__((always_inline)) {
         // 0, 5, 1: S^T chain (k-steps 0, 1, NKK/2); 2: after it; 3, 4: O^T chain
         constexpr int point = decltype(pc)::value;
-        if constexpr (point == 5) {
+        if constexpr (HLP) {
+          // the helper wave streams and converts the tiles
+        } else if constexpr (point == 5) {
           // this lane's loads of tile t+1 (t+2 and the one instruction of t+3 issued at
           // point 0 may stay in flight), then its share of that tile's V read for conversion
           if (more1) {
@@ -726,9 +811,15 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(Dev p, const float* __
 hipError_t launch_attn_fwd(const Dev& p, const void* q, const void* k, const void* v, float* a, float* lse,
                            int32_t* jstar, float* dom, void* ws, hipStream_t st) {
   const dim3 g1(p.fwd_chunks, p.Tq, p.U), g2((p.R + 3) / 4, p.U);
+  // query tiles of at most seven row blocks leave a wave without rows: it takes the streaming
+  const bool hlp = p.RT <= kRowsPerTileMax - 32;
   if (p.d == 128) {
-    hipLaunchKernelGGL(fwd_partial_kernel<128>, g1, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, (float*)ws, a, lse, jstar, dom);
+    if (hlp)
+      hipLaunchKernelGGL((fwd_partial_kernel<128, true>), g1, dim3(NTHREADS), 0, st, p, (const __bf16*)q,
+                         (const __bf16*)k, (const __bf16*)v, (float*)ws, a, lse, jstar, dom);
+    else
+      hipLaunchKernelGGL((fwd_partial_kernel<128, false>), g1, dim3(NTHREADS), 0, st, p, (const __bf16*)q,
+                         (const __bf16*)k, (const __bf16*)v, (float*)ws, a, lse, jstar, dom);
     if (p.fwd_chunks > 8)
       hipLaunchKernelGGL((fwd_combine_kernel<128, 0>), g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
     else if (p.fwd_chunks > 4)
@@ -736,8 +827,12 @@ hipError_t launch_attn_fwd(const Dev& p, const void* q, const void* k, const voi
     else if (p.fwd_chunks > 1)
       hipLaunchKernelGGL((fwd_combine_kernel<128, 4>), g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
   } else {
-    hipLaunchKernelGGL(fwd_partial_kernel<64>, g1, dim3(NTHREADS), 0, st, p, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, (float*)ws, a, lse, jstar, dom);
+    if (hlp)
+      hipLaunchKernelGGL((fwd_partial_kernel<64, true>), g1, dim3(NTHREADS), 0, st, p, (const __bf16*)q,
+                         (const __bf16*)k, (const __bf16*)v, (float*)ws, a, lse, jstar, dom);
+    else
+      hipLaunchKernelGGL((fwd_partial_kernel<64, false>), g1, dim3(NTHREADS), 0, st, p, (const __bf16*)q,
+                         (const __bf16*)k, (const __bf16*)v, (float*)ws, a, lse, jstar, dom);
     if (p.fwd_chunks > 8)
       hipLaunchKernelGGL((fwd_combine_kernel<64, 0>), g2, dim3(256), 0, st, p, (const float*)ws, a, lse, jstar, dom);
     else if (p.fwd_chunks > 4)
